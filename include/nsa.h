@@ -1,0 +1,182 @@
+/*
+ * nsa.h -- C ABI of the MI355X (gfx950) library for block-sparse attention
+ * driven by top-k KV-tile selection.
+ *
+ * Two calls make up the path:
+ *   nsa_select             query/key tiles -> int8 keep flags + per-row CSR list
+ *   nsa_block_sparse_attn  attention over the kept tiles -> output + logsumexp
+ * plus host-only sizing, two stage entry points (pooling, scores) and status
+ * strings.
+ *
+ * What the selection computes is defined by the page
+ * "automatic/modules/attention/sparse/selector.py" (functions SparseSpec,
+ * BlockSelection, pool_blocks, diagonal_blocks, score_blocks, selection_plan,
+ * select_blocks). The attention consumer is not printed on any page; its
+ * definition here is the usual scaled softmax attention restricted to the kept
+ * tiles (see nsa_block_sparse_attn).
+ *
+ * Conventions common to every call
+ *   - Tensors are dense, contiguous, row-major (B, H, S, D) in device memory.
+ *   - The caller allocates and owns every buffer; the library keeps no pointer
+ *     after a call returns. All device work is enqueued on `stream` (a
+ *     hipStream_t; NULL = the default stream) and runs asynchronously; nothing
+ *     synchronises the device.
+ *   - Every argument is validated before any work is enqueued; on an error the
+ *     call returns a negative nsa_status and leaves all outputs untouched.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef NSA_H
+#define NSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. 0 = success; NSA_DENSE is informational (> 0); errors < 0. */
+enum nsa_status {
+    NSA_OK = 0,
+    NSA_DENSE = 1,                /* the budget covers every candidate: attend densely */
+    NSA_ERR_NULL_ARG = -1,        /* a required pointer is NULL */
+    NSA_ERR_BAD_SHAPE = -2,       /* inconsistent sizes, Hq % Hkv != 0, mask not broadcastable */
+    NSA_ERR_BAD_DTYPE = -3,       /* dtype not F32/BF16, or q/k/v/out dtypes differ */
+    NSA_ERR_UNSUPPORTED = -4,     /* valid request this build does not run (see each call) */
+    NSA_ERR_WORKSPACE = -5,       /* workspace missing or smaller than nsa_sizes.workspace_bytes */
+    NSA_ERR_BAD_SPEC = -6,        /* block size <= 0, budget < 0 or NaN, chunk bytes < 0 */
+    NSA_ERR_HIP = -7,             /* a HIP runtime call failed: see nsa_last_hip_error() */
+    NSA_ERR_CAPACITY = -8         /* col_idx capacity below the selection's nnz */
+};
+
+enum nsa_dtype { NSA_F32 = 0, NSA_BF16 = 1 };
+
+/* A device tensor of shape (B, H, S, D), contiguous. */
+typedef struct nsa_tensor {
+    void* data;      /* device pointer */
+    int32_t dtype;   /* enum nsa_dtype */
+    int32_t B, H, S, D;
+} nsa_tensor;
+
+/* Selection spec; the fields and defaults of SparseSpec on the selection page:
+ * budget 0.30, block_q 128, block_kv 64, head_shared 0, force 0,
+ * score_chunk_bytes 256 MiB. budget is the fraction of each row's candidate
+ * tiles (neither must-keep nor dropped) chosen by score; pinned and diagonal
+ * tiles come on top. head_shared scores once for all heads with the head-mean
+ * of the pooled queries and of the pooled keys. force skips the dense short
+ * circuit. score_chunk_bytes bounds the fp32 score buffer per head chunk. */
+typedef struct nsa_spec {
+    float budget;
+    int32_t block_q;
+    int32_t block_kv;
+    int32_t head_shared;
+    int32_t force;
+    int64_t score_chunk_bytes;
+} nsa_spec;
+
+/* Optional tile mask in HOST memory (pins or drops), int8, nonzero = set,
+ * contiguous (b_dim, h_dim, nq, nk) and broadcast over the selection shape
+ * (B, H', NQ, NK): b_dim in {1, B}, h_dim in {1, H'}, nq == NQ, nk == NK.
+ * H' = 1 when head_shared, else Hq. */
+typedef struct nsa_mask {
+    const int8_t* data;
+    int32_t b_dim, h_dim, nq, nk;
+} nsa_mask;
+
+/* A block selection (the BlockSelection of the selection page plus its CSR
+ * form). Device buffers are caller-owned:
+ *   keep    int8  (B, H', NQ, NK)     1 = tile kept
+ *   row_ptr int32 (B*H'*NQ + 1)       row r = (b*H' + h')*NQ + i
+ *   col_idx int32 (capacity >= nnz)   kept kv tiles per row, strictly ascending
+ * nsa_select fills the buffers and every geometry field. */
+typedef struct nsa_selection {
+    int8_t* keep;
+    int32_t* row_ptr;
+    int32_t* col_idx;
+    int64_t col_capacity;   /* entries available in col_idx (set by the caller) */
+    int64_t nnz;            /* number of kept tiles (set by nsa_select) */
+    int32_t B, H, NQ, NK;   /* H = H' (selection heads: 1 or Hq) */
+    int32_t block_q, block_kv;
+    int32_t seq_q, seq_kv;
+    float budget;
+} nsa_selection;
+
+/* Sizes of a selection, from geometry and masks only (no tensor data). */
+typedef struct nsa_sizes {
+    int32_t NQ, NK;          /* ceil(S / block_q), ceil(S / block_kv) */
+    int32_t sel_heads;       /* H' */
+    int32_t dense;           /* 1 when the dense short circuit applies (and force is 0) */
+    int64_t rows;            /* B * H' * NQ */
+    int64_t nnz;             /* exact number of kept tiles */
+    int64_t workspace_bytes; /* device workspace nsa_select needs */
+} nsa_sizes;
+
+/* Host only. Computes the plan of selection_plan on the selection page: NQ,
+ * NK, must = diagonal OR pins, forbidden = drops, candidates c_r, per-row
+ * budget k_r = ceil(fl32(c_r) * fl32(budget)), the exact nnz
+ * = sum_r |must_r \ forbidden_r| + min(k_r, c_r), and the dense decision (every
+ * k_r >= c_r and force == 0). q and k are read for their shapes only; pins and
+ * drops may be NULL. If row_ptr_host is non-NULL it receives rows+1 int32
+ * offsets. Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE, BAD_SPEC, UNSUPPORTED
+ * (nnz >= 2^31). */
+int nsa_select_sizes(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec,
+                     const nsa_mask* pins, const nsa_mask* drops, nsa_sizes* out,
+                     int32_t* row_ptr_host);
+
+/* select_blocks of the selection page. Pools q over block_q tokens and k over
+ * block_kv tokens (fp32 means; a tail tile is averaged over its real length),
+ * scores every (query tile, kv tile) pair by the pooled dot product (no scale,
+ * no softmax; head_shared: head-means of both operands; GQA: query head h uses
+ * kv head h / (Hq/Hkv)), then per row keeps must, plus the k_r best candidates
+ * (score descending, ties to the lower kv index, -0.0 == +0.0), minus drops.
+ *   q: (B, Hq, Sq, D), k: (B, Hkv, Skv, D), same dtype (F32 or BF16), finite.
+ *   out: keep / row_ptr / col_idx buffers and col_capacity set by the caller.
+ *   workspace: device scratch of at least nsa_sizes.workspace_bytes, 256-byte
+ *   aligned; its contents are undefined after the call.
+ * Returns NSA_DENSE (outputs untouched, nothing enqueued) when the dense short
+ * circuit applies. Errors as nsa_select_sizes, plus WORKSPACE, CAPACITY, HIP.
+ * UNSUPPORTED: D not in {64, 128, 256}, NK > 4096. Result on non-finite
+ * inputs is unspecified. */
+int nsa_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec,
+               const nsa_mask* pins, const nsa_mask* drops, nsa_selection* out,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention over the kept tiles. For query head h, kv head g = h / (Hq/Hkv)
+ * and selection head h' = h (or 0 when sel->H == 1). Key u is visible to query
+ * t iff tile (t / block_q, u / block_kv) is kept in row (b, h', t / block_q)
+ * and, when causal != 0, u <= t. With l_tu = D^-1/2 q_t . k_u:
+ *   lse[t] = ln sum_{visible u} exp(l_tu)            (fp32, natural log)
+ *   out[t] = sum_{visible u} exp(l_tu - lse[t]) v_u   (dtype of q)
+ * A query with no visible key gets out = 0 and lse = -inf. sel == NULL means
+ * dense (every tile kept: the consumer side of NSA_DENSE).
+ *   q, out: (B, Hq, S, D); k, v: (B, Hkv, S, D); lse: device fp32 (B, Hq, S).
+ * UNSUPPORTED: Sq != Skv (the selection page pools both from equal-length
+ * sequences in every workload here), D not in {64, 128}. */
+int nsa_block_sparse_attn(const nsa_tensor* q, const nsa_tensor* k, const nsa_tensor* v,
+                          const nsa_selection* sel, int causal, nsa_tensor* out,
+                          float* lse, void* stream);
+
+/* Stage entry point: pool_blocks of the selection page on its own.
+ * x: (B, H, S, D) F32/BF16 device; out: device fp32 (B, H, ceil(S/block), D). */
+int nsa_pool_blocks(const nsa_tensor* x, int32_t block, float* out, void* stream);
+
+/* Stage entry point: the full fp32 score tensor of score_blocks on the
+ * selection page, (B, H', NQ, NK), written to scores (device). Needs a
+ * workspace of nsa_sizes.workspace_bytes (as nsa_select). */
+int nsa_score_blocks(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec,
+                     float* scores, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. Never NULL. */
+const char* nsa_status_string(int status);
+
+/* The hipError_t of the last NSA_ERR_HIP returned on this thread (0 if none). */
+int nsa_last_hip_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* nsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSA_H */

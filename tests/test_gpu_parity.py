@@ -1,0 +1,176 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element by element.
+
+Small, seeded cases that span several tiles, ragged tails, GQA, head-shared
+scoring, pins and drops (drops winning over the diagonal, empty rows), the
+dense short circuit, sequences shorter than a block, the widest supported row
+(NK = 4096), all-tied scores, and both attention kernels (bf16 MFMA and the
+general fp32/bf16 kernel).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import top_kv_tile_amd as tkt
+from parity_util import check_attention, run_case, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _qkv(B, Hq, Hkv, S, D, seed, dtype):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, Hq, S, D, generator=g).to(dtype)
+    k = torch.randn(B, Hkv, S, D, generator=g).to(dtype)
+    v = torch.randn(B, Hkv, S, D, generator=g).to(dtype)
+    return q, k, v
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("S,D,block", [(300, 64, 64), (100, 128, 128), (1000, 128, 64), (64, 256, 32)])
+def test_pool_blocks(dtype, S, D, block):
+    say(f"pool dtype={dtype} S={S} D={D} block={block}")
+    g = torch.Generator().manual_seed(S + D)
+    x = torch.randn(2, 3, S, D, generator=g).to(dtype)
+    got = tkt.nsa_pool_blocks(to_dev(x), block).cpu().double()
+    ref = oracle.pool_blocks(x, block).double()
+    n = block
+    bound = 2 * n * 2.0 ** -24 * x.abs().max().item() + 1e-30
+    assert got.shape == ref.shape
+    assert (got - ref).abs().max().item() <= bound
+
+
+@pytest.mark.parametrize("Hq,Hkv,shared", [(4, 4, False), (8, 2, False), (6, 3, True)])
+def test_score_blocks(Hq, Hkv, shared):
+    say(f"scores Hq={Hq} Hkv={Hkv} shared={shared}")
+    S, D, bq, bkv = 2000, 128, 128, 64
+    q, k, _ = _qkv(1, Hq, Hkv, S, D, seed=Hq * 7 + Hkv, dtype=torch.bfloat16)
+    spec = tkt.SparseSpec(block_q=bq, block_kv=bkv, head_shared=shared)
+    got = tkt.nsa_score_blocks(to_dev(q), to_dev(k), spec).cpu().numpy().astype(np.float64)
+    ref = oracle.score_blocks(q, k, bq, bkv, shared).astype(np.float64)
+    qh, kh = oracle.head_operands(oracle.pool_blocks(q, bq), oracle.pool_blocks(k, bkv), shared)
+    mag = np.abs(qh.double().numpy()) @ np.swapaxes(np.abs(kh.double().numpy()), -1, -2)
+    assert got.shape == ref.shape
+    assert np.all(np.abs(got - ref) <= 4 * D * 2.0 ** -24 * mag + 1e-30)
+
+
+CASES = [
+    # name, B, Hq, Hkv, S, D, bq, bkv, budget, shared, causal, dtype
+    ("tiny_f32_causal", 1, 2, 2, 512, 64, 64, 32, 0.30, False, True, torch.float32),
+    ("bf16_gqa_causal_ragged", 2, 4, 2, 1000, 128, 128, 64, 0.30, False, True, torch.bfloat16),
+    ("bf16_shared_noncausal_ragged", 1, 4, 4, 777, 128, 128, 64, 0.25, True, False, torch.bfloat16),
+    ("bf16_d64_bq64_gqa8", 1, 8, 1, 2048, 64, 64, 64, 0.20, False, True, torch.bfloat16),
+    ("bf16_bq32", 1, 2, 2, 640, 128, 32, 64, 0.40, False, True, torch.bfloat16),
+    ("bf16_general_kernel_bkv32", 1, 2, 1, 700, 64, 64, 32, 0.30, False, True, torch.bfloat16),
+    ("f32_d128_noncausal", 1, 2, 2, 600, 128, 128, 64, 0.50, False, False, torch.float32),
+    ("bf16_budget0", 1, 2, 2, 1024, 128, 128, 64, 0.0, False, False, torch.bfloat16),
+    ("bf16_nk100", 1, 2, 2, 6400, 128, 128, 64, 0.10, False, False, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_select_and_attention(case):
+    name, B, Hq, Hkv, S, D, bq, bkv, budget, shared, causal, dtype = case
+    say(f"case {name}")
+    q, k, v = _qkv(B, Hq, Hkv, S, D, seed=abs(hash(name)) % 10000, dtype=dtype)
+    spec = tkt.SparseSpec(budget=budget, block_q=bq, block_kv=bkv, head_shared=shared)
+    rep = run_case(q, k, v, spec, causal, where=name)
+    say(f"  {rep}")
+
+
+def test_pins_drops_broadcast_and_drop_wins():
+    """Pins per batch, drops per head, a dropped diagonal tile (empty causal rows)."""
+    B, Hq, Hkv, S, D, bq, bkv = 2, 4, 2, 1024, 128, 128, 64
+    say("pins/drops broadcast")
+    q, k, v = _qkv(B, Hq, Hkv, S, D, seed=77, dtype=torch.bfloat16)
+    nq, nk = 8, 16
+    rng = np.random.default_rng(5)
+    pins = (rng.random((B, 1, nq, nk)) < 0.1).astype(np.int8)
+    drops = (rng.random((1, Hq, nq, nk)) < 0.1).astype(np.int8)
+    drops[0, 1, 3, 6] = 1  # diagonal tiles of row 3 are kv 6 and 7
+    drops[0, 1, 3, 7] = 1
+    pins[:, :, 3, :] = 0
+    spec = tkt.SparseSpec(budget=0.3, block_q=bq, block_kv=bkv)
+    rep = run_case(q, k, v, spec, True, pins=pins, drops=drops, where="pins_drops")
+    say(f"  {rep}")
+
+
+def test_force_budget_one_equals_dense():
+    """budget 1 + force keeps everything; the GPU result equals the GPU dense call and the oracle."""
+    say("force budget 1")
+    q, k, v = _qkv(1, 4, 2, 1000, 128, seed=3, dtype=torch.bfloat16)
+    spec = tkt.SparseSpec(budget=1.0, block_q=128, block_kv=64, force=True)
+    rep = run_case(q, k, v, spec, True, where="force1")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    sel = tkt.nsa_select(qd, kd, spec)
+    assert int(sel.keep.min().item()) == 1
+    o1, l1 = tkt.nsa_block_sparse_attn(qd, kd, vd, sel, True)
+    o2, l2 = tkt.nsa_block_sparse_attn(qd, kd, vd, None, True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    say(f"  {rep}")
+
+
+def test_dense_short_circuit():
+    say("dense short circuit")
+    q, k, v = _qkv(1, 2, 2, 512, 64, seed=4, dtype=torch.float32)
+    spec = tkt.SparseSpec(budget=1.0, block_q=64, block_kv=32)
+    assert tkt.nsa_select(to_dev(q), to_dev(k), spec) is None
+    rep = run_case(q, k, v, spec, False, where="dense")  # attention with selection None
+    say(f"  {rep}")
+
+
+def test_short_sequence_single_tile():
+    """S below one block: a single partial tile; forced selection keeps the diagonal only."""
+    say("short sequence")
+    q, k, v = _qkv(1, 2, 2, 50, 128, seed=6, dtype=torch.bfloat16)
+    spec = tkt.SparseSpec(budget=0.3, block_q=128, block_kv=64)
+    assert tkt.nsa_select(to_dev(q), to_dev(k), spec) is None  # no candidates: dense
+    rep = run_case(q, k, v, tkt.SparseSpec(budget=0.3, force=True), True, where="short")
+    say(f"  {rep}")
+
+
+def test_empty_sequence():
+    say("empty sequence")
+    q = torch.zeros(1, 2, 0, 64, device="cuda:0")
+    spec = tkt.SparseSpec(budget=0.3, force=True)
+    sel = tkt.nsa_select(q, q, spec)
+    assert sel is not None and sel.keep.numel() == 0 and sel.nnz == 0
+    out, lse = tkt.nsa_block_sparse_attn(q, q, q, sel, True)
+    assert out.numel() == 0 and lse.numel() == 0
+    assert tkt.nsa_select(q, q, tkt.SparseSpec(budget=0.3)) is None
+
+
+def test_all_tied_scores_pick_lowest_index():
+    say("all ties")
+    B, H, S, D = 1, 2, 2048, 128
+    _, k, v = _qkv(B, H, H, S, D, seed=8, dtype=torch.bfloat16)
+    q = torch.zeros(B, H, S, D, dtype=torch.bfloat16)
+    rep = run_case(q, k, v, tkt.SparseSpec(budget=0.3), False, where="ties")
+    say(f"  {rep}")
+
+
+def test_widest_row_nk4096():
+    """NK = 4096 (64 score slots per lane), per-head GQA scoring, sampled attention rows."""
+    say("nk4096")
+    B, Hq, Hkv, S, D = 1, 2, 1, 4096 * 16, 64
+    q, k, v = _qkv(B, Hq, Hkv, S, D, seed=9, dtype=torch.bfloat16)
+    spec = tkt.SparseSpec(budget=0.02, block_q=64, block_kv=16)
+    rows = [(0, 0, 0), (0, 1, 517), (0, 0, 1023)]
+    rep = run_case(q, k, v, spec, True, rows=rows, where="nk4096")
+    say(f"  {rep}")
+
+
+def test_error_codes_do_not_launch():
+    say("error codes")
+    q = torch.zeros(1, 4, 128, 128, dtype=torch.bfloat16, device="cuda:0")
+    k = torch.zeros(1, 3, 128, 128, dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(tkt.NsaError) as e:
+        tkt.nsa_select(q, k, tkt.SparseSpec())
+    assert e.value.status == -2
+    with pytest.raises(tkt.NsaError) as e:
+        tkt.nsa_select(q, q, tkt.SparseSpec(budget=float("nan")))
+    assert e.value.status == -6
+    with pytest.raises(tkt.NsaError) as e:
+        tkt.nsa_block_sparse_attn(q, q.float(), q, None, True)
+    assert e.value.status == -3

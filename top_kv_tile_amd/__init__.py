@@ -1,0 +1,23 @@
+"""MI355X (gfx950) block-sparse attention driven by top-k KV-tile selection.
+
+The work runs in hand-written HIP kernels behind the C ABI of include/nsa.h
+(``libnsa.so``, built in-tree by ``python -m top_kv_tile_amd.build``); this
+package is its thin Python binding. See ``top_kv_tile_amd.nsa``.
+"""
+from .nsa import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    NsaError,
+    Selection,
+    Sizes,
+    SparseSpec,
+    lib,
+    nsa_block_sparse_attn,
+    nsa_pool_blocks,
+    nsa_score_blocks,
+    nsa_select,
+    nsa_select_sizes,
+    nsa_status_string,
+)
+
+__version__ = "0.1.0"

@@ -1,0 +1,555 @@
+// C ABI of the library: validation, the host-side selection plan, workspace
+// layout and kernel launches. Declarations and contracts are in include/nsa.h.
+//
+// The plan follows selection_plan on the page
+// "automatic/modules/attention/sparse/selector.py": it depends only on the
+// geometry and the pin/drop masks, never on tensor data, so it is computed on
+// the host (no device readback) and uploaded with the launches.
+#include "../../include/nsa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "nsa_internal.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_fail(hipError_t e) {
+    g_last_hip = (int)e;
+    return NSA_ERR_HIP;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int64_t numel(const nsa_tensor* t) { return (int64_t)t->B * t->H * t->S * t->D; }
+
+int check_tensor(const nsa_tensor* t) {
+    if (!t) return NSA_ERR_NULL_ARG;
+    if (t->dtype != NSA_F32 && t->dtype != NSA_BF16) return NSA_ERR_BAD_DTYPE;
+    if (t->B < 0 || t->H <= 0 || t->S < 0 || t->D <= 0) return NSA_ERR_BAD_SHAPE;
+    if (!t->data && numel(t) > 0) return NSA_ERR_NULL_ARG;
+    return NSA_OK;
+}
+
+struct Geo {
+    int B, Hq, Hkv, Sq, Skv, D, NQ, NK, NKW, Hsel, group;
+    int bf16;
+    int64_t rows;
+};
+
+int check_spec(const nsa_spec* s) {
+    if (!s) return NSA_ERR_NULL_ARG;
+    if (s->block_q <= 0 || s->block_kv <= 0) return NSA_ERR_BAD_SPEC;
+    if (!(s->budget >= 0.0f)) return NSA_ERR_BAD_SPEC;  // rejects NaN and negatives
+    if (s->score_chunk_bytes < 0) return NSA_ERR_BAD_SPEC;
+    return NSA_OK;
+}
+
+int check_mask(const nsa_mask* m, const Geo& g) {
+    if (!m) return NSA_OK;
+    if (m->b_dim != 1 && m->b_dim != g.B) return NSA_ERR_BAD_SHAPE;
+    if (m->h_dim != 1 && m->h_dim != g.Hsel) return NSA_ERR_BAD_SHAPE;
+    if (m->nq != g.NQ || m->nk != g.NK) return NSA_ERR_BAD_SHAPE;
+    if (!m->data && (int64_t)m->b_dim * m->h_dim * m->nq * m->nk > 0) return NSA_ERR_NULL_ARG;
+    return NSA_OK;
+}
+
+int validate_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, const nsa_mask* pins,
+                    const nsa_mask* drops, Geo& g) {
+    int st;
+    if ((st = check_tensor(q)) != NSA_OK) return st;
+    if ((st = check_tensor(k)) != NSA_OK) return st;
+    if ((st = check_spec(spec)) != NSA_OK) return st;
+    if (q->dtype != k->dtype) return NSA_ERR_BAD_DTYPE;
+    if (q->B != k->B || q->D != k->D) return NSA_ERR_BAD_SHAPE;
+    if (q->H % k->H != 0) return NSA_ERR_BAD_SHAPE;
+    g.B = q->B;
+    g.Hq = q->H;
+    g.Hkv = k->H;
+    g.Sq = q->S;
+    g.Skv = k->S;
+    g.D = q->D;
+    g.NQ = (int)ceil_div(q->S, spec->block_q);
+    g.NK = (int)ceil_div(k->S, spec->block_kv);
+    g.NKW = (int)ceil_div(g.NK, 64);
+    g.Hsel = spec->head_shared ? 1 : q->H;
+    g.group = q->H / k->H;
+    g.bf16 = q->dtype == NSA_BF16;
+    g.rows = (int64_t)g.B * g.Hsel * g.NQ;
+    if ((st = check_mask(pins, g)) != NSA_OK) return st;
+    if ((st = check_mask(drops, g)) != NSA_OK) return st;
+    if (g.D != 64 && g.D != 128 && g.D != 256) return NSA_ERR_UNSUPPORTED;
+    if (g.NK > 4096) return NSA_ERR_UNSUPPORTED;
+    return NSA_OK;
+}
+
+// Pack an int8 mask (nonzero = set) into 64-bit words per (b, h, i) row: bit
+// (j % 64) of word j / 64.
+void pack_mask(const nsa_mask* m, int NKW, std::vector<uint64_t>& out) {
+    const int64_t nrows = (int64_t)m->b_dim * m->h_dim * m->nq;
+    out.assign((size_t)(nrows * NKW), 0ull);
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int8_t* src = m->data + r * m->nk;
+        uint64_t* dst = out.data() + r * NKW;
+        int j = 0;
+        for (; j + 8 <= m->nk; j += 8) {
+            uint64_t x;
+            std::memcpy(&x, src + j, 8);
+            // any nonzero byte -> bit 0 of that byte
+            x |= x >> 4;
+            x |= x >> 2;
+            x |= x >> 1;
+            x &= 0x0101010101010101ull;
+            // gather bit 0 of each byte into the low 8 bits
+            const uint64_t bits = (x * 0x0102040810204080ull) >> 56;
+            dst[j >> 6] |= bits << (j & 63);
+        }
+        for (; j < m->nk; ++j)
+            if (src[j]) dst[j >> 6] |= 1ull << (j & 63);
+    }
+}
+
+struct Plan {
+    Geo g;
+    std::vector<int32_t> row_ptr;  // rows + 1
+    std::vector<uint64_t> pin_words, drop_words;
+    int pb = 1, ph = 1, db = 1, dh = 1;
+    int64_t nnz = 0;
+    bool dense = true;
+};
+
+// k_r = ceil(fl32(c_r) * fl32(budget)): an integer count times the budget,
+// evaluated in float32 (the type torch promotes that product to).
+inline int64_t keep_per_row(int64_t c, float budget) {
+    volatile float prod = (float)c * budget;  // one IEEE fp32 rounding, no contraction
+    return (int64_t)std::ceil((float)prod);
+}
+
+int build_plan(const Geo& g, const nsa_spec* spec, const nsa_mask* pins, const nsa_mask* drops, Plan& p,
+               bool want_row_ptr) {
+    p.g = g;
+    if (pins) {
+        pack_mask(pins, g.NKW, p.pin_words);
+        p.pb = pins->b_dim;
+        p.ph = pins->h_dim;
+    }
+    if (drops) {
+        pack_mask(drops, g.NKW, p.drop_words);
+        p.db = drops->b_dim;
+        p.dh = drops->h_dim;
+    }
+    // Per distinct (pin slab, drop slab) pair: kept count of each query tile.
+    std::vector<int64_t> slab_key;
+    std::vector<std::vector<int32_t>> slab_counts;
+    std::vector<uint64_t> diag(g.NKW);
+    auto counts_for = [&](int ps, int ds) -> const std::vector<int32_t>& {
+        const int64_t key = (int64_t)ps * 1000003 + ds;
+        for (size_t x = 0; x < slab_key.size(); ++x)
+            if (slab_key[x] == key) return slab_counts[x];
+        std::vector<int32_t> cnt(g.NQ);
+        for (int i = 0; i < g.NQ; ++i) {
+            // diagonal: kv tiles j with i*bq < (j+1)*bkv and j*bkv < (i+1)*bq
+            const int64_t lo = ((int64_t)i * spec->block_q) / spec->block_kv;
+            const int64_t hi = std::min<int64_t>(
+                ceil_div((int64_t)(i + 1) * spec->block_q, spec->block_kv) - 1, g.NK - 1);
+            std::fill(diag.begin(), diag.end(), 0ull);
+            for (int64_t j = lo; j <= hi; ++j) diag[j >> 6] |= 1ull << (j & 63);
+            const uint64_t* pw = pins ? p.pin_words.data() + ((int64_t)ps * g.NQ + i) * g.NKW : nullptr;
+            const uint64_t* dw = drops ? p.drop_words.data() + ((int64_t)ds * g.NQ + i) * g.NKW : nullptr;
+            int64_t c = 0, mk = 0;
+            for (int w = 0; w < g.NKW; ++w) {
+                const int rem = g.NK - 64 * w;
+                const uint64_t valid = rem >= 64 ? ~0ull : ((1ull << rem) - 1);
+                const uint64_t must = (diag[w] | (pw ? pw[w] : 0ull)) & valid;
+                const uint64_t forb = (dw ? dw[w] : 0ull) & valid;
+                c += __builtin_popcountll(valid & ~must & ~forb);
+                mk += __builtin_popcountll(must & ~forb);
+            }
+            const int64_t kr = keep_per_row(c, spec->budget);
+            if (kr < c) p.dense = false;
+            cnt[i] = (int32_t)(mk + std::min(kr, c));
+        }
+        slab_key.push_back(key);
+        slab_counts.push_back(std::move(cnt));
+        return slab_counts.back();
+    };
+    if (want_row_ptr) p.row_ptr.resize((size_t)g.rows + 1);
+    int64_t acc = 0;
+    int64_t r = 0;
+    if (want_row_ptr) p.row_ptr[0] = 0;
+    for (int b = 0; b < g.B; ++b)
+        for (int h = 0; h < g.Hsel; ++h) {
+            const int ps = (b % p.pb) * p.ph + (h % p.ph);
+            const int ds = (b % p.db) * p.dh + (h % p.dh);
+            const std::vector<int32_t>& cnt = counts_for(ps, ds);
+            for (int i = 0; i < g.NQ; ++i) {
+                acc += cnt[i];
+                ++r;
+                if (acc > INT32_MAX) return NSA_ERR_UNSUPPORTED;
+                if (want_row_ptr) p.row_ptr[r] = (int32_t)acc;
+            }
+        }
+    p.nnz = acc;
+    return NSA_OK;
+}
+
+struct WsLayout {
+    size_t pq = 0, pk = 0, mq = 0, mk = 0, scores = 0, pinw = 0, dropw = 0, total = 0;
+    int chunk = 1;
+};
+
+WsLayout ws_layout(const Geo& g, const nsa_spec* spec, bool has_pins, const nsa_mask* pins, bool has_drops,
+                   const nsa_mask* drops) {
+    WsLayout w;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    w.pq = take((size_t)g.B * g.Hq * g.NQ * g.D * 4);
+    w.pk = take((size_t)g.B * g.Hkv * g.NK * g.D * 4);
+    if (spec->head_shared) {
+        w.mq = take((size_t)g.B * g.NQ * g.D * 4);
+        w.mk = take((size_t)g.B * g.NK * g.D * 4);
+    }
+    // Head chunk of the score buffer, as score_blocks sizes it: as many heads
+    // as fit in score_chunk_bytes of NQ x NK fp32 scores, at least one.
+    const int64_t per_head = std::max<int64_t>((int64_t)g.NQ * g.NK * 4, 1);
+    w.chunk = (int)std::max<int64_t>(1, std::min<int64_t>(g.Hsel, spec->score_chunk_bytes / per_head));
+    w.scores = take((size_t)g.B * w.chunk * g.NQ * g.NK * 4);
+    if (has_pins) w.pinw = take((size_t)pins->b_dim * pins->h_dim * g.NQ * g.NKW * 8);
+    if (has_drops) w.dropw = take((size_t)drops->b_dim * drops->h_dim * g.NQ * g.NKW * 8);
+    w.total = off;
+    return w;
+}
+
+// Pinned host staging for the plan uploads, so that hipMemcpyAsync stays
+// asynchronous. A small ring per device; a slot is reused only after the copy
+// that last read it has completed.
+struct StagingSlot {
+    void* host = nullptr;
+    size_t cap = 0;
+    hipEvent_t done = nullptr;
+    bool pending = false;
+};
+struct Staging {
+    static constexpr int kSlots = 8;
+    std::mutex mu;
+    StagingSlot slot[64][kSlots];
+    int next[64] = {};
+};
+Staging& staging() {
+    static Staging* s = new Staging();  // lives until process exit
+    return *s;
+}
+
+// Copies the host ranges (src[x], bytes[x]) to dst[x] on `stream` through one
+// pinned staging slot.
+hipError_t upload(int n, void* const* dst, const void* const* src, const size_t* bytes, hipStream_t stream) {
+    size_t total = 0;
+    for (int x = 0; x < n; ++x) total += align256(bytes[x]);
+    if (total == 0) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    Staging& st = staging();
+    std::lock_guard<std::mutex> lock(st.mu);
+    StagingSlot& s = st.slot[dev][st.next[dev]];
+    st.next[dev] = (st.next[dev] + 1) % Staging::kSlots;
+    if (!s.done) {
+        if ((e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    if (s.pending) {
+        if ((e = hipEventSynchronize(s.done)) != hipSuccess) return e;
+        s.pending = false;
+    }
+    if (s.cap < total) {
+        if (s.host) (void)hipHostFree(s.host);
+        s.host = nullptr;
+        s.cap = 0;
+        const size_t cap = std::max<size_t>(total, 1 << 20);
+        if ((e = hipHostMalloc(&s.host, cap, hipHostMallocDefault)) != hipSuccess) return e;
+        s.cap = cap;
+    }
+    size_t off = 0;
+    for (int x = 0; x < n; ++x) {
+        if (bytes[x] == 0) continue;
+        char* h = (char*)s.host + off;
+        std::memcpy(h, src[x], bytes[x]);
+        if ((e = hipMemcpyAsync(dst[x], h, bytes[x], hipMemcpyHostToDevice, stream)) != hipSuccess) return e;
+        off += align256(bytes[x]);
+    }
+    if ((e = hipEventRecord(s.done, stream)) != hipSuccess) return e;
+    s.pending = true;
+    return hipSuccess;
+}
+
+// Enqueues pooling (+ head means) of q and k into the workspace.
+int run_pool(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, const Geo& g, const WsLayout& w,
+             char* ws, hipStream_t stream, const float** qh, const float** kh, int* Hk) {
+    hipError_t e;
+    float* pq = (float*)(ws + w.pq);
+    float* pk = (float*)(ws + w.pk);
+    if ((e = nsa::launch_pool(q->data, g.bf16, (int64_t)g.B * g.Hq, g.Sq, g.D, spec->block_q, pq, stream)) !=
+        hipSuccess)
+        return hip_fail(e);
+    if ((e = nsa::launch_pool(k->data, g.bf16, (int64_t)g.B * g.Hkv, g.Skv, g.D, spec->block_kv, pk,
+                              stream)) != hipSuccess)
+        return hip_fail(e);
+    if (spec->head_shared) {
+        float* mq = (float*)(ws + w.mq);
+        float* mk = (float*)(ws + w.mk);
+        if ((e = nsa::launch_head_mean(pq, g.B, g.Hq, g.NQ, g.D, mq, stream)) != hipSuccess) return hip_fail(e);
+        if ((e = nsa::launch_head_mean(pk, g.B, g.Hkv, g.NK, g.D, mk, stream)) != hipSuccess) return hip_fail(e);
+        *qh = mq;
+        *kh = mk;
+        *Hk = 1;
+    } else {
+        *qh = pq;
+        *kh = pk;
+        *Hk = g.Hkv;
+    }
+    return NSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nsa_version(void) { return "0.1.0"; }
+
+int nsa_last_hip_error(void) { return g_last_hip; }
+
+const char* nsa_status_string(int status) {
+    switch (status) {
+        case NSA_OK: return "ok";
+        case NSA_DENSE: return "dense: the budget covers every candidate tile, attend densely";
+        case NSA_ERR_NULL_ARG: return "a required pointer is NULL";
+        case NSA_ERR_BAD_SHAPE: return "inconsistent shapes (or Hq % Hkv != 0, or a mask that does not broadcast)";
+        case NSA_ERR_BAD_DTYPE: return "unsupported or mismatched dtype";
+        case NSA_ERR_UNSUPPORTED: return "valid request not supported by this build";
+        case NSA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case NSA_ERR_BAD_SPEC: return "invalid spec (block size <= 0, budget < 0 or NaN, chunk bytes < 0)";
+        case NSA_ERR_HIP: return "HIP runtime error (see nsa_last_hip_error)";
+        case NSA_ERR_CAPACITY: return "col_idx capacity is below the selection's nnz";
+        default: return "unknown status";
+    }
+}
+
+int nsa_select_sizes(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, const nsa_mask* pins,
+                     const nsa_mask* drops, nsa_sizes* out, int32_t* row_ptr_host) {
+    try {
+        if (!out) return NSA_ERR_NULL_ARG;
+        Geo g;
+        int st = validate_select(q, k, spec, pins, drops, g);
+        if (st != NSA_OK) return st;
+        Plan p;
+        st = build_plan(g, spec, pins, drops, p, row_ptr_host != nullptr);
+        if (st != NSA_OK) return st;
+        const WsLayout w = ws_layout(g, spec, pins != nullptr, pins, drops != nullptr, drops);
+        out->NQ = g.NQ;
+        out->NK = g.NK;
+        out->sel_heads = g.Hsel;
+        out->dense = (p.dense && !spec->force) ? 1 : 0;
+        out->rows = g.rows;
+        out->nnz = p.nnz;
+        out->workspace_bytes = (int64_t)w.total;
+        if (row_ptr_host) std::memcpy(row_ptr_host, p.row_ptr.data(), p.row_ptr.size() * sizeof(int32_t));
+        return NSA_OK;
+    } catch (const std::bad_alloc&) {
+        return NSA_ERR_UNSUPPORTED;
+    } catch (...) {
+        return NSA_ERR_UNSUPPORTED;
+    }
+}
+
+int nsa_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, const nsa_mask* pins,
+               const nsa_mask* drops, nsa_selection* out, void* workspace, size_t workspace_bytes,
+               void* stream_) {
+    try {
+        hipStream_t stream = (hipStream_t)stream_;
+        if (!out) return NSA_ERR_NULL_ARG;
+        Geo g;
+        int st = validate_select(q, k, spec, pins, drops, g);
+        if (st != NSA_OK) return st;
+        Plan p;
+        st = build_plan(g, spec, pins, drops, p, true);
+        if (st != NSA_OK) return st;
+        if (p.dense && !spec->force) return NSA_DENSE;
+        if (g.rows > 0 && (!out->keep || !out->row_ptr)) return NSA_ERR_NULL_ARG;
+        if (!out->row_ptr) return NSA_ERR_NULL_ARG;
+        if (p.nnz > 0 && !out->col_idx) return NSA_ERR_NULL_ARG;
+        if (out->col_capacity < p.nnz) return NSA_ERR_CAPACITY;
+        const WsLayout w = ws_layout(g, spec, pins != nullptr, pins, drops != nullptr, drops);
+        if (workspace_bytes < w.total) return NSA_ERR_WORKSPACE;
+        if (w.total > 0 && (!workspace || ((uintptr_t)workspace & 255))) return NSA_ERR_WORKSPACE;
+
+        out->nnz = p.nnz;
+        out->B = g.B;
+        out->H = g.Hsel;
+        out->NQ = g.NQ;
+        out->NK = g.NK;
+        out->block_q = spec->block_q;
+        out->block_kv = spec->block_kv;
+        out->seq_q = g.Sq;
+        out->seq_kv = g.Skv;
+        out->budget = spec->budget;
+
+        char* ws = (char*)workspace;
+        {
+            void* dst[3] = {out->row_ptr, ws + w.pinw, ws + w.dropw};
+            const void* src[3] = {p.row_ptr.data(), p.pin_words.data(), p.drop_words.data()};
+            size_t bytes[3] = {p.row_ptr.size() * sizeof(int32_t), pins ? p.pin_words.size() * 8 : 0,
+                               drops ? p.drop_words.size() * 8 : 0};
+            hipError_t e = upload(3, dst, src, bytes, stream);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        if (g.rows == 0 || g.NK == 0) return NSA_OK;
+
+        const float* qh;
+        const float* kh;
+        int Hk;
+        if ((st = run_pool(q, k, spec, g, w, ws, stream, &qh, &kh, &Hk)) != NSA_OK) return st;
+        float* scores = (float*)(ws + w.scores);
+        for (int h0 = 0; h0 < g.Hsel; h0 += w.chunk) {
+            const int nh = std::min(w.chunk, g.Hsel - h0);
+            hipError_t e = nsa::launch_scores(qh, kh, g.B, g.Hsel, Hk, g.group, h0, nh, g.NQ, g.NK, g.D, scores,
+                                              stream);
+            if (e != hipSuccess) return hip_fail(e);
+            nsa::TopkArgs ta;
+            ta.scores = scores;
+            ta.B = g.B;
+            ta.Hsel = g.Hsel;
+            ta.h0 = h0;
+            ta.nh = nh;
+            ta.NQ = g.NQ;
+            ta.NK = g.NK;
+            ta.NKW = g.NKW;
+            ta.block_q = spec->block_q;
+            ta.block_kv = spec->block_kv;
+            ta.budget = spec->budget;
+            ta.pin_words = pins ? (const uint64_t*)(ws + w.pinw) : nullptr;
+            ta.pb = p.pb;
+            ta.ph = p.ph;
+            ta.drop_words = drops ? (const uint64_t*)(ws + w.dropw) : nullptr;
+            ta.db = p.db;
+            ta.dh = p.dh;
+            ta.row_ptr = out->row_ptr;
+            ta.keep = out->keep;
+            ta.col_idx = out->col_idx;
+            if ((e = nsa::launch_topk(ta, stream)) != hipSuccess) return hip_fail(e);
+        }
+        return NSA_OK;
+    } catch (...) {
+        return NSA_ERR_UNSUPPORTED;
+    }
+}
+
+int nsa_pool_blocks(const nsa_tensor* x, int32_t block, float* out, void* stream) {
+    int st = check_tensor(x);
+    if (st != NSA_OK) return st;
+    if (block <= 0) return NSA_ERR_BAD_SPEC;
+    if (x->D != 64 && x->D != 128 && x->D != 256) return NSA_ERR_UNSUPPORTED;
+    const int64_t n = (int64_t)x->B * x->H * ceil_div(x->S, block) * x->D;
+    if (n > 0 && !out) return NSA_ERR_NULL_ARG;
+    hipError_t e = nsa::launch_pool(x->data, x->dtype == NSA_BF16, (int64_t)x->B * x->H, x->S, x->D, block, out,
+                                    (hipStream_t)stream);
+    return e == hipSuccess ? NSA_OK : hip_fail(e);
+}
+
+int nsa_score_blocks(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, float* scores,
+                     void* workspace, size_t workspace_bytes, void* stream_) {
+    try {
+        hipStream_t stream = (hipStream_t)stream_;
+        Geo g;
+        int st = validate_select(q, k, spec, nullptr, nullptr, g);
+        if (st != NSA_OK) return st;
+        const WsLayout w = ws_layout(g, spec, false, nullptr, false, nullptr);
+        if (workspace_bytes < w.total) return NSA_ERR_WORKSPACE;
+        if (w.total > 0 && (!workspace || ((uintptr_t)workspace & 255))) return NSA_ERR_WORKSPACE;
+        if (g.rows > 0 && g.NK > 0 && !scores) return NSA_ERR_NULL_ARG;
+        if (g.rows == 0 || g.NK == 0) return NSA_OK;
+        const float* qh;
+        const float* kh;
+        int Hk;
+        if ((st = run_pool(q, k, spec, g, w, (char*)workspace, stream, &qh, &kh, &Hk)) != NSA_OK) return st;
+        hipError_t e = nsa::launch_scores(qh, kh, g.B, g.Hsel, Hk, g.group, 0, g.Hsel, g.NQ, g.NK, g.D, scores,
+                                          stream);
+        return e == hipSuccess ? NSA_OK : hip_fail(e);
+    } catch (...) {
+        return NSA_ERR_UNSUPPORTED;
+    }
+}
+
+int nsa_block_sparse_attn(const nsa_tensor* q, const nsa_tensor* k, const nsa_tensor* v, const nsa_selection* sel,
+                          int causal, nsa_tensor* out, float* lse, void* stream_) {
+    hipStream_t stream = (hipStream_t)stream_;
+    int st;
+    if ((st = check_tensor(q)) != NSA_OK) return st;
+    if ((st = check_tensor(k)) != NSA_OK) return st;
+    if ((st = check_tensor(v)) != NSA_OK) return st;
+    if ((st = check_tensor(out)) != NSA_OK) return st;
+    if (q->dtype != k->dtype || q->dtype != v->dtype || q->dtype != out->dtype) return NSA_ERR_BAD_DTYPE;
+    if (q->B != k->B || q->B != v->B || k->H != v->H || k->S != v->S) return NSA_ERR_BAD_SHAPE;
+    if (q->D != k->D || q->D != v->D) return NSA_ERR_BAD_SHAPE;
+    if (out->B != q->B || out->H != q->H || out->S != q->S || out->D != q->D) return NSA_ERR_BAD_SHAPE;
+    if (q->H % k->H != 0) return NSA_ERR_BAD_SHAPE;
+    if (numel(q) > 0 && !lse) return NSA_ERR_NULL_ARG;
+    if (causal && q->S != k->S) return NSA_ERR_UNSUPPORTED;
+    if (q->D != 64 && q->D != 128) return NSA_ERR_UNSUPPORTED;
+    if (q->S != k->S) return NSA_ERR_UNSUPPORTED;
+
+    nsa::AttnArgs a;
+    a.q = q->data;
+    a.k = k->data;
+    a.v = v->data;
+    a.out = out->data;
+    a.lse = lse;
+    a.B = q->B;
+    a.Hq = q->H;
+    a.Hkv = k->H;
+    a.S = q->S;
+    a.D = q->D;
+    a.causal = causal ? 1 : 0;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)q->D));
+    if (sel) {
+        if (!sel->row_ptr) return NSA_ERR_NULL_ARG;
+        if (sel->nnz > 0 && !sel->col_idx) return NSA_ERR_NULL_ARG;
+        if (sel->block_q <= 0 || sel->block_kv <= 0) return NSA_ERR_BAD_SPEC;
+        if (sel->B != q->B || (sel->H != 1 && sel->H != q->H)) return NSA_ERR_BAD_SHAPE;
+        if (sel->seq_q != q->S || sel->seq_kv != k->S) return NSA_ERR_BAD_SHAPE;
+        if (sel->NQ != ceil_div(q->S, sel->block_q) || sel->NK != ceil_div(k->S, sel->block_kv))
+            return NSA_ERR_BAD_SHAPE;
+        a.row_ptr = sel->row_ptr;
+        a.col_idx = sel->col_idx;
+        a.Hsel = sel->H;
+        a.block_q = sel->block_q;
+        a.block_kv = sel->block_kv;
+    } else {
+        a.row_ptr = nullptr;
+        a.col_idx = nullptr;
+        a.Hsel = q->H;
+        a.block_q = 128;
+        a.block_kv = 64;
+    }
+    a.NQ = (int)ceil_div(q->S, a.block_q);
+    a.NK = (int)ceil_div(k->S, a.block_kv);
+    if ((int64_t)a.B * a.Hq * a.NQ == 0) return NSA_OK;
+    const int bf16 = q->dtype == NSA_BF16;
+    hipError_t e = nsa::attn_mfma_supported(a, bf16) ? nsa::launch_attn_mfma(a, stream)
+                                                       : nsa::launch_attn_simt(a, bf16, stream);
+    return e == hipSuccess ? NSA_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Internal launch interface between the C ABI (nsa_api.cpp) and the HIP
+// kernels. Every launcher enqueues on `stream` and returns the hipError_t of
+// the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nsa {
+
+// ---- selection stage -------------------------------------------------------
+
+// Mean over blocks of `block` tokens: x (heads, S, D) -> out (heads, N, D) fp32.
+hipError_t launch_pool(const void* x, int bf16, int64_t heads, int S, int D, int block,
+                       float* out, hipStream_t stream);
+
+// out[b, n, :] = mean over h of in[b, h, n, :]  (in: (B, H, N, D) fp32).
+hipError_t launch_head_mean(const float* in, int B, int H, int N, int D, float* out,
+                            hipStream_t stream);
+
+// Scores for selection heads [h0, h0 + nh): s[b, h - h0, i, j] = qh[b, h, i] . kh[b, h / group, j]
+// qh: (B, Hsel, NQ, D) fp32, kh: (B, Hk, NK, D) fp32, s: (B, nh, NQ, NK) fp32.
+hipError_t launch_scores(const float* qh, const float* kh, int B, int Hsel, int Hk, int group,
+                         int h0, int nh, int NQ, int NK, int D, float* s, hipStream_t stream);
+
+// Per-row top-k over the score chunk of heads [h0, h0 + nh) and CSR emission.
+struct TopkArgs {
+    const float* scores;       // (B, nh, NQ, NK)
+    int B, Hsel, h0, nh, NQ, NK, NKW;
+    int block_q, block_kv;
+    float budget;
+    const uint64_t* pin_words; // (pb, ph, NQ, NKW) or null; bit (j % 64) of word j / 64
+    int pb, ph;
+    const uint64_t* drop_words;
+    int db, dh;
+    const int32_t* row_ptr;    // (B*Hsel*NQ + 1)
+    int8_t* keep;              // (B, Hsel, NQ, NK)
+    int32_t* col_idx;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+
+// ---- attention stage -------------------------------------------------------
+
+struct AttnArgs {
+    const void* q;            // (B, Hq, S, D)
+    const void* k;            // (B, Hkv, S, D)
+    const void* v;
+    void* out;                // (B, Hq, S, D), dtype of q
+    float* lse;               // (B, Hq, S)
+    const int32_t* row_ptr;   // null = dense
+    const int32_t* col_idx;
+    int B, Hq, Hkv, Hsel, S, D, NQ, NK, block_q, block_kv;
+    int causal;
+    float scale_log2;         // D^-1/2 * log2(e)
+};
+// bf16 MFMA path: block_q in {32, 64, 96, 128}, block_kv == 64, D in {64, 128}.
+bool attn_mfma_supported(const AttnArgs& a, int bf16);
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream);
+// General path (fp32 or bf16 inputs, any block sizes, D in {64, 128}).
+hipError_t launch_attn_simt(const AttnArgs& a, int bf16, hipStream_t stream);
+
+}  // namespace nsa

@@ -1,0 +1,464 @@
+// Selection-stage kernels for gfx950 (CDNA4): pooling, head means, the pooled
+// score product on fp32 MFMA, and the per-row top-k with CSR compaction.
+//
+// What is computed follows the page "automatic/modules/attention/sparse/selector.py"
+// (pool_blocks, score_blocks, diagonal_blocks, selection_plan, select_blocks).
+// How it is computed is designed for CDNA4: one 64-lane wavefront per pooled
+// tile or per selection row, 16-byte coalesced loads, MFMA for the dense
+// contraction, ballot/popcount for the compaction.
+#include "nsa_internal.h"
+
+#include <float.h>
+
+namespace nsa {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Order LDS traffic between the lanes of one wavefront (no workgroup barrier:
+// waves of a workgroup progress independently here).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+__device__ __forceinline__ float wave_min_f(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float wave_max_f(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+
+// ---------------------------------------------------------------- pooling
+//
+// One wavefront pools one tile of `block` token rows of one head. A token row
+// of D elements is split into CPR 16-byte chunks; the 64 lanes cover RG = 64/CPR
+// rows at a time, so each load instruction of the wave reads 1 KiB of
+// contiguous memory. Per lane the sum runs in fp32 over its rows, then the RG
+// partial sums are added across lanes and divided by the tile's real length.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ xv, float* __restrict__ out,
+                                                   int S, int block, int ntiles, int64_t total) {
+    constexpr int ESZ = BF16 ? 2 : 4;
+    constexpr int VEC = 16 / ESZ;      // elements per 16-byte chunk
+    constexpr int CPR = D / VEC;       // chunks per token row
+    constexpr int RG = 64 / CPR;       // rows in flight per wave instruction
+    static_assert(CPR <= 64 && 64 % CPR == 0, "row must split evenly over the wave");
+    const int lane = threadIdx.x & 63;
+    const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (tile >= total) return;
+    const int64_t head = tile / ntiles;
+    const int i = (int)(tile - head * ntiles);
+    const int c = lane % CPR, rg = lane / CPR;
+    const int t0 = i * block;
+    const int len = min(block, S - t0);
+    const char* base = (const char*)xv + ((head * S + t0) * (int64_t)D + (int64_t)c * VEC) * ESZ;
+    const int64_t row_bytes = (int64_t)D * ESZ;
+
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+
+    auto add = [&](u32x4 w) {
+        if constexpr (BF16) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += bf16lo(w[e]);
+                acc[2 * e + 1] += bf16hi(w[e]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(w[e]);
+        }
+    };
+
+    int r = rg;
+    constexpr int U = 8;  // loads in flight per lane
+    for (; r + (U - 1) * RG < len; r += U * RG) {
+        u32x4 w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            w[u] = __builtin_nontemporal_load((const u32x4*)(base + (int64_t)(r + u * RG) * row_bytes));
+#pragma unroll
+        for (int u = 0; u < U; ++u) add(w[u]);
+    }
+    for (; r < len; r += RG) add(*(const u32x4*)(base + (int64_t)r * row_bytes));
+
+#pragma unroll
+    for (int off = CPR; off < 64; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
+    }
+    if (rg == 0) {
+        const float n = (float)len;
+        float* o = out + tile * D + c * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+            f32x4 v = {acc[e] / n, acc[e + 1] / n, acc[e + 2] / n, acc[e + 3] / n};
+            *(f32x4*)(o + e) = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- head means
+__global__ __launch_bounds__(256) void head_mean_kernel(const float* __restrict__ in, float* __restrict__ out,
+                                                        int B, int H, int N, int D) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t per_b = (int64_t)N * D;
+    if (idx >= (int64_t)B * per_b) return;
+    const int64_t b = idx / per_b, nd = idx - b * per_b;
+    const float* p = in + b * H * per_b + nd;
+    float s = 0.f;
+    for (int h = 0; h < H; ++h) s += p[(int64_t)h * per_b];
+    out[idx] = s / (float)H;
+}
+
+// ---------------------------------------------------------------- scores
+//
+// One wavefront computes a 64 x 64 block of one head's score matrix with
+// v_mfma_f32_32x32x2_f32 (2 x 2 blocks of 32 x 32). The contraction index is
+// split between the two lane halves: at step s lane half hf supplies
+// d = kc + 8*hf + s, so every lane reads 8 consecutive floats of its row. The
+// pooled operands are small and stay in L2.
+template <int D>
+__global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qh, const float* __restrict__ kh,
+                                                    int Hsel, int Hk, int group, int h0, int nh, int NQ,
+                                                    int NK, int nbi, int nbj, float* __restrict__ s) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nbj4 = (nbj + 3) >> 2;
+    int64_t wid = blockIdx.x;
+    const int bj = (int)(wid % nbj4) * 4 + wave;
+    wid /= nbj4;
+    const int bi = (int)(wid % nbi);
+    wid /= nbi;
+    const int hl = (int)(wid % nh);
+    const int b = (int)(wid / nh);
+    if (bj >= nbj) return;
+    const int h = h0 + hl;
+    const int hk = (Hk == 1) ? 0 : h / group;
+    const float* A = qh + ((int64_t)b * Hsel + h) * NQ * D;
+    const float* Bm = kh + ((int64_t)b * Hk + hk) * NK * D;
+    const int i0 = bi * 64, j0 = bj * 64;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const float* a0p = A + (int64_t)min(i0 + l32, NQ - 1) * D + 8 * hf;
+    const float* a1p = A + (int64_t)min(i0 + 32 + l32, NQ - 1) * D + 8 * hf;
+    const float* b0p = Bm + (int64_t)min(j0 + l32, NK - 1) * D + 8 * hf;
+    const float* b1p = Bm + (int64_t)min(j0 + 32 + l32, NK - 1) * D + 8 * hf;
+
+    f32x16 c00 = {}, c01 = {}, c10 = {}, c11 = {};
+#pragma unroll 2
+    for (int kc = 0; kc < D; kc += 16) {
+        f32x4 a0[2], a1[2], b0[2], b1[2];
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            a0[v] = *(const f32x4*)(a0p + kc + 4 * v);
+            a1[v] = *(const f32x4*)(a1p + kc + 4 * v);
+            b0[v] = *(const f32x4*)(b0p + kc + 4 * v);
+            b1[v] = *(const f32x4*)(b1p + kc + 4 * v);
+        }
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const float x0 = a0[st >> 2][st & 3], x1 = a1[st >> 2][st & 3];
+            const float y0 = b0[st >> 2][st & 3], y1 = b1[st >> 2][st & 3];
+            c00 = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, y0, c00, 0, 0, 0);
+            c01 = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, y1, c01, 0, 0, 0);
+            c10 = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, y0, c10, 0, 0, 0);
+            c11 = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, y1, c11, 0, 0, 0);
+        }
+    }
+    // Accumulator layout of a 32 x 32 block: lane holds column l32 and rows
+    // 8*q + 4*hf + e at element 4*q + e.
+    float* out = s + ((int64_t)b * nh + hl) * NQ * NK;
+    auto store = [&](const f32x16& c, int ib, int jb) {
+        const int col = j0 + jb + l32;
+        if (col >= NK) return;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = i0 + ib + 8 * q + 4 * hf + e;
+                if (row < NQ) out[(int64_t)row * NK + col] = c[4 * q + e];
+            }
+    };
+    store(c00, 0, 0);
+    store(c01, 0, 32);
+    store(c10, 32, 0);
+    store(c11, 32, 32);
+}
+
+// ---------------------------------------------------------------- top-k
+//
+// One wavefront per selection row. Element j = 64*t + lane sits in register
+// slot t of lane `lane`, so the 64-bit ballot of slot t is exactly word t of
+// the row's bit masks (pins, drops, keep).
+//
+// Exact top-k by value bucketing: every candidate is mapped to one of 256
+// buckets by a function of its score that never decreases as the score grows
+// (fp32 subtract and multiply by a positive constant, truncation; the row
+// maximum gets the top bucket). Buckets strictly above the bucket holding the
+// k-th largest score are taken whole, the rest dropped, and the search repeats
+// inside that bucket until what is left is either exactly what is needed or a
+// set of equal scores, which is then taken in ascending kv index order. This
+// picks the first k candidates in (score descending, index ascending) order;
+// -0.0 and +0.0 fall into the same bucket and tie.
+template <int EPL>
+struct MaskT { typedef uint32_t type; };
+template <>
+struct MaskT<64> { typedef uint64_t type; };
+
+template <int EPL>
+__device__ typename MaskT<EPL>::type select_top(const float (&s)[EPL], typename MaskT<EPL>::type active,
+                                                int need, uint32_t* hist, int lane) {
+    typedef typename MaskT<EPL>::type M;
+    M picked = 0;
+    for (int iter = 0; iter < 64 && need > 0; ++iter) {
+        int mine = __builtin_popcountll((uint64_t)active);
+        const int na = wave_sum_i(mine);
+        if (na <= need) {
+            picked |= active;
+            active = 0;
+            need = 0;
+            break;
+        }
+        float lo = FLT_MAX, hi = -FLT_MAX;
+#pragma unroll
+        for (int t = 0; t < EPL; ++t)
+            if ((active >> t) & 1) {
+                lo = fminf(lo, s[t]);
+                hi = fmaxf(hi, s[t]);
+            }
+        lo = wave_min_f(lo);
+        hi = wave_max_f(hi);
+        if (!(hi > lo)) break;  // every remaining score is equal: index order below
+        const bool half = !(hi - lo <= FLT_MAX);
+        const float lo_u = half ? 0.5f * lo : lo;
+        const float range = half ? 0.5f * hi - 0.5f * lo : hi - lo;
+        float scale = 255.0f / range;
+        if (!(scale <= FLT_MAX)) scale = FLT_MAX;
+        auto bucket = [&](float x) -> int {
+            if (x == hi) return 255;
+            const float u = ((half ? 0.5f * x : x) - lo_u) * scale;
+            const int b = (int)u;
+            return b > 254 ? 254 : (b < 0 ? 0 : b);
+        };
+        for (int q = lane; q < 256; q += 64) hist[q] = 0;
+        wave_lds_sync();
+#pragma unroll
+        for (int t = 0; t < EPL; ++t)
+            if ((active >> t) & 1) atomicAdd(&hist[bucket(s[t])], 1u);
+        wave_lds_sync();
+        // Lane L owns buckets 4L .. 4L+3. Count what lies strictly above each.
+        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
+                       h3 = hist[4 * lane + 3];
+        const int own = (int)(h0 + h1 + h2 + h3);
+        int above_lane = 0;  // sum over lanes with a larger index
+        {
+            int x = own;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_down(x, o);
+                if (lane + o < 64) x += y;
+            }
+            above_lane = x - own;  // inclusive suffix minus own
+        }
+        int found = -1, found_above = 0;
+        {
+            int ab = above_lane;
+            const uint32_t hh[4] = {h3, h2, h1, h0};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int q = 4 * lane + 3 - e;
+                if (found < 0 && ab < need && need <= ab + (int)hh[e]) {
+                    found = q;
+                    found_above = ab;
+                }
+                ab += (int)hh[e];
+            }
+        }
+        wave_lds_sync();
+        const uint64_t who = __ballot(found >= 0);
+        const int src = __builtin_ctzll(who);
+        const int bstar = __shfl(found, src);
+        const int above = __shfl(found_above, src);
+        M next = 0;
+#pragma unroll
+        for (int t = 0; t < EPL; ++t)
+            if ((active >> t) & 1) {
+                const int bk = bucket(s[t]);
+                if (bk > bstar) picked |= (M)1 << t;
+                else if (bk == bstar) next |= (M)1 << t;
+            }
+        active = next;
+        need -= above;
+    }
+    if (need > 0) {
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+        for (int t = 0; t < EPL; ++t) {
+            const bool a = (active >> t) & 1;
+            const uint64_t m = __ballot(a);
+            const int cnt = __builtin_popcountll(m);
+            if (cnt <= need) {
+                if (a) picked |= (M)1 << t;
+                need -= cnt;
+            } else {
+                if (a && __builtin_popcountll(m & below) < need) picked |= (M)1 << t;
+                need = 0;
+            }
+            if (need == 0) break;
+        }
+    }
+    return picked;
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+    typedef typename MaskT<EPL>::type M;
+    __shared__ uint32_t hist_all[4][256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t* hist = hist_all[wave];
+    const int64_t lr = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t nrows = (int64_t)a.B * a.nh * a.NQ;
+    if (lr >= nrows) return;
+    const int i = (int)(lr % a.NQ);
+    const int64_t bh = lr / a.NQ;
+    const int hl = (int)(bh % a.nh);
+    const int b = (int)(bh / a.nh);
+    const int h = a.h0 + hl;
+    const int64_t r = ((int64_t)b * a.Hsel + h) * a.NQ + i;
+    const float* srow = a.scores + lr * a.NK;
+    const uint64_t* pw =
+        a.pin_words ? a.pin_words + (((int64_t)(b % a.pb) * a.ph + (h % a.ph)) * a.NQ + i) * a.NKW : nullptr;
+    const uint64_t* dw =
+        a.drop_words ? a.drop_words + (((int64_t)(b % a.db) * a.dh + (h % a.dh)) * a.NQ + i) * a.NKW : nullptr;
+    const int64_t qlo = (int64_t)i * a.block_q, qhi = (int64_t)(i + 1) * a.block_q;
+
+    float s[EPL];
+    M cand = 0, must_kept = 0;
+#pragma unroll
+    for (int t = 0; t < EPL; ++t) {
+        const int j = 64 * t + lane;
+        const bool valid = j < a.NK;
+        s[t] = valid ? srow[j] : 0.f;
+        const bool in_words = 64 * t < a.NK;
+        const bool pin = (pw && in_words) ? ((pw[t] >> lane) & 1) : false;
+        const bool drop = (dw && in_words) ? ((dw[t] >> lane) & 1) : false;
+        const bool diag = (qlo < (int64_t)(j + 1) * a.block_kv) && ((int64_t)j * a.block_kv < qhi);
+        const bool must = valid && (diag || pin);
+        const bool forb = valid && drop;
+        if (valid && !must && !forb) cand |= (M)1 << t;
+        if (must && !forb) must_kept |= (M)1 << t;
+    }
+    const int c = wave_sum_i(__builtin_popcountll((uint64_t)cand));
+    // k_r = ceil(fl32(c) * fl32(budget)): the product rounds to fp32 first.
+    const float kf = ceilf(__fmul_rn((float)c, a.budget));
+    const int k = (kf >= (float)c) ? c : (int)kf;
+    M picked = 0;
+    if (k >= c) picked = cand;
+    else if (k > 0) picked = select_top<EPL>(s, cand, k, hist, lane);
+    const M keepm = must_kept | picked;
+
+    int8_t* krow = a.keep + r * a.NK;
+    const int32_t row_begin = a.row_ptr[r];
+    const int32_t row_len = a.row_ptr[r + 1] - row_begin;  // planned on the host from the same rule
+    int32_t* crow = a.col_idx + row_begin;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int pos = 0;
+#pragma unroll
+    for (int t = 0; t < EPL; ++t) {
+        const int j = 64 * t + lane;
+        const bool kb = (keepm >> t) & 1;
+        if (j < a.NK) krow[j] = kb ? 1 : 0;
+        const uint64_t m = __ballot(kb);
+        const int slot = pos + __builtin_popcountll(m & below);
+        if (kb && slot < row_len) crow[slot] = j;  // never write past the planned row
+        pos += __builtin_popcountll(m);
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_pool(const void* x, int bf16, int64_t heads, int S, int D, int block, float* out,
+                       hipStream_t stream) {
+    const int ntiles = (S + block - 1) / block;
+    const int64_t total = heads * ntiles;
+    if (total == 0) return hipSuccess;
+    const dim3 grid((unsigned)((total + 3) / 4));
+#define NSA_POOL(DD, BB)                                                                          \
+    hipLaunchKernelGGL((pool_kernel<DD, BB>), grid, dim3(256), 0, stream, x, out, S, block, ntiles, total)
+    if (bf16) {
+        if (D == 64) NSA_POOL(64, true);
+        else if (D == 128) NSA_POOL(128, true);
+        else if (D == 256) NSA_POOL(256, true);
+        else return hipErrorInvalidValue;
+    } else {
+        if (D == 64) NSA_POOL(64, false);
+        else if (D == 128) NSA_POOL(128, false);
+        else if (D == 256) NSA_POOL(256, false);
+        else return hipErrorInvalidValue;
+    }
+#undef NSA_POOL
+    return hipGetLastError();
+}
+
+hipError_t launch_head_mean(const float* in, int B, int H, int N, int D, float* out, hipStream_t stream) {
+    const int64_t total = (int64_t)B * N * D;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(head_mean_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, in,
+                       out, B, H, N, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_scores(const float* qh, const float* kh, int B, int Hsel, int Hk, int group, int h0, int nh,
+                         int NQ, int NK, int D, float* s, hipStream_t stream) {
+    if (NQ == 0 || NK == 0 || nh == 0 || B == 0) return hipSuccess;
+    const int nbi = (NQ + 63) / 64, nbj = (NK + 63) / 64;
+    const int64_t blocks = (int64_t)B * nh * nbi * ((nbj + 3) / 4);
+    const dim3 grid((unsigned)blocks);
+#define NSA_SCORE(DD)                                                                                 \
+    hipLaunchKernelGGL((score_kernel<DD>), grid, dim3(256), 0, stream, qh, kh, Hsel, Hk, group, h0, nh, NQ, \
+                       NK, nbi, nbj, s)
+    if (D == 64) NSA_SCORE(64);
+    else if (D == 128) NSA_SCORE(128);
+    else if (D == 256) NSA_SCORE(256);
+    else return hipErrorInvalidValue;
+#undef NSA_SCORE
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
+    const int64_t rows = (int64_t)a.B * a.nh * a.NQ;
+    if (rows == 0 || a.NK == 0) return hipSuccess;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    const int epl = (a.NK + 63) / 64;
+#define NSA_TOPK(E) hipLaunchKernelGGL((topk_kernel<E>), grid, dim3(256), 0, stream, a)
+    if (epl <= 1) NSA_TOPK(1);
+    else if (epl <= 2) NSA_TOPK(2);
+    else if (epl <= 4) NSA_TOPK(4);
+    else if (epl <= 8) NSA_TOPK(8);
+    else if (epl <= 16) NSA_TOPK(16);
+    else if (epl <= 32) NSA_TOPK(32);
+    else if (epl <= 64) NSA_TOPK(64);
+    else return hipErrorInvalidValue;
+#undef NSA_TOPK
+    return hipGetLastError();
+}
+
+}  // namespace nsa

@@ -1,0 +1,270 @@
+"""Python binding of the C ABI in include/nsa.h (ctypes; argument marshalling only).
+
+Every step of the path runs in the HIP library ``libnsa.so`` built next to this
+file; torch supplies device memory and the current stream. There is no CPU or
+eager fallback: when the library is missing every call raises.
+
+Names follow the C ABI: ``nsa_select``, ``nsa_block_sparse_attn``,
+``nsa_select_sizes``, ``nsa_pool_blocks``, ``nsa_score_blocks``,
+``nsa_status_string``. ``SparseSpec`` and ``Selection`` mirror the SparseSpec and
+BlockSelection of the page "automatic/modules/attention/sparse/selector.py".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+__all__ = [
+    "SparseSpec", "Selection", "Sizes", "NsaError", "lib", "nsa_select_sizes", "nsa_select",
+    "nsa_block_sparse_attn", "nsa_pool_blocks", "nsa_score_blocks", "nsa_status_string",
+    "LIB_PATH", "EXPORTS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnsa.so")
+EXPORTS = ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_pool_blocks",
+           "nsa_score_blocks", "nsa_status_string", "nsa_last_hip_error", "nsa_version")
+
+NSA_OK, NSA_DENSE = 0, 1
+NSA_F32, NSA_BF16 = 0, 1
+
+
+class NsaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {nsa_status_string(status)} (status {status})")
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("B", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("S", ctypes.c_int32), ("D", ctypes.c_int32)]
+
+
+class _Spec(ctypes.Structure):
+    _fields_ = [("budget", ctypes.c_float), ("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32),
+                ("head_shared", ctypes.c_int32), ("force", ctypes.c_int32),
+                ("score_chunk_bytes", ctypes.c_int64)]
+
+
+class _Mask(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("b_dim", ctypes.c_int32), ("h_dim", ctypes.c_int32),
+                ("nq", ctypes.c_int32), ("nk", ctypes.c_int32)]
+
+
+class _Selection(ctypes.Structure):
+    _fields_ = [("keep", ctypes.c_void_p), ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
+                ("col_capacity", ctypes.c_int64), ("nnz", ctypes.c_int64),
+                ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("NQ", ctypes.c_int32), ("NK", ctypes.c_int32),
+                ("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32),
+                ("seq_q", ctypes.c_int32), ("seq_kv", ctypes.c_int32), ("budget", ctypes.c_float)]
+
+
+class _Sizes(ctypes.Structure):
+    _fields_ = [("NQ", ctypes.c_int32), ("NK", ctypes.c_int32), ("sel_heads", ctypes.c_int32),
+                ("dense", ctypes.c_int32), ("rows", ctypes.c_int64), ("nnz", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libnsa.so (raises if it was not built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m top_kv_tile_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        L.nsa_select_sizes.argtypes = [P(_Tensor), P(_Tensor), P(_Spec), P(_Mask), P(_Mask), P(_Sizes),
+                                       ctypes.c_void_p]
+        L.nsa_select.argtypes = [P(_Tensor), P(_Tensor), P(_Spec), P(_Mask), P(_Mask), P(_Selection),
+                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.nsa_block_sparse_attn.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Selection), ctypes.c_int,
+                                            P(_Tensor), ctypes.c_void_p, ctypes.c_void_p]
+        L.nsa_pool_blocks.argtypes = [P(_Tensor), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        L.nsa_score_blocks.argtypes = [P(_Tensor), P(_Tensor), P(_Spec), ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_size_t, ctypes.c_void_p]
+        L.nsa_status_string.argtypes = [ctypes.c_int]
+        L.nsa_status_string.restype = ctypes.c_char_p
+        L.nsa_version.restype = ctypes.c_char_p
+        for name in ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_pool_blocks",
+                     "nsa_score_blocks", "nsa_last_hip_error"):
+            getattr(L, name).restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def nsa_status_string(status: int) -> str:
+    return lib().nsa_status_string(int(status)).decode()
+
+
+@dataclass(frozen=True)
+class SparseSpec:
+    """Selection spec (defaults of SparseSpec on the selection page)."""
+    budget: float = 0.30
+    block_q: int = 128
+    block_kv: int = 64
+    head_shared: bool = False
+    force: bool = False
+    score_chunk_bytes: int = 256 << 20
+
+    def _c(self) -> _Spec:
+        return _Spec(float(self.budget), int(self.block_q), int(self.block_kv), int(bool(self.head_shared)),
+                     int(bool(self.force)), int(self.score_chunk_bytes))
+
+
+@dataclass
+class Sizes:
+    NQ: int
+    NK: int
+    sel_heads: int
+    dense: bool
+    rows: int
+    nnz: int
+    workspace_bytes: int
+
+
+@dataclass
+class Selection:
+    """Keep flags and CSR of a block selection (device tensors)."""
+    keep: torch.Tensor       # int8 (B, H', NQ, NK)
+    row_ptr: torch.Tensor    # int32 (B*H'*NQ + 1)
+    col_idx: torch.Tensor    # int32 (nnz)
+    block_q: int
+    block_kv: int
+    budget: float
+    seq_q: int
+    seq_kv: int
+
+    @property
+    def shape(self):
+        return tuple(self.keep.shape)
+
+    @property
+    def nnz(self) -> int:
+        return int(self.col_idx.numel())
+
+    def density(self) -> float:
+        """Fraction of tiles kept; reads back from the device (reporting and tests only)."""
+        return float(self.keep.sum().item()) / max(self.keep.numel(), 1)
+
+    def _c(self) -> _Selection:
+        B, H, NQ, NK = self.keep.shape
+        return _Selection(self.keep.data_ptr(), self.row_ptr.data_ptr(),
+                          self.col_idx.data_ptr() if self.col_idx.numel() else None,
+                          self.col_idx.numel(), self.col_idx.numel(), B, H, NQ, NK, self.block_q,
+                          self.block_kv, self.seq_q, self.seq_kv, float(self.budget))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return NSA_F32
+    if t.dtype == torch.bfloat16:
+        return NSA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _tensor(t: torch.Tensor) -> _Tensor:
+    if t.dim() != 4:
+        raise ValueError("tensors are 4-D (B, H, S, D)")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    B, H, S, D = t.shape
+    return _Tensor(t.data_ptr() if t.numel() else None, _dtype_code(t), B, H, S, D)
+
+
+def _mask(m, keepalive: list):
+    if m is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(m).astype(np.int8, copy=False))
+    if a.ndim != 4:
+        raise ValueError("masks are 4-D (B|1, H'|1, NQ, NK)")
+    keepalive.append(a)
+    return ctypes.pointer(_Mask(a.ctypes.data if a.size else None, *a.shape))
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(status: int, what: str):
+    if status < 0:
+        raise NsaError(status, what)
+    return status
+
+
+def nsa_select_sizes(q: torch.Tensor, k: torch.Tensor, spec: SparseSpec, pins=None, drops=None) -> Sizes:
+    keep = []
+    out = _Sizes()
+    _check(lib().nsa_select_sizes(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)), ctypes.byref(spec._c()),
+                                  _mask(pins, keep), _mask(drops, keep), ctypes.byref(out), None),
+           "nsa_select_sizes")
+    return Sizes(out.NQ, out.NK, out.sel_heads, bool(out.dense), out.rows, out.nnz, out.workspace_bytes)
+
+
+def nsa_select(q: torch.Tensor, k: torch.Tensor, spec: SparseSpec = SparseSpec(), pins=None, drops=None,
+               stream=None, workspace: torch.Tensor | None = None):
+    """select_blocks: returns a Selection, or None when the dense short circuit applies."""
+    sizes = nsa_select_sizes(q, k, spec, pins, drops)
+    if sizes.dense:
+        return None
+    dev = q.device
+    B = q.shape[0]
+    keep = torch.empty((B, sizes.sel_heads, sizes.NQ, sizes.NK), dtype=torch.int8, device=dev)
+    row_ptr = torch.empty(sizes.rows + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(sizes.nnz, dtype=torch.int32, device=dev)
+    if workspace is None or workspace.numel() < sizes.workspace_bytes:
+        workspace = torch.empty(max(sizes.workspace_bytes, 1), dtype=torch.uint8, device=dev)
+    sel = Selection(keep, row_ptr, col_idx, spec.block_q, spec.block_kv, spec.budget, q.shape[2], k.shape[2])
+    csel = sel._c()
+    hold = []
+    st = _check(lib().nsa_select(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)), ctypes.byref(spec._c()),
+                                 _mask(pins, hold), _mask(drops, hold), ctypes.byref(csel),
+                                 ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)),
+                "nsa_select")
+    if st == NSA_DENSE:
+        return None
+    return sel
+
+
+def nsa_block_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, selection: Selection | None,
+                          causal: bool, stream=None, out: torch.Tensor | None = None,
+                          lse: torch.Tensor | None = None):
+    """Attention over the kept tiles; returns (out in q's dtype, lse fp32 (B, Hq, S))."""
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    csel = ctypes.byref(selection._c()) if selection is not None else None
+    _check(lib().nsa_block_sparse_attn(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)),
+                                       ctypes.byref(_tensor(v)), csel, int(bool(causal)),
+                                       ctypes.byref(_tensor(out)), ctypes.c_void_p(lse.data_ptr()),
+                                       _stream(stream)),
+           "nsa_block_sparse_attn")
+    return out, lse
+
+
+def nsa_pool_blocks(x: torch.Tensor, block: int, stream=None) -> torch.Tensor:
+    n = -(-x.shape[2] // block)
+    out = torch.empty((x.shape[0], x.shape[1], n, x.shape[3]), dtype=torch.float32, device=x.device)
+    _check(lib().nsa_pool_blocks(ctypes.byref(_tensor(x)), int(block), ctypes.c_void_p(out.data_ptr()),
+                                 _stream(stream)), "nsa_pool_blocks")
+    return out
+
+
+def nsa_score_blocks(q: torch.Tensor, k: torch.Tensor, spec: SparseSpec, stream=None) -> torch.Tensor:
+    sizes = nsa_select_sizes(q, k, SparseSpec(budget=0.0, block_q=spec.block_q, block_kv=spec.block_kv,
+                                              head_shared=spec.head_shared, force=True,
+                                              score_chunk_bytes=spec.score_chunk_bytes))
+    ws = torch.empty(max(sizes.workspace_bytes, 1), dtype=torch.uint8, device=q.device)
+    s = torch.empty((q.shape[0], sizes.sel_heads, sizes.NQ, sizes.NK), dtype=torch.float32, device=q.device)
+    _check(lib().nsa_score_blocks(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)), ctypes.byref(spec._c()),
+                                  ctypes.c_void_p(s.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                  _stream(stream)), "nsa_score_blocks")
+    return s

@@ -1,0 +1,254 @@
+"""Benchmark of the hot path on one MI355X: top-k KV-tile selection + block-sparse attention.
+
+One step = nsa_select (pool, score, top-k, CSR) + nsa_block_sparse_attn over one
+batch of the long-context workload (B 1, Hq 64, Hkv 8, S 131072, D 128, bf16,
+causal, block_q 128 / block_kv 64, budget 0.05, sink tile pinned, 1% of
+non-diagonal tiles dropped), inputs resident in HBM.
+
+value = attention FLOPs over kept tiles (tiles entirely in the causal future
+excluded, full tile area otherwise: 4 * D * |Q_i| * |K_j| per kept tile and
+query head) divided by the wall time of a whole step.
+
+Prints ONE JSON line (see the keys below). Usage:
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+import top_kv_tile_amd as tkt  # noqa: E402
+
+METRIC = "block-sparse attn TFLOP/s over kept tiles (+% MFMA peak); select GB/s"
+WORKLOAD = "long_causal_gqa_bf16_s128k"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+ATTN_KERNEL_SRC = os.path.join(ROOT, "top_kv_tile_amd", "csrc", "attn_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", f"attn_fwd_{WORKLOAD}_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kept_tile_flops(sel: tkt.Selection, w: synth.Workload):
+    """(full-tile FLOPs, visible-pair FLOPs, kept tiles visited) over all query heads."""
+    row_ptr = sel.row_ptr.cpu().numpy().astype(np.int64)
+    col = sel.col_idx.cpu().numpy().astype(np.int64)
+    B, H, NQ, NK = sel.keep.shape
+    rows = np.arange(B * H * NQ)
+    counts = np.diff(row_ptr)
+    row_of = np.repeat(rows, counts)
+    ti = row_of % NQ
+    q_lo = ti * w.block_q
+    q_hi = np.minimum(q_lo + w.block_q, w.S)          # exclusive
+    k_lo = col * w.block_kv
+    k_hi = np.minimum(k_lo + w.block_kv, w.S)
+    if w.causal:
+        live = k_lo <= q_hi - 1
+    else:
+        live = np.ones_like(k_lo, bool)
+    area = (q_hi - q_lo) * (k_hi - k_lo)
+    if w.causal:
+        # visible pairs of a tile: sum over queries t in [q_lo, q_hi) of
+        # clip(t - k_lo + 1, 0, n), n = k_hi - k_lo (a ramp, then n per query)
+        n = k_hi - k_lo
+        t_flat = k_lo + n - 1
+        r_lo, r_hi = np.maximum(q_lo, k_lo), np.minimum(q_hi - 1, t_flat - 1)
+        m = np.clip(r_hi - r_lo + 1, 0, None)
+        first = r_lo - k_lo + 1
+        vis = m * first + m * (m - 1) // 2
+        vis = vis + np.clip(q_hi - 1 - np.maximum(q_lo, t_flat) + 1, 0, None) * n
+    else:
+        vis = area
+    heads_per_row = (w.Hq // H)
+    D = w.D
+    full = float(4 * D * (area * live).sum() * heads_per_row)
+    visible = float(4 * D * vis.sum() * heads_per_row)
+    return full, visible, int(live.sum()) * heads_per_row
+
+
+def read_traffic():
+    """Counter-based HBM traffic per attention launch from the committed profile, or None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                a, b = line.split(":", 1)
+                kv[a.strip()] = b.strip()
+    try:
+        src_hash = hashlib.sha256(open(ATTN_KERNEL_SRC, "rb").read()).hexdigest()
+        if kv.get("kernel_source_sha256") != src_hash:
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, w: synth.Workload, budget_s: float = 20.0):
+    """The oracle, untuned, on a bounded sample of the same workload (host cores)."""
+    import oracle
+
+    threads = torch.get_num_threads()
+    g0 = 0  # one GQA group: query heads 0..7 with kv head 0
+    G = w.Hq // w.Hkv
+    q = inp.q[:, g0 * G:(g0 + 1) * G]
+    k = inp.k[:, g0:g0 + 1]
+    v = inp.v[:, g0:g0 + 1]
+    t0 = time.perf_counter()
+    ref = oracle.select_blocks(q, k, w.budget, w.block_q, w.block_kv, w.head_shared, False, inp.pins, inp.drops)
+    t_sel = time.perf_counter() - t0
+    sel_rows = G * w.nq
+    rng = np.random.default_rng(11)
+    t_att, n_rows, fl = 0.0, 0, 0.0
+    keep = ref["keep"]
+    while t_att < budget_s * 0.6 and n_rows < 256:
+        h = int(rng.integers(G))
+        i = int(rng.integers(w.nq))
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, keep, w.block_q, w.block_kv, w.causal, rows=[(0, h, i)])
+        t_att += time.perf_counter() - t0
+        n_rows += 1
+        cols = np.nonzero(keep[0, h, i])[0]
+        qhi = min((i + 1) * w.block_q, w.S)
+        live = cols[cols * w.block_kv <= qhi - 1]
+        fl += 4.0 * w.D * w.block_q * w.block_kv * live.size
+    per_row_s = t_sel / sel_rows + t_att / n_rows
+    per_row_flops = fl / n_rows
+    value = per_row_flops / per_row_s / 1e12
+    return {
+        "value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "host_cpus": os.cpu_count(),
+        "sample": (f"oracle.select_blocks on one GQA group ({G} query heads x {w.nq} query tiles, "
+                   f"{t_sel:.1f} s) + oracle.attention (fp64) on {n_rows} seeded (head, query-tile) rows "
+                   f"({t_att:.1f} s); per-row select + attention time, kept-tile FLOPs of the sampled rows"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB read + 1 GiB write elementwise kernel 3 times "
+                         "(reference for HBM byte counters) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    if args.calibrate_copy:
+        x = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": x.numel() * 4, "bytes_written": y.numel() * 4}))
+        return
+
+    w = synth.workload(args.workload)
+    log(f"[bench] generating {w.name}")
+    t0 = time.perf_counter()
+    inp = synth.make_inputs(w)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
+    dev = torch.device("cuda:0")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    spec = tkt.SparseSpec(budget=w.budget, block_q=w.block_q, block_kv=w.block_kv, head_shared=w.head_shared)
+    sizes = tkt.nsa_select_sizes(q, k, spec, inp.pins, inp.drops)
+    ws = torch.empty(sizes.workspace_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sel = tkt.nsa_select(q, k, spec, inp.pins, inp.drops, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        tkt.nsa_block_sparse_attn(q, k, v, sel, w.causal, out=out, lse=lse)
+        if ev is not None:
+            ev[2].record(stream)
+        return sel
+
+    log("[bench] warmup")
+    for _ in range(args.warmup):
+        sel = step()
+    torch.cuda.synchronize()
+    full_flops, vis_flops, tiles = kept_tile_flops(sel, w)
+
+    log(f"[bench] timing {args.steps} steps")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+
+    value = full_flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = full_flops / (attn_ms * 1e-3) / 1e12
+    select_bytes = (q.numel() + k.numel()) * q.element_size() + sel.keep.numel() + 4 * (sel.nnz + sel.row_ptr.numel())
+    select_bytes += (2 * w.nq * ((w.nk + 63) // 64) * 8)  # bit-packed pins + drops
+    select_gbs = select_bytes / (sel_ms * 1e-3) / 1e9
+    traffic = read_traffic()
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
+                   "block_q": w.block_q, "block_kv": w.block_kv, "budget": w.budget, "causal": w.causal,
+                   "head_shared": w.head_shared, "sink_pin": w.sink_pin, "drop_frac": w.drop_frac,
+                   "nnz_tiles": sel.nnz, "kept_tiles_visited": tiles},
+        "roofline": {"bound": "mfma", "kernel": "attn_mfma_kernel<128,4>",
+                     "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "flops_per_launch": full_flops, "visible_pair_flops_per_launch": vis_flops,
+                     "avg_launch_ms": round(attn_ms, 4)},
+        "stages": {"select_ms": round(sel_ms, 4), "select_GBps": round(select_gbs, 1),
+                   "select_frac_hbm": round(select_gbs / PEAK_HBM_GBS, 4),
+                   "select_algorithmic_bytes": select_bytes, "attn_ms": round(attn_ms, 4),
+                   "attn_TFLOPs": round(attn_tflops, 2)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle on a bounded sample)")
+        res["cpu_baseline"] = cpu_baseline(inp, w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -28,6 +28,9 @@ namespace nsa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -35,6 +38,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.69314718055994530942f;
+// s_waitcnt immediate for gfx9-family: vmcnt(0), expcnt and lgkmcnt left at their maximum.
+constexpr int kVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
     uint32_t u = __float_as_uint(x);
@@ -42,10 +47,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
     u += 0x7fffu + ((u >> 16) & 1u);                                 // round to nearest even
     return u >> 16;
 }
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Raw buffer resource over `bytes` bytes at p (stride 0, no swizzle): loads
+// at offsets past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
 
 // Work item of a workgroup. Workgroups are dispatched round-robin over the 8
 // XCDs (block n runs on XCD n % 8); inside each run of 64 consecutive blocks,
@@ -106,26 +114,31 @@ __device__ __forceinline__ void tile_range(const AttnArgs& a, int b, int h, int 
 
 // ============================================================ MFMA kernel
 //
-// LDS layout per buffer (bf16):
-//   Ks [64][D + 8]   key-major, row pitch padded by 16 bytes
-//   Vt [D][64 + 8]   d-major; inside each group of 16 keys the two middle
-//                    quads are swapped (key quads 0,2,1,3), so the 8 keys one
-//                    lane feeds to an MFMA k-slot are 16 contiguous bytes.
+// LDS, per workgroup: two K stages and two V stages of one 64-key tile each,
+// row-major (64 x D bf16, no padding), filled by buffer-to-LDS DMA. Rows are
+// XOR-swizzled in 16-byte chunks so both read patterns are bank-conflict free:
+//   K (read 16 bytes per lane, 16 rows per pass):  chunk ^= (row / RPB) % CH
+//   V (transposed 8-byte reads, 4 rows per pass):  chunk ^= 4 * ((row / RPB) % 4) % CH
+// (RPB = token rows per 256-byte bank row, CH = 16-byte chunks per token row).
+//
+// Per tile n the loop issues S(n+1) = K(n+1) Q^T on the matrix cores before the
+// softmax of tile n, so the exponentials of one tile run under the QK^T of the
+// next, then O^T += V(n)^T P(n)^T. V^T fragments come straight from the
+// row-major V tile with ds_read_b64_tr_b16: within each 16-lane group, result
+// element e of lane i is element (i mod 4) of the 8 bytes addressed by lane
+// 4e + i/4, so lane i receives one d column over four keys.
 template <int D>
-struct MfmaLds {
-    static constexpr int KP = D + 8;        // Ks row pitch (elements)
-    static constexpr int VP = 64 + 8;       // Vt row pitch (elements)
-    static constexpr int KS = 64 * KP;      // Ks elements
-    static constexpr int VS = D * VP;       // Vt elements
-    static constexpr int BUF = KS + VS;     // one stage
-    static constexpr int BYTES = 2 * BUF * 2;
+struct MfmaGeo {
+    static constexpr int ROWB = D * 2;            // bytes per token row
+    static constexpr int CH = ROWB / 16;          // 16-byte chunks per row
+    static constexpr int RPB = 256 / ROWB;        // rows per 256-byte bank row
+    static constexpr int TILEB = 64 * ROWB;       // bytes per 64-row tile
+    static constexpr int RPI = 1024 / ROWB;       // rows per 1 KiB DMA instruction
+    static constexpr int NINSTR = TILEB / 1024;   // DMA instructions per tile
+    static constexpr int BYTES = 4 * TILEB;       // 2 K stages + 2 V stages
+    __device__ static int kswz(int row) { return (row / RPB) % CH; }
+    __device__ static int vswz(int row) { return (4 * ((row / RPB) % 4)) % CH; }
 };
-
-__device__ __forceinline__ int vt_pos(int key) {  // key 0..63 -> position in a Vt row
-    const int quad = (key >> 2) & 3;
-    const int pq = ((quad & 1) << 1) | (quad >> 1);  // 0,1,2,3 -> 0,2,1,3
-    return (key & ~15) | (pq << 2) | (key & 3);
-}
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
@@ -133,13 +146,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     constexpr int BKV = 64;
     constexpr int KSTEPS = D / 16;      // QK^T contraction steps of 16
     constexpr int DBLK = D / 32;        // O^T row blocks of 32
-    constexpr int KCH = D / 8;          // 16-byte chunks per K row
-    constexpr int KLOADS = BKV * KCH / NT;
-    constexpr int VUNITS = 16 * (D / 8);  // (key quad, d chunk) units
-    constexpr int VLOADS = (VUNITS + NT - 1) / NT;
-    static_assert(KLOADS * NT == BKV * KCH, "K tile must split evenly");
-    using L = MfmaLds<D>;
-    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    using G = MfmaGeo<D>;
+    constexpr int IPW = (G::NINSTR + NW - 1) / NW;  // DMA instructions per wave per tile
+    extern __shared__ __attribute__((aligned(1024))) char lds[];
+    typedef __attribute__((address_space(3))) void lds_void;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
@@ -152,166 +162,222 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     const int qrow = qw0 + l32;                      // this lane's query row
     const bool qvalid = qrow < a.S && (wave * 32 + l32) < bq;
 
-    const uint16_t* qp = (const uint16_t*)a.q + (((int64_t)wk.b * a.Hq + wk.h) * a.S) * D;
-    const uint16_t* kp = (const uint16_t*)a.k + (((int64_t)wk.b * a.Hkv + wk.g) * a.S) * D;
-    const uint16_t* vp = (const uint16_t*)a.v + (((int64_t)wk.b * a.Hkv + wk.g) * a.S) * D;
+    // Per-head buffer resources: 32-bit offsets, and reads past the end of the
+    // head return zeros (ragged tails need no branches). The host guarantees
+    // (S + 64) * D * 2 < 2^31.
+    const int head_bytes = a.S * G::ROWB;
+    const __amdgpu_buffer_rsrc_t qrs =
+        make_rsrc((const uint16_t*)a.q + (((int64_t)wk.b * a.Hq + wk.h) * a.S) * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t krs =
+        make_rsrc((const uint16_t*)a.k + (((int64_t)wk.b * a.Hkv + wk.g) * a.S) * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs =
+        make_rsrc((const uint16_t*)a.v + (((int64_t)wk.b * a.Hkv + wk.g) * a.S) * D, head_bytes);
 
-    // Q^T operand: lane holds q[qrow][16*ks + 8*hf .. +8] for every ks.
+    // Q^T operand: lane holds q[qrow][16*ks + 8*hf .. +8] for every ks (zeros past S).
     bf16x8 qf[KSTEPS];
+    {
+        const int qoff = (wave * 32 + l32) < bq ? (qrow * D + 8 * hf) * 2 : head_bytes;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (qvalid) w = *(const u32x4*)(qp + (int64_t)qrow * D + 16 * ks + 8 * hf);
-        qf[ks] = __builtin_bit_cast(bf16x8, w);
+        for (int ks = 0; ks < KSTEPS; ++ks)
+            qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff + 32 * ks, 0, 0));
     }
 
     int e_begin, e_end;
     tile_range(a, wk.b, wk.h, wk.i, q_last, e_begin, e_end);
+    const int ntiles = e_end - e_begin;
+
+    // The row's kv-tile indices, 64 at a time: lane x holds entry base + x and
+    // the loop reads them with readlane (no memory access per tile).
+    int col_base = e_begin;
+    int col_lane = 0;
+    auto fetch_cols = [&](int base) {
+        col_base = base;
+        const int e = base + lane;
+        col_lane = a.row_ptr ? (e < e_end ? a.col_idx[e] : 0) : e;
+    };
+    fetch_cols(e_begin);
+    auto tile_of = [&](int n) -> int {  // n-th visited tile (n uniform)
+        const int e = e_begin + n;
+        if (e - col_base >= 64) fetch_cols(e);
+        return __builtin_amdgcn_readlane(col_lane, e - col_base);
+    };
+
+    // DMA: wave w issues instructions w, w + NW, ...; lane L of instruction ii
+    // fills LDS bytes ii*1024 + 16L, i.e. row ii*RPI + L/CH, physical chunk L%CH,
+    // from the logical chunk given by the row's swizzle.
+    // Rows past the end of the sequence (ragged last tile) read row S - 1
+    // instead: in range, finite, and masked out (K) or weighted by p = 0 (V).
+    int drow[IPW], kchunk[IPW], vchunk[IPW];
+#pragma unroll
+    for (int x = 0; x < IPW; ++x) {
+        const int ii = wave + NW * x;
+        const int row = ii * G::RPI + lane / G::CH, pc = lane % G::CH;
+        drow[x] = row;
+        kchunk[x] = (pc ^ G::kswz(row)) * 16;
+        vchunk[x] = (pc ^ G::vswz(row)) * 16;
+    }
+    char* kst[2] = {lds, lds + G::TILEB};
+    char* vst[2] = {lds + 2 * G::TILEB, lds + 3 * G::TILEB};
+    auto dma = [&](__amdgpu_buffer_rsrc_t rs, const int (&chunk)[IPW], char* stage_base, int j) {
+        const int key0 = j * BKV;
+#pragma unroll
+        for (int x = 0; x < IPW; ++x) {
+            const int ii = wave + NW * x;
+            if (G::NINSTR % NW == 0 || ii < G::NINSTR) {
+                const int off = min(key0 + drow[x], a.S - 1) * G::ROWB + chunk[x];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(stage_base + ii * 1024), 16, off, 0, 0, 0);
+            }
+        }
+    };
+    auto dma_k = [&](int j, int stage) { dma(krs, kchunk, kst[stage], j); };
+    auto dma_v = [&](int j, int stage) { dma(vrs, vchunk, vst[stage], j); };
+
+    // LDS read offsets (bytes) that do not depend on the tile.
+    // K: lane reads row 32*mb + l32, logical chunk 2*ks + hf.
+    int krow_off[2], kswz_l[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int row = 32 * mb + l32;
+        krow_off[mb] = row * G::ROWB;
+        kswz_l[mb] = G::kswz(row);
+    }
+    // V^T: lane (group g = lane/16, s = lane%16) addresses row 16*kk + 4*hf + s/4
+    // (+8 for the second half) at d = 32*m + 16*(g%2) + 4*(s%4).
+    const int vg = lane >> 4, vs = lane & 15;
+    const int v_e = vs >> 2, v_q = vs & 3;
 
     f32x16 oacc[DBLK];
 #pragma unroll
     for (int m = 0; m < DBLK; ++m) oacc[m] = (f32x16){};
-    float m_run = kNegInf;  // running max (log2 domain) of this lane's query row
+    float m_ref = kNegInf;  // exponent reference of this lane's query row (raw dot-product units)
     float l_run = 0.f;      // partial sum over this lane's half of every tile
+    const float tau_raw = 8.0f / a.scale_log2;
 
-    u32x4 kreg[KLOADS];
-    u32x4 vreg[VLOADS][4];
-
-    auto tile_of = [&](int e) -> int { return a.row_ptr ? a.col_idx[e] : e; };
-    auto load_tile = [&](int j) {
-        const int key0 = j * BKV;
+    auto qk = [&](f32x16 (&sacc)[2], int stage) {
+        const char* ks = kst[stage];
+        sacc[0] = (f32x16){};
+        sacc[1] = (f32x16){};
 #pragma unroll
-        for (int x = 0; x < KLOADS; ++x) {
-            const int c = tid + NT * x;
-            const int row = c / KCH, ch = c % KCH;
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (key0 + row < a.S) w = *(const u32x4*)(kp + (int64_t)(key0 + row) * D + ch * 8);
-            kreg[x] = w;
-        }
+        for (int ks_ = 0; ks_ < KSTEPS; ++ks_) {
 #pragma unroll
-        for (int x = 0; x < VLOADS; ++x) {
-            const int u = tid + NT * x;
-            const int kq = u & 15, dc = u >> 4;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = key0 + 4 * kq + r;
-                u32x4 w = {0u, 0u, 0u, 0u};
-                if (key < a.S && u < VUNITS) w = *(const u32x4*)(vp + (int64_t)key * D + dc * 8);
-                vreg[x][r] = w;
+            for (int mb = 0; mb < 2; ++mb) {
+                const int chunk = (2 * ks_ + hf) ^ kswz_l[mb];
+                const bf16x8 kf =
+                    __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + krow_off[mb] + chunk * 16));
+                sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks_], sacc[mb], 0, 0, 0);
             }
         }
     };
-    auto store_tile = [&](int buf) {
-        uint16_t* ks = lds + buf * L::BUF;
-        uint16_t* vt = ks + L::KS;
-#pragma unroll
-        for (int x = 0; x < KLOADS; ++x) {
-            const int c = tid + NT * x;
-            const int row = c / KCH, ch = c % KCH;
-            *(u32x4*)(ks + row * L::KP + ch * 8) = kreg[x];
-        }
-#pragma unroll
-        for (int x = 0; x < VLOADS; ++x) {
-            const int u = tid + NT * x;
-            if (VUNITS % NT != 0 && u >= VUNITS) break;
-            const int kq = u & 15, dc = u >> 4;
-            const int pos = vt_pos(4 * kq);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {  // dword e holds d = 8*dc + 2e (low) and 2e+1 (high)
-                const uint32_t k0 = vreg[x][0][e], k1 = vreg[x][1][e], k2 = vreg[x][2][e], k3 = vreg[x][3][e];
-                u32x2 lo, hi;
-                lo[0] = (k0 & 0xffffu) | (k1 << 16);
-                lo[1] = (k2 & 0xffffu) | (k3 << 16);
-                hi[0] = (k0 >> 16) | (k1 & 0xffff0000u);
-                hi[1] = (k2 >> 16) | (k3 & 0xffff0000u);
-                *(u32x2*)(vt + (8 * dc + 2 * e) * L::VP + pos) = lo;
-                *(u32x2*)(vt + (8 * dc + 2 * e + 1) * L::VP + pos) = hi;
-            }
-        }
-    };
-
-    if (e_begin < e_end) {
-        load_tile(tile_of(e_begin));
-        store_tile(0);
-    }
-    __syncthreads();
-
-    for (int e = e_begin; e < e_end; ++e) {
-        const int cur = (e - e_begin) & 1;
-        const int j = tile_of(e);
-        const bool has_next = e + 1 < e_end;
-        if (has_next) load_tile(tile_of(e + 1));
-
-        const int key0 = j * BKV;
-        // Whole tile masked for this wave: every key is after every query row.
-        const bool wave_dead = a.causal && key0 > qw0 + 31;
-        if (!wave_dead) {
-            const uint16_t* ks = lds + cur * L::BUF;
-            const uint16_t* vt = ks + L::KS;
-            // S^T = K Q^T : two 32-key blocks.
-            f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
-#pragma unroll
-            for (int ks_ = 0; ks_ < KSTEPS; ++ks_) {
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    const bf16x8 kf = __builtin_bit_cast(
-                        bf16x8, *(const u32x4*)(ks + (32 * mb + l32) * L::KP + 16 * ks_ + 8 * hf));
-                    sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks_], sacc[mb], 0, 0, 0);
-                }
-            }
-            // Lane holds query qrow and keys key0 + 32*mb + 8*q + 4*hf + e at sacc[mb][4q + e].
-            const bool need_mask = (a.causal && key0 + BKV - 1 > qw0) || (key0 + BKV > a.S);
-            float mx = kNegInf;
+    auto softmax_pv = [&](f32x16 (&sacc)[2], int key0, int stage) {
+        // Lane holds query qrow and keys key0 + 32*mb + 8*q + 4*hf + e at sacc[mb][4q + e]
+        // (raw dot products; the softmax scale is folded into the exponent below).
+        const bool need_mask = (a.causal && key0 + BKV - 1 > qw0) || (key0 + BKV > a.S);
+        if (need_mask) {
+            int lim = min(BKV - 1, a.S - 1 - key0);           // last visible key offset
+            if (a.causal) lim = min(lim, qrow - key0);
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int x = 0; x < 16; ++x) {
-                    float sv = sacc[mb][x] * a.scale_log2;
-                    if (need_mask) {
-                        const int key = key0 + 32 * mb + 8 * (x >> 2) + 4 * hf + (x & 3);
-                        if (key >= a.S || (a.causal && key > qrow)) sv = kNegInf;
-                    }
-                    sacc[mb][x] = sv;
-                    mx = fmaxf(mx, sv);
+                    const int off = 32 * mb + 8 * (x >> 2) + 4 * hf + (x & 3);
+                    sacc[mb][x] = off <= lim ? sacc[mb][x] : kNegInf;
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = (m_new == kNegInf) ? 0.f : m_new;  // no visible key yet: keep zeros
-            const float alpha = fast_exp2(m_run - m_use);
-            m_run = m_new;
-            float psum = 0.f;
-            bf16x8 pf[4];
+        }
+        float mx = kNegInf;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int mb = kk >> 1, q4 = 8 * (kk & 1);
-                float p[8];
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    p[x] = fast_exp2(sacc[mb][q4 + x] - m_use);
-                    psum += p[x];
-                }
-                u32x4 w;
-#pragma unroll
-                for (int x = 0; x < 4; ++x) w[x] = pack_bf16x2(p[2 * x], p[2 * x + 1]);
-                pf[kk] = __builtin_bit_cast(bf16x8, w);
-            }
-            l_run = l_run * alpha + psum;
+            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[mb][x]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // Lazy reference: the exponent reference m_ref (raw units) moves only when
+        // a row's maximum exceeds it by more than 8 / scale, so p <= 2^8 and the
+        // O / l rescale is skipped on almost every tile. Any reference gives the
+        // same normalised result; LSE adds it back at the end.
+        const bool grow = mx > m_ref + tau_raw;
+        if (__ballot(grow)) {  // wave-uniform: some row needs a new reference
+            const float m_new = grow ? mx : m_ref;
+            const float alpha = fast_exp2((m_ref - m_new) * a.scale_log2);  // 0 when m_ref = -inf
+            m_ref = m_new;
+            l_run *= alpha;
 #pragma unroll
             for (int m = 0; m < DBLK; ++m) oacc[m] *= alpha;
-            // O^T += V^T P^T
+        }
+        const float mref_s = (m_ref == kNegInf) ? 0.f : m_ref * a.scale_log2;
+        float psum = 0.f;
+        bf16x8 pf[4];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < 4; ++kk) {
+            const int mb = kk >> 1, q4 = 8 * (kk & 1);
 #pragma unroll
-                for (int m = 0; m < DBLK; ++m) {
-                    const bf16x8 vf = __builtin_bit_cast(
-                        bf16x8, *(const u32x4*)(vt + (32 * m + l32) * L::VP + 16 * kk + 8 * hf));
-                    oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], oacc[m], 0, 0, 0);
-                }
+            for (int x = 0; x < 8; ++x) {
+                const float pv = fast_exp2(__builtin_fmaf(sacc[mb][q4 + x], a.scale_log2, -mref_s));
+                psum += pv;
+                pf[kk][x] = (__bf16)pv;
             }
         }
-        if (has_next) store_tile(cur ^ 1);
-        __syncthreads();
+        l_run += psum;
+        // O^T += V^T P^T ; the V^T fragment of k-step kk, row block m is two
+        // transposed reads: keys 16kk + 4hf + (0..3) and 16kk + 8 + 4hf + (0..3).
+        const char* vt = vst[stage];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+            for (int m = 0; m < DBLK; ++m) {
+                const int d = 32 * m + 16 * (vg & 1) + 4 * v_q;
+                const int row0 = 16 * kk + 4 * hf + v_e;
+                const int row1 = row0 + 8;
+                const int c = d >> 3, b = (d & 7) * 2;
+                typedef __attribute__((address_space(3))) short4_t lds_s4;
+                const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s4*)(vt + row0 * G::ROWB + ((c ^ G::vswz(row0)) * 16) + b));
+                const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s4*)(vt + row1 * G::ROWB + ((c ^ G::vswz(row1)) * 16) + b));
+                const short8_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[kk],
+                                                                   oacc[m], 0, 0, 0);
+            }
+        }
+    };
+
+    // Prologue: K(0), V(0), K(1) in flight; S(0) once K(0) has landed.
+    int j_cur = 0, j_next = 0;
+    if (ntiles > 0) {
+        j_cur = tile_of(0);
+        dma_k(j_cur, 0);
+        dma_v(j_cur, 0);
     }
+    if (ntiles > 1) {
+        j_next = tile_of(1);
+        dma_k(j_next, 1);
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+    f32x16 sa[2], sb[2];
+    const bool dead0 = ntiles > 0 && a.causal && j_cur * BKV > qw0 + 31;
+    if (ntiles > 0 && !dead0) qk(sa, 0);
+    __syncthreads();  // K stage 0 is refilled by the first step
+
+    // One step: tile n with S(n) in scur, K(n+1) in K stage (n+1)&1, V(n) in V stage n&1.
+    auto step = [&](int n, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+        const int kst_next = (n + 1) & 1, vst_cur = n & 1;
+        const int j_after = (n + 2 < ntiles) ? tile_of(n + 2) : 0;
+        if (n + 2 < ntiles) dma_k(j_after, n & 1);          // K(n) stage is free again
+        if (n + 1 < ntiles) dma_v(j_next, kst_next);        // V(n-1) stage is free again
+        const bool dead_cur = a.causal && j_cur * BKV > qw0 + 31;
+        const bool dead_next = a.causal && j_next * BKV > qw0 + 31;
+        if (n + 1 < ntiles && !dead_next) qk(snext, kst_next);
+        if (!dead_cur) softmax_pv(scur, j_cur * BKV, vst_cur);
+        j_cur = j_next;
+        j_next = j_after;
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        __syncthreads();
+    };
+    int n = 0;
+    for (; n + 1 < ntiles; n += 2) {
+        step(n, sa, sb);
+        step(n + 1, sb, sa);
+    }
+    if (n < ntiles) step(n, sa, sb);
 
     // Finish: combine the two lane halves of the row sum.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -323,14 +389,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
         for (int m = 0; m < DBLK; ++m)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                u32x2 w;
-                w[0] = pack_bf16x2(oacc[m][4 * q] * inv, oacc[m][4 * q + 1] * inv);
-                w[1] = pack_bf16x2(oacc[m][4 * q + 2] * inv, oacc[m][4 * q + 3] * inv);
-                *(u32x2*)(op + 32 * m + 8 * q + 4 * hf) = w;
+                bf16x4 w;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) w[x] = (__bf16)(oacc[m][4 * q + x] * inv);
+                *(bf16x4*)(op + 32 * m + 8 * q + 4 * hf) = w;
             }
         if (hf == 0) {
             a.lse[((int64_t)wk.b * a.Hq + wk.h) * a.S + qrow] =
-                empty ? kNegInf : (m_run + __log2f(l_tot)) * kLn2;
+                empty ? kNegInf : (m_ref * a.scale_log2 + __log2f(l_tot)) * kLn2;
         }
     }
 }
@@ -444,7 +510,9 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a) {
 }  // namespace
 
 bool attn_mfma_supported(const AttnArgs& a, int bf16) {
-    return bf16 && a.block_kv == 64 && a.block_q % 32 == 0 && a.block_q >= 32 && a.block_q <= 128 &&
+    // Buffer offsets are 32-bit: one head plus a tile of slack must stay below 2^31 bytes.
+    const bool fits = ((int64_t)a.S + 64) * a.D * 2 < ((int64_t)1 << 31);
+    return bf16 && fits && a.block_kv == 64 && a.block_q % 32 == 0 && a.block_q >= 32 && a.block_q <= 128 &&
            (a.D == 64 || a.D == 128);
 }
 
@@ -455,7 +523,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream) {
     const int nw = a.block_q / 32;
 #define NSA_ATTN(DD, NWW)                                                                             \
     do {                                                                                              \
-        const size_t lds_bytes = MfmaLds<DD>::BYTES;                                                 \
+        const size_t lds_bytes = MfmaGeo<DD>::BYTES;                                                 \
         hipLaunchKernelGGL((attn_mfma_kernel<DD, NWW>), grid, dim3(64 * NWW), lds_bytes, stream, a); \
     } while (0)
     if (a.D == 128) {

@@ -141,6 +141,22 @@ def test_empty_sequence():
     assert tkt.nsa_select(q, q, tkt.SparseSpec(budget=0.3)) is None
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_growing_logits_move_the_softmax_reference(causal):
+    """Keys whose scale grows along the sequence make later tiles' logits dominate,
+    so the running softmax reference moves on many tiles (online rescale path).
+    Outputs reach |O| > 4, where half a bf16 ulp is 0.0156, so the error is
+    measured relative to max(1, |O|); a misordered rescale gives O(1) errors."""
+    say(f"growing logits causal={causal}")
+    B, H, S, D = 1, 4, 4096, 128
+    q, k, v = _qkv(B, H, H, S, D, seed=31, dtype=torch.float32)
+    ramp = (1.0 + torch.arange(S, dtype=torch.float32) / 256.0)[None, None, :, None]
+    k = (k * ramp).to(torch.bfloat16)
+    q, v = q.to(torch.bfloat16), v.to(torch.bfloat16)
+    rep = run_case(q, k, v, tkt.SparseSpec(budget=0.5), causal, where="growing", relative=True)
+    say(f"  {rep}")
+
+
 def test_all_tied_scores_pick_lowest_index():
     say("all ties")
     B, H, S, D = 1, 2, 2048, 128

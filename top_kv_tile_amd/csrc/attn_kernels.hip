@@ -253,24 +253,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     float l_run = 0.f;      // partial sum over this lane's half of every tile
     const float tau_raw = 8.0f / a.scale_log2;
 
-    auto qk = [&](f32x16 (&sacc)[2], int stage) {
-        const char* ks = kst[stage];
-        sacc[0] = (f32x16){};
-        sacc[1] = (f32x16){};
-#pragma unroll
-        for (int ks_ = 0; ks_ < KSTEPS; ++ks_) {
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const int chunk = (2 * ks_ + hf) ^ kswz_l[mb];
-                const bf16x8 kf =
-                    __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + krow_off[mb] + chunk * 16));
-                sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks_], sacc[mb], 0, 0, 0);
-            }
-        }
-    };
-    auto softmax_pv = [&](f32x16 (&sacc)[2], int key0, int stage) {
-        // Lane holds query qrow and keys key0 + 32*mb + 8*q + 4*hf + e at sacc[mb][4q + e]
-        // (raw dot products; the softmax scale is folded into the exponent below).
+    // Masks of a partial tile (causal diagonal or ragged tail): keys past the
+    // lane's query row or past S get -inf. Only partial tiles take this branch.
+    auto mask_tile = [&](f32x16 (&sacc)[2], int key0) {
         const bool need_mask = (a.causal && key0 + BKV - 1 > qw0) || (key0 + BKV > a.S);
         if (need_mask) {
             int lim = min(BKV - 1, a.S - 1 - key0);           // last visible key offset
@@ -283,42 +268,57 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
                     sacc[mb][x] = off <= lim ? sacc[mb][x] : kNegInf;
                 }
         }
+    };
+    // S^T = K Q^T for the tile in K stage `stage` (raw dot products).
+    auto qk_frag = [&](const char* ks, int ks_, int mb) -> bf16x8 {
+        const int chunk = (2 * ks_ + hf) ^ kswz_l[mb];
+        return __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + krow_off[mb] + chunk * 16));
+    };
+    // One straight-line block: the matrix cores compute S(next) while the
+    // vector ALUs turn S(cur) into P (row max, exponentials, bf16 pack, row
+    // sum). Lane holds query qrow and keys 32*mb + 8*q + 4*hf + e at
+    // sacc[mb][4q + e]; the softmax scale is folded into one FMA per logit.
+    // Lazy reference: m_ref (raw units) moves only when a row's maximum exceeds
+    // it by more than 8 / scale, so p <= 2^8 and O is rescaled on few tiles;
+    // any reference gives the same normalised result and LSE adds it back.
+    auto qk_softmax = [&](f32x16 (&scur)[2], f32x16 (&snext)[2], int kstage, bf16x8 (&pf)[4]) -> float {
+        const char* ks = kst[kstage];
+        snext[0] = (f32x16){};
+        snext[1] = (f32x16){};
         float mx = kNegInf;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[mb][x]);
+            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, scur[mb][x]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // Lazy reference: the exponent reference m_ref (raw units) moves only when
-        // a row's maximum exceeds it by more than 8 / scale, so p <= 2^8 and the
-        // O / l rescale is skipped on almost every tile. Any reference gives the
-        // same normalised result; LSE adds it back at the end.
         const bool grow = mx > m_ref + tau_raw;
-        if (__ballot(grow)) {  // wave-uniform: some row needs a new reference
-            const float m_new = grow ? mx : m_ref;
-            const float alpha = fast_exp2((m_ref - m_new) * a.scale_log2);  // 0 when m_ref = -inf
-            m_ref = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int m = 0; m < DBLK; ++m) oacc[m] *= alpha;
-        }
-        const float mref_s = (m_ref == kNegInf) ? 0.f : m_ref * a.scale_log2;
+        const float m_new = grow ? mx : m_ref;
+        const float alpha = grow ? fast_exp2((m_ref - m_new) * a.scale_log2) : 1.0f;  // 0 when m_ref = -inf
+        const float mref_s = (m_new == kNegInf) ? 0.f : m_new * a.scale_log2;
         float psum = 0.f;
-        bf16x8 pf[4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int mb = kk >> 1, q4 = 8 * (kk & 1);
+        for (int ks_ = 0; ks_ < KSTEPS; ++ks_) {
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                const float pv = fast_exp2(__builtin_fmaf(sacc[mb][q4 + x], a.scale_log2, -mref_s));
-                psum += pv;
-                pf[kk][x] = (__bf16)pv;
+            for (int mb = 0; mb < 2; ++mb)
+                snext[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qk_frag(ks, ks_, mb), qf[ks_], snext[mb], 0, 0, 0);
+            if (ks_ < 4) {  // four of the eight k-steps carry the softmax of one P fragment each
+                const int kk = ks_, mb = kk >> 1, q4 = 8 * (kk & 1);
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const float pv = fast_exp2(__builtin_fmaf(scur[mb][q4 + x], a.scale_log2, -mref_s));
+                    psum += pv;
+                    pf[kk][x] = (__bf16)pv;
+                }
             }
         }
-        l_run += psum;
-        // O^T += V^T P^T ; the V^T fragment of k-step kk, row block m is two
-        // transposed reads: keys 16kk + 4hf + (0..3) and 16kk + 8 + 4hf + (0..3).
-        const char* vt = vst[stage];
+        l_run = l_run * alpha + psum;
+        m_ref = m_new;
+        return grow ? alpha : 1.0f;
+    };
+    // O^T += V^T P^T ; the V^T fragment of k-step kk, row block m is two
+    // transposed reads: keys 16kk + 4hf + (0..3) and 16kk + 8 + 4hf + (0..3).
+    auto pv = [&](const bf16x8 (&pf)[4], int vstage) {
+        const char* vt = vst[vstage];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
@@ -353,20 +353,33 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
     f32x16 sa[2], sb[2];
-    const bool dead0 = ntiles > 0 && a.causal && j_cur * BKV > qw0 + 31;
-    if (ntiles > 0 && !dead0) qk(sa, 0);
+    sa[0] = (f32x16){};
+    sa[1] = (f32x16){};
+    if (ntiles > 0) {
+#pragma unroll
+        for (int ks_ = 0; ks_ < KSTEPS; ++ks_)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+                sa[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qk_frag(kst[0], ks_, mb), qf[ks_], sa[mb], 0, 0, 0);
+    }
     __syncthreads();  // K stage 0 is refilled by the first step
 
     // One step: tile n with S(n) in scur, K(n+1) in K stage (n+1)&1, V(n) in V stage n&1.
+    // Tiles entirely after this wave's rows are computed like any other and
+    // come out fully masked (p = 0); they are rare (the causal diagonal).
     auto step = [&](int n, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
         const int kst_next = (n + 1) & 1, vst_cur = n & 1;
         const int j_after = (n + 2 < ntiles) ? tile_of(n + 2) : 0;
         if (n + 2 < ntiles) dma_k(j_after, n & 1);          // K(n) stage is free again
         if (n + 1 < ntiles) dma_v(j_next, kst_next);        // V(n-1) stage is free again
-        const bool dead_cur = a.causal && j_cur * BKV > qw0 + 31;
-        const bool dead_next = a.causal && j_next * BKV > qw0 + 31;
-        if (n + 1 < ntiles && !dead_next) qk(snext, kst_next);
-        if (!dead_cur) softmax_pv(scur, j_cur * BKV, vst_cur);
+        mask_tile(scur, j_cur * BKV);
+        bf16x8 pf[4];
+        const float alpha = qk_softmax(scur, snext, kst_next, pf);
+        if (__ballot(alpha != 1.0f)) {  // wave-uniform: some row moved its reference
+#pragma unroll
+            for (int m = 0; m < DBLK; ++m) oacc[m] *= alpha;
+        }
+        pv(pf, vst_cur);
         j_cur = j_next;
         j_next = j_after;
         __builtin_amdgcn_s_waitcnt(kVmcnt0);

@@ -221,27 +221,36 @@ struct MaskT { typedef uint32_t type; };
 template <>
 struct MaskT<64> { typedef uint64_t type; };
 
+// Bits lo..hi (clipped to 0..63) of a 64-bit word; empty when lo > hi.
+__device__ __forceinline__ uint64_t range_bits(int lo, int hi) {
+    lo = lo < 0 ? 0 : lo;
+    hi = hi > 63 ? 63 : hi;
+    if (lo > hi) return 0ull;
+    const uint64_t upto = hi == 63 ? ~0ull : ((1ull << (hi + 1)) - 1ull);
+    return upto & ~((1ull << lo) - 1ull);
+}
+
 template <int EPL>
 __device__ typename MaskT<EPL>::type select_top(const float (&s)[EPL], typename MaskT<EPL>::type active,
                                                 int need, uint32_t* hist, int lane) {
     typedef typename MaskT<EPL>::type M;
+    constexpr int NB = (EPL + 3) / 4;  // packed bucket bytes
     M picked = 0;
+    uint32_t bk[NB];
     for (int iter = 0; iter < 64 && need > 0; ++iter) {
-        int mine = __builtin_popcountll((uint64_t)active);
-        const int na = wave_sum_i(mine);
+        const int na = wave_sum_i(__builtin_popcountll((uint64_t)active));
         if (na <= need) {
             picked |= active;
-            active = 0;
             need = 0;
             break;
         }
         float lo = FLT_MAX, hi = -FLT_MAX;
 #pragma unroll
-        for (int t = 0; t < EPL; ++t)
-            if ((active >> t) & 1) {
-                lo = fminf(lo, s[t]);
-                hi = fmaxf(hi, s[t]);
-            }
+        for (int t = 0; t < EPL; ++t) {
+            const bool on = (active >> t) & 1;
+            lo = fminf(lo, on ? s[t] : FLT_MAX);
+            hi = fmaxf(hi, on ? s[t] : -FLT_MAX);
+        }
         lo = wave_min_f(lo);
         hi = wave_max_f(hi);
         if (!(hi > lo)) break;  // every remaining score is equal: index order below
@@ -250,45 +259,42 @@ __device__ typename MaskT<EPL>::type select_top(const float (&s)[EPL], typename 
         const float range = half ? 0.5f * hi - 0.5f * lo : hi - lo;
         float scale = 255.0f / range;
         if (!(scale <= FLT_MAX)) scale = FLT_MAX;
-        auto bucket = [&](float x) -> int {
-            if (x == hi) return 255;
-            const float u = ((half ? 0.5f * x : x) - lo_u) * scale;
-            const int b = (int)u;
-            return b > 254 ? 254 : (b < 0 ? 0 : b);
-        };
         for (int q = lane; q < 256; q += 64) hist[q] = 0;
         wave_lds_sync();
 #pragma unroll
-        for (int t = 0; t < EPL; ++t)
-            if ((active >> t) & 1) atomicAdd(&hist[bucket(s[t])], 1u);
+        for (int w = 0; w < NB; ++w) bk[w] = 0;
+#pragma unroll
+        for (int t = 0; t < EPL; ++t) {
+            const float x = s[t];
+            const float u = ((half ? 0.5f * x : x) - lo_u) * scale;
+            int b = (int)u;
+            b = b > 254 ? 254 : (b < 0 ? 0 : b);
+            b = (x == hi) ? 255 : b;
+            bk[t >> 2] |= (uint32_t)b << (8 * (t & 3));
+            // inactive elements count into this lane's spare bin (256 + lane): no branch
+            atomicAdd(&hist[((active >> t) & 1) ? b : 256 + lane], 1u);
+        }
         wave_lds_sync();
         // Lane L owns buckets 4L .. 4L+3. Count what lies strictly above each.
         const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
                        h3 = hist[4 * lane + 3];
         const int own = (int)(h0 + h1 + h2 + h3);
-        int above_lane = 0;  // sum over lanes with a larger index
-        {
-            int x = own;
+        int x = own;
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_down(x, o);
-                if (lane + o < 64) x += y;
-            }
-            above_lane = x - own;  // inclusive suffix minus own
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_down(x, o);
+            if (lane + o < 64) x += y;
         }
+        int ab = x - own;  // sum over lanes with a larger index
         int found = -1, found_above = 0;
-        {
-            int ab = above_lane;
-            const uint32_t hh[4] = {h3, h2, h1, h0};
+        const uint32_t hh[4] = {h3, h2, h1, h0};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int q = 4 * lane + 3 - e;
-                if (found < 0 && ab < need && need <= ab + (int)hh[e]) {
-                    found = q;
-                    found_above = ab;
-                }
-                ab += (int)hh[e];
+        for (int e = 0; e < 4; ++e) {
+            if (found < 0 && ab < need && need <= ab + (int)hh[e]) {
+                found = 4 * lane + 3 - e;
+                found_above = ab;
             }
+            ab += (int)hh[e];
         }
         wave_lds_sync();
         const uint64_t who = __ballot(found >= 0);
@@ -297,12 +303,12 @@ __device__ typename MaskT<EPL>::type select_top(const float (&s)[EPL], typename 
         const int above = __shfl(found_above, src);
         M next = 0;
 #pragma unroll
-        for (int t = 0; t < EPL; ++t)
-            if ((active >> t) & 1) {
-                const int bk = bucket(s[t]);
-                if (bk > bstar) picked |= (M)1 << t;
-                else if (bk == bstar) next |= (M)1 << t;
-            }
+        for (int t = 0; t < EPL; ++t) {
+            const int b = (bk[t >> 2] >> (8 * (t & 3))) & 0xff;
+            const M on = (active >> t) & 1;
+            picked |= (on & (M)(b > bstar)) << t;
+            next |= (on & (M)(b == bstar)) << t;
+        }
         active = next;
         need -= above;
     }
@@ -310,14 +316,14 @@ __device__ typename MaskT<EPL>::type select_top(const float (&s)[EPL], typename 
         const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
         for (int t = 0; t < EPL; ++t) {
-            const bool a = (active >> t) & 1;
-            const uint64_t m = __ballot(a);
+            const bool on = (active >> t) & 1;
+            const uint64_t m = __ballot(on);
             const int cnt = __builtin_popcountll(m);
             if (cnt <= need) {
-                if (a) picked |= (M)1 << t;
+                if (on) picked |= (M)1 << t;
                 need -= cnt;
             } else {
-                if (a && __builtin_popcountll(m & below) < need) picked |= (M)1 << t;
+                if (on && __builtin_popcountll(m & below) < need) picked |= (M)1 << t;
                 need = 0;
             }
             if (need == 0) break;
@@ -329,8 +335,9 @@ __device__ typename MaskT<EPL>::type select_top(const float (&s)[EPL], typename 
 template <int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     typedef typename MaskT<EPL>::type M;
-    __shared__ uint32_t hist_all[4][256];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ uint32_t hist_all[4][256 + 64];  // 256 buckets + one spare bin per lane
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar row math
     uint32_t* hist = hist_all[wave];
     const int64_t lr = (int64_t)blockIdx.x * 4 + wave;
     const int64_t nrows = (int64_t)a.B * a.nh * a.NQ;
@@ -346,25 +353,35 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
         a.pin_words ? a.pin_words + (((int64_t)(b % a.pb) * a.ph + (h % a.ph)) * a.NQ + i) * a.NKW : nullptr;
     const uint64_t* dw =
         a.drop_words ? a.drop_words + (((int64_t)(b % a.db) * a.dh + (h % a.dh)) * a.NQ + i) * a.NKW : nullptr;
-    const int64_t qlo = (int64_t)i * a.block_q, qhi = (int64_t)(i + 1) * a.block_q;
+    // Diagonal: kv tiles j with i*bq < (j+1)*bkv and j*bkv < (i+1)*bq, i.e.
+    // floor(i*bq/bkv) <= j <= ceil((i+1)*bq/bkv) - 1.
+    const int dlo = (int)(((int64_t)i * a.block_q) / a.block_kv);
+    const int dhi = (int)(((int64_t)(i + 1) * a.block_q + a.block_kv - 1) / a.block_kv) - 1;
 
+    // Scores: slot t of lane L is element 64t + L (index clamped in range;
+    // slots past NK are never candidates).
     float s[EPL];
-    M cand = 0, must_kept = 0;
 #pragma unroll
+    for (int t = 0; t < EPL; ++t) s[t] = srow[min(64 * t + lane, a.NK - 1)];
+    // Masks: wave-uniform 64-bit words per slot (bit = lane), built one slot
+    // at a time on the scalar unit.
+    M cand = 0, must_kept = 0;
+    int c = 0;
+#pragma unroll 1
     for (int t = 0; t < EPL; ++t) {
-        const int j = 64 * t + lane;
-        const bool valid = j < a.NK;
-        s[t] = valid ? srow[j] : 0.f;
-        const bool in_words = 64 * t < a.NK;
-        const bool pin = (pw && in_words) ? ((pw[t] >> lane) & 1) : false;
-        const bool drop = (dw && in_words) ? ((dw[t] >> lane) & 1) : false;
-        const bool diag = (qlo < (int64_t)(j + 1) * a.block_kv) && ((int64_t)j * a.block_kv < qhi);
-        const bool must = valid && (diag || pin);
-        const bool forb = valid && drop;
-        if (valid && !must && !forb) cand |= (M)1 << t;
-        if (must && !forb) must_kept |= (M)1 << t;
+        const int base = 64 * t;
+        const int rem = a.NK - base;
+        const uint64_t valid = rem >= 64 ? ~0ull : (rem > 0 ? (1ull << rem) - 1ull : 0ull);
+        const uint64_t diag = range_bits(dlo - base, dhi - base);
+        const uint64_t pin = (pw && rem > 0) ? pw[t] : 0ull;
+        const uint64_t drop = (dw && rem > 0) ? dw[t] : 0ull;
+        const uint64_t must = (diag | pin) & valid;
+        const uint64_t cw = valid & ~must & ~drop;
+        const uint64_t mk = must & ~drop;
+        c += __builtin_popcountll(cw);
+        cand |= (M)((cw >> lane) & 1ull) << t;
+        must_kept |= (M)((mk >> lane) & 1ull) << t;
     }
-    const int c = wave_sum_i(__builtin_popcountll((uint64_t)cand));
     // k_r = ceil(fl32(c) * fl32(budget)): the product rounds to fp32 first.
     const float kf = ceilf(__fmul_rn((float)c, a.budget));
     const int k = (kf >= (float)c) ? c : (int)kf;

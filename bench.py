@@ -210,6 +210,7 @@ def main():
     attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
 
     value = full_flops / (ms_step * 1e-3) / 1e12
+    kv_bytes = float(tiles * 2 * w.block_kv * w.D * 2 + 2 * q.numel() * q.element_size())
     attn_tflops = full_flops / (attn_ms * 1e-3) / 1e12
     select_bytes = (q.numel() + k.numel()) * q.element_size() + sel.keep.numel() + 4 * (sel.nnz + sel.row_ptr.numel())
     select_bytes += (2 * w.nq * ((w.nk + 63) // 64) * 8)  # bit-packed pins + drops
@@ -238,7 +239,14 @@ def main():
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
                      "flops_per_launch": full_flops, "visible_pair_flops_per_launch": vis_flops,
-                     "avg_launch_ms": round(attn_ms, 4)},
+                     "avg_launch_ms": round(attn_ms, 4),
+                     # K/V supply: every kept, live tile visit reads one 64-key K tile and
+                     # one V tile (32 KiB at D = 128) unless L2 still holds it; plus Q read
+                     # and O written once. On this workload the visits are scattered and
+                     # this stream, not the matrix cores, bounds the kernel.
+                     "kv_visit_bytes_per_launch": kv_bytes,
+                     "kv_visit_GBps": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1),
+                     "kv_visit_frac_hbm": round(kv_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "stages": {"select_ms": round(sel_ms, 4), "select_GBps": round(select_gbs, 1),
                    "select_frac_hbm": round(select_gbs / PEAK_HBM_GBS, 4),
                    "select_algorithmic_bytes": select_bytes, "attn_ms": round(attn_ms, 4),

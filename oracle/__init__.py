@@ -32,3 +32,4 @@ from .select import (  # noqa: F401
     NEAR_TIE_REL,
 )
 from .attention import attention, attention_dense_literal, visible_key_counts  # noqa: F401
+from .attention_bwd import attention_backward  # noqa: F401

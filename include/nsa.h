@@ -156,6 +156,34 @@ int nsa_block_sparse_attn(const nsa_tensor* q, const nsa_tensor* k, const nsa_te
                           const nsa_selection* sel, int causal, nsa_tensor* out,
                           float* lse, void* stream);
 
+/* Device workspace, in bytes, that nsa_block_sparse_attn_bwd needs for these
+ * shapes and this selection (sel may be NULL for dense). Host only. */
+int nsa_attn_bwd_workspace_size(const nsa_tensor* q, const nsa_tensor* k, const nsa_selection* sel,
+                                int64_t* bytes);
+
+/* Gradients of nsa_block_sparse_attn (same visibility, same selection). With
+ * P_tu = exp(l_tu - lse[t]) on visible pairs and dO the upstream gradient:
+ *   Delta_t = dO_t . out_t,  dS_tu = P_tu (dO_t . v_u - Delta_t)
+ *   dq[t] = D^-1/2 sum_u dS_tu k_u
+ *   dk[u] = D^-1/2 sum_t dS_tu q_t,  dv[u] = sum_t P_tu dO_t
+ * where the sums for dk and dv also run over the query heads of the kv head's
+ * GQA group. Queries with no visible key (lse = -inf) contribute nothing.
+ * This differentiates the consumer of the selection page's BlockSelection;
+ * the selection itself (a top-k) has no gradient.
+ *   q, out, dout, dq: (B, Hq, S, D); k, v, dk, dv: (B, Hkv, S, D); all the
+ *   dtype of q. lse: device fp32 (B, Hq, S) as returned by the forward.
+ *   sel: the forward's selection, or NULL for dense. Its keep flags are read
+ *   to build a kv-tile-major index and row_ptr / col_idx for the query-major
+ *   walk, so both must describe the same selection (nsa_select writes both).
+ *   workspace: device scratch of nsa_attn_bwd_workspace_size bytes, 256-byte
+ *   aligned; contents undefined afterwards.
+ * Every element of dq, dk and dv is written. Errors as the forward, plus
+ * WORKSPACE. */
+int nsa_block_sparse_attn_bwd(const nsa_tensor* q, const nsa_tensor* k, const nsa_tensor* v,
+                              const nsa_tensor* out, const float* lse, const nsa_tensor* dout,
+                              const nsa_selection* sel, int causal, nsa_tensor* dq, nsa_tensor* dk,
+                              nsa_tensor* dv, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Stage entry point: pool_blocks of the selection page on its own.
  * x: (B, H, S, D) F32/BF16 device; out: device fp32 (B, H, ceil(S/block), D). */
 int nsa_pool_blocks(const nsa_tensor* x, int32_t block, float* out, void* stream);

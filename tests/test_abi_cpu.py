@@ -171,3 +171,54 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(N, "_LIB", None)
     with pytest.raises(RuntimeError, match="missing"):
         N.lib()
+
+
+def _bwd(L, q, k, v, out, lse, do, sel, causal, dq, dk, dv, ws, nbytes):
+    return L.nsa_block_sparse_attn_bwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(out), lse,
+                                       ctypes.byref(do), ctypes.byref(sel) if sel is not None else None, causal,
+                                       ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ws, nbytes, None)
+
+
+def test_backward_workspace_size(L):
+    q, k = _t(2, 4, 1000, 128), _t(2, 2, 1000, 128)
+    n = ctypes.c_int64(-1)
+    assert L.nsa_attn_bwd_workspace_size(ctypes.byref(q), ctypes.byref(k), None, ctypes.byref(n)) == 0
+    a = lambda x: (x + 255) // 256 * 256
+    assert n.value == a(2 * 4 * 1000 * 4)  # Delta only
+    sel = N._Selection(keep=1, row_ptr=1, col_idx=1, nnz=300, B=2, H=4, NQ=8, NK=16, block_q=128, block_kv=64,
+                       seq_q=1000, seq_kv=1000)
+    assert L.nsa_attn_bwd_workspace_size(ctypes.byref(q), ctypes.byref(k), ctypes.byref(sel), ctypes.byref(n)) == 0
+    assert n.value == a(2 * 4 * 1000 * 4) + a(2 * 4 * 16 * 4) + a((2 * 4 * 16 + 1) * 4) + a(300 * 4)
+    bad = N._Selection(keep=1, row_ptr=1, col_idx=1, nnz=300, B=2, H=3, NQ=8, NK=16, block_q=128, block_kv=64,
+                       seq_q=1000, seq_kv=1000)
+    assert L.nsa_attn_bwd_workspace_size(ctypes.byref(q), ctypes.byref(k), ctypes.byref(bad), ctypes.byref(n)) == -2
+    assert L.nsa_attn_bwd_workspace_size(ctypes.byref(q), ctypes.byref(k), None, None) == -1
+
+
+def test_backward_rejects_before_launch(L):
+    q, k = _t(1, 4, 256, 128), _t(1, 2, 256, 128)
+    lse = ctypes.c_void_p(1)
+    ws = ctypes.c_void_p(256)
+    big = 1 << 30
+    ok = dict(q=q, k=k, v=_t(1, 2, 256, 128), out=_t(1, 4, 256, 128), lse=lse, do=_t(1, 4, 256, 128), sel=None,
+              causal=1, dq=_t(1, 4, 256, 128), dk=_t(1, 2, 256, 128), dv=_t(1, 2, 256, 128), ws=ws, nbytes=big)
+
+    def call(**over):
+        args = dict(ok)
+        args.update(over)
+        return _bwd(L, **args)
+
+    assert call(v=_t(1, 2, 256, 128, N.NSA_F32)) == -3             # dtype mismatch
+    assert call(dq=_t(1, 4, 255, 128)) == -2                        # dq shape
+    assert call(dk=_t(1, 4, 256, 128)) == -2                        # dk heads
+    assert call(lse=None) == -1                                     # missing lse
+    assert call(nbytes=16) == -5                                    # workspace too small
+    assert call(ws=None) == -5
+    assert call(q=_t(1, 4, 256, 96), out=_t(1, 4, 256, 96), do=_t(1, 4, 256, 96), dq=_t(1, 4, 256, 96),
+                k=_t(1, 2, 256, 96), v=_t(1, 2, 256, 96), dk=_t(1, 2, 256, 96), dv=_t(1, 2, 256, 96)) == -4
+    sel_nokeep = N._Selection(keep=None, row_ptr=1, col_idx=1, nnz=5, B=1, H=4, NQ=2, NK=4, block_q=128,
+                              block_kv=64, seq_q=256, seq_kv=256)
+    assert call(sel=sel_nokeep) == -1
+    sel_badnnz = N._Selection(keep=1, row_ptr=1, col_idx=1, nnz=-3, B=1, H=4, NQ=2, NK=4, block_q=128,
+                              block_kv=64, seq_q=256, seq_kv=256)
+    assert call(sel=sel_badnnz) == -2

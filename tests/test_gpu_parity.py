@@ -62,6 +62,8 @@ CASES = [
     ("bf16_shared_noncausal_ragged", 1, 4, 4, 777, 128, 128, 64, 0.25, True, False, torch.bfloat16),
     ("bf16_d64_bq64_gqa8", 1, 8, 1, 2048, 64, 64, 64, 0.20, False, True, torch.bfloat16),
     ("bf16_bq32", 1, 2, 2, 640, 128, 32, 64, 0.40, False, True, torch.bfloat16),
+    ("bf16_bq96_ragged", 1, 2, 1, 1000, 128, 96, 64, 0.30, False, True, torch.bfloat16),
+    ("bf16_d64_bq96", 1, 4, 2, 1000, 64, 96, 64, 0.30, False, True, torch.bfloat16),
     ("bf16_general_kernel_bkv32", 1, 2, 1, 700, 64, 64, 32, 0.30, False, True, torch.bfloat16),
     ("f32_d128_noncausal", 1, 2, 2, 600, 128, 128, 64, 0.50, False, False, torch.float32),
     ("bf16_budget0", 1, 2, 2, 1024, 128, 128, 64, 0.0, False, False, torch.bfloat16),

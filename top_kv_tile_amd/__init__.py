@@ -12,7 +12,9 @@ from .nsa import (  # noqa: F401
     Sizes,
     SparseSpec,
     lib,
+    nsa_attn_bwd_workspace_size,
     nsa_block_sparse_attn,
+    nsa_block_sparse_attn_bwd,
     nsa_pool_blocks,
     nsa_score_blocks,
     nsa_select,

@@ -1,0 +1,945 @@
+// Gradients of block-sparse attention for gfx950 (CDNA4).
+//
+// The forward is softmax attention of each query over the keys of the kv
+// tiles its query tile keeps (keep flags / CSR of the selection defined on the
+// page "automatic/modules/attention/sparse/selector.py", BlockSelection), with
+// GQA, an optional causal mask and scale D^-1/2. Given dO and the forward's
+// LSE, with P_tu = exp(scale q_t.k_u - LSE_t) on visible pairs:
+//   Delta_t = dO_t . O_t
+//   dP_tu = dO_t . v_u,  dS_tu = P_tu (dP_tu - Delta_t)
+//   dQ_t = scale sum_u dS_tu k_u
+//   dK_u = scale sum_t dS_tu q_t,  dV_u = sum_t P_tu dO_t   (summed over the heads of a GQA group)
+// Tiles entirely in the causal future are skipped as in the forward.
+//
+// Kernels:
+//  * delta_kernel: Delta per query row.
+//  * colcount_kernel / colscan_kernel / colfill_kernel: the kv-tile-major
+//    index of the keep flags (for each selection head and kv tile, the query
+//    tiles that keep it, ascending).
+//  * bwd_dq_mfma_kernel: one workgroup per (batch, query head, query tile),
+//    walking the query-major CSR like the forward. S^T = K Q^T and
+//    dP^T = V dO^T, then dQ^T += K^T dS^T with K^T read from the row-major K
+//    tile by transposing LDS reads.
+//  * bwd_dkdv_mfma_kernel: one workgroup per (batch, kv head, kv tile),
+//    walking the kv-tile-major index over the query heads of the group in
+//    64-query chunks. S = Q K^T and dP = dO V^T, then dV^T += dO^T P and
+//    dK^T += Q^T dS with Q^T / dO^T read by transposing LDS reads.
+//  * bwd_dq_simt_kernel / bwd_dkdv_simt_kernel: fp32 FMA fallback for fp32
+//    inputs and block sizes the MFMA kernels do not take.
+#include "nsa_internal.h"
+
+#include <math.h>
+
+namespace nsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kPosInf = __builtin_huge_valf();
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters at their maximum
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+// LSE in log2 units as the exponent offset of P; an empty row (LSE = -inf)
+// maps to +inf so that every P of that row is exactly 0.
+__device__ __forceinline__ float lse_offset(float lse) { return lse == kNegInf ? kPosInf : lse * kLog2e; }
+
+__device__ __forceinline__ float load_elem(const void* base, int64_t idx, bool bf16) {
+    if (bf16) return __uint_as_float((uint32_t)((const uint16_t*)base)[idx] << 16);
+    return ((const float*)base)[idx];
+}
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ============================================================ preprocessing
+
+// Delta[r] = sum_d dO[r, d] * O[r, d] in fp32; D / 8 lanes per row, 8 elements per lane.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void delta_kernel(const void* out, const void* dout, float* delta, int64_t rows) {
+    constexpr int LPR = D / 8;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t r = t / LPR;
+    const int part = (int)(t % LPR);
+    float acc = 0.f;
+    if (r < rows) {
+        const int64_t base = r * D + part * 8;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc += load_elem(dout, base + x, BF16) * load_elem(out, base + x, BF16);
+    }
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (r < rows && part == 0) delta[r] = acc;
+}
+
+// counts[bh * NK + j] = number of query tiles i with keep[bh, i, j] != 0.
+// Grid: blocks of 256 columns, ceil(NK / 256) per slab bh.
+__global__ __launch_bounds__(256) void colcount_kernel(const int8_t* keep, int NQ, int NK, int32_t* counts) {
+    const int per = (NK + 255) / 256;
+    const int64_t bh = blockIdx.x / per;
+    const int j = (int)(blockIdx.x % per) * 256 + threadIdx.x;
+    if (j >= NK) return;
+    const int8_t* col = keep + bh * NQ * (int64_t)NK + j;
+    int c = 0;
+    for (int i = 0; i < NQ; ++i) c += col[(int64_t)i * NK] != 0;
+    counts[bh * NK + j] = c;
+}
+
+// Exclusive prefix sum of n counts into col_ptr[0 .. n] (one workgroup),
+// clamped to cap (the capacity of row_idx) so that flags that disagree with the
+// CSR cannot index past it.
+__global__ __launch_bounds__(1024) void colscan_kernel(const int32_t* counts, int64_t n, int32_t cap,
+                                                       int32_t* col_ptr) {
+    __shared__ int32_t part[1024];
+    const int tid = threadIdx.x;
+    const int64_t per = (n + 1023) / 1024;
+    const int64_t lo = min(n, tid * per), hi = min(n, lo + per);
+    int32_t s = 0;
+    for (int64_t x = lo; x < hi; ++x) s += counts[x];
+    part[tid] = s;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan
+        const int32_t v = tid >= o ? part[tid - o] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    int32_t run = part[tid] - s;
+    for (int64_t x = lo; x < hi; ++x) {
+        col_ptr[x] = min(run, cap);
+        run += counts[x];
+    }
+    if (tid == 1023) col_ptr[n] = min(part[1023], cap);
+}
+
+// row_idx[col_ptr[bh * NK + j] ..] = the query tiles keeping (bh, j), ascending.
+__global__ __launch_bounds__(256) void colfill_kernel(const int8_t* keep, int NQ, int NK, const int32_t* col_ptr,
+                                                      int32_t* row_idx) {
+    const int per = (NK + 255) / 256;
+    const int64_t bh = blockIdx.x / per;
+    const int j = (int)(blockIdx.x % per) * 256 + threadIdx.x;
+    if (j >= NK) return;
+    const int8_t* col = keep + bh * NQ * (int64_t)NK + j;
+    int32_t p = col_ptr[bh * NK + j];
+    const int32_t p_end = col_ptr[bh * NK + j + 1];
+    for (int i = 0; i < NQ && p < p_end; ++i)
+        if (col[(int64_t)i * NK] != 0) row_idx[p++] = i;
+}
+
+// ============================================================ shared helpers
+
+// Range of query-major CSR entries for query tile (b, h, i) up to query q_last.
+__device__ __forceinline__ void q_tile_range(const AttnBwdArgs& a, int b, int h, int i, int q_last, int& start,
+                                             int& end) {
+    if (a.row_ptr) {
+        const int hs = (a.Hsel == 1) ? 0 : h;
+        const int64_t r = ((int64_t)b * a.Hsel + hs) * a.NQ + i;
+        start = a.row_ptr[r];
+        end = a.row_ptr[r + 1];
+        if (a.causal) {
+            int lo = start, hi = end;  // first entry starting after q_last
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if ((int64_t)a.col_idx[mid] * a.block_kv > q_last) hi = mid;
+                else lo = mid + 1;
+            }
+            end = lo;
+        }
+    } else {
+        start = 0;
+        end = a.NK;
+        if (a.causal) end = min(a.NK, q_last / a.block_kv + 1);
+    }
+}
+
+// Range of kv-tile-major entries for kv tile (b, selection head hs, j), trimmed
+// under causal to query tiles whose last row reaches key0. Dense: all tiles.
+__device__ __forceinline__ void kv_tile_range(const AttnBwdArgs& a, int b, int hs, int j, int key0, int& start,
+                                              int& end) {
+    if (a.col_ptr) {
+        const int64_t c = ((int64_t)b * a.Hsel + hs) * a.NK + j;
+        start = a.col_ptr[c];
+        end = a.col_ptr[c + 1];
+        if (a.causal) {
+            int lo = start, hi = end;  // first entry whose tile ends at or after key0
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if ((int64_t)a.row_idx[mid] * a.block_q + a.block_q - 1 >= key0) hi = mid;
+                else lo = mid + 1;
+            }
+            start = lo;
+        }
+    } else {
+        start = a.causal ? key0 / a.block_q : 0;
+        end = a.NQ;
+    }
+}
+__device__ __forceinline__ int kv_entry(const AttnBwdArgs& a, int e) { return a.row_idx ? a.row_idx[e] : e; }
+
+// ============================================================ MFMA geometry
+//
+// A 64-row tile of D bf16 per row, row-major in LDS, filled by buffer-to-LDS
+// DMA (1 KiB per wave instruction). Rows are XOR-swizzled in 16-byte chunks.
+// Tiles read only as rows (16 bytes per lane, 16 consecutive rows per pass)
+// use rswz = (row / RPB) % CH. Tiles read both as rows and transposed
+// (ds_read_b64_tr_b16: 4 consecutive rows x 4 columns of 8 bytes per 16
+// lanes) use bswz, a one-bit rotation of the same index: consecutive rows map
+// to distinct chunks (row reads), and the four rows of a transposed read land
+// in distinct chunk pairs (transposed reads). Both are bank-conflict free.
+template <int D>
+struct Geo {
+    static constexpr int ROWB = D * 2;
+    static constexpr int CH = ROWB / 16;
+    static constexpr int CHB = CH == 16 ? 4 : 3;  // log2(CH)
+    static constexpr int RPB = 256 / ROWB;
+    static constexpr int TILEB = 64 * ROWB;
+    static constexpr int RPI = 1024 / ROWB;
+    static constexpr int NINSTR = TILEB / 1024;
+    __device__ static int rswz(int row) { return (row / RPB) % CH; }
+    __device__ static int bswz(int row) {
+        const int x = (row / RPB) % CH;
+        return ((x << 1) | (x >> (CHB - 1))) & (CH - 1);
+    }
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) short4_t lds_s4;
+
+// DMA of one 64-row tile (rows row0 .. row0 + 63 of a head, clamped to S - 1)
+// into `dst`, by the NW waves of the workgroup. `swz` picks the swizzle.
+template <int D, int NW, bool BOTH>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, char* dst, int row0, int S, int wave, int lane) {
+    using G = Geo<D>;
+#pragma unroll
+    for (int x = 0; x < (G::NINSTR + NW - 1) / NW; ++x) {
+        const int ii = wave + NW * x;
+        if (G::NINSTR % NW == 0 || ii < G::NINSTR) {
+            const int row = ii * G::RPI + lane / G::CH, pc = lane % G::CH;
+            const int chunk = pc ^ (BOTH ? G::bswz(row) : G::rswz(row));
+            const int off = min(row0 + row, S - 1) * G::ROWB + chunk * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + ii * 1024), 16, off, 0, 0, 0);
+        }
+    }
+}
+
+// 16-byte row fragment: row `row`, logical chunk `chunk`.
+template <int D, bool BOTH>
+__device__ __forceinline__ bf16x8 row_frag(const char* tile, int row, int chunk) {
+    using G = Geo<D>;
+    const int pc = chunk ^ (BOTH ? G::bswz(row) : G::rswz(row));
+    return __builtin_bit_cast(bf16x8, *(const u32x4*)(tile + row * G::ROWB + pc * 16));
+}
+
+// Transposed A fragment for a 32x32x16 MFMA whose contraction runs over tile
+// rows: lane (l32, hf) receives column d = 32 m + l32 at rows
+// r0 + 4 hf + (0..3) and r0 + 8 + 4 hf + (0..3). Within each 16-lane group,
+// ds_read_b64_tr_b16 gives result element e of lane i from element (i mod 4)
+// of the 8 bytes addressed by lane 4e + i/4.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int r0, int m, int lane) {
+    using G = Geo<D>;
+    const int vg = lane >> 4, vs = lane & 15, hf = lane >> 5;
+    const int d = 32 * m + 16 * (vg & 1) + 4 * (vs & 3);
+    const int row0 = r0 + 4 * hf + (vs >> 2);
+    const int row1 = row0 + 8;
+    const int c = d >> 3, b = (d & 7) * 2;
+    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s4*)(tile + row0 * G::ROWB + ((c ^ G::bswz(row0)) * 16) + b));
+    const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s4*)(tile + row1 * G::ROWB + ((c ^ G::bswz(row1)) * 16) + b));
+    const short8_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ============================================================ dQ (MFMA)
+//
+// Work item order as in the forward: kv-head major, query tile descending,
+// query head fastest, runs of 64 blocks spread over the 8 XCDs.
+struct Work {
+    int b, h, g, i;
+};
+__device__ __forceinline__ Work decode_q_work(int64_t n, int64_t total, int Hq, int Hkv, int NQ) {
+    int64_t w = n;
+    const int64_t full = (total / 64) * 64;
+    if (n < full) {
+        const int64_t run = n >> 6;
+        const int r = (int)(n & 63);
+        w = run * 64 + (r & 7) * 8 + (r >> 3);
+    }
+    const int G = Hq / Hkv;
+    Work wk;
+    const int hh = (int)(w % G);
+    w /= G;
+    wk.i = NQ - 1 - (int)(w % NQ);
+    w /= NQ;
+    wk.g = (int)(w % Hkv);
+    wk.b = (int)(w / Hkv);
+    wk.h = wk.g * G + hh;
+    return wk;
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void bwd_dq_mfma_kernel(AttnBwdArgs a) {
+    constexpr int KSTEPS = D / 16;
+    constexpr int DBLK = D / 32;
+    using G = Geo<D>;
+    extern __shared__ __attribute__((aligned(1024))) char lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int64_t total = (int64_t)a.B * a.Hq * a.NQ;
+    const Work wk = decode_q_work(blockIdx.x, total, a.Hq, a.Hkv, a.NQ);
+    const int bq = a.block_q;
+    const int q0 = wk.i * bq;
+    const int qw0 = q0 + wave * 32;
+    const int q_last = min(q0 + bq, a.S) - 1;
+    const int qrow = qw0 + l32;
+    const bool qvalid = qrow < a.S && (wave * 32 + l32) < bq;
+
+    const int head_bytes = a.S * G::ROWB;
+    const int64_t qhead = ((int64_t)wk.b * a.Hq + wk.h) * a.S;
+    const int64_t khead = ((int64_t)wk.b * a.Hkv + wk.g) * a.S;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc((const uint16_t*)a.q + qhead * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t dors = make_rsrc((const uint16_t*)a.dout + qhead * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc((const uint16_t*)a.k + khead * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const uint16_t*)a.v + khead * D, head_bytes);
+
+    // B operands of S^T = K Q^T and dP^T = V dO^T: this lane's query row.
+    bf16x8 qf[KSTEPS], dof[KSTEPS];
+    {
+        const int off = (wave * 32 + l32) < bq ? (qrow * D + 8 * hf) * 2 : head_bytes;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, off + 32 * ks, 0, 0));
+            dof[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(dors, off + 32 * ks, 0, 0));
+        }
+    }
+    const float lse_l2 = qvalid ? lse_offset(a.lse[qhead + qrow]) : kPosInf;
+    const float delta = qvalid ? a.delta[qhead + qrow] : 0.f;
+
+    int e_begin, e_end;
+    q_tile_range(a, wk.b, wk.h, wk.i, q_last, e_begin, e_end);
+    const int ntiles = e_end - e_begin;
+    int col_base = e_begin, col_lane = 0;
+    auto fetch_cols = [&](int base) {
+        col_base = base;
+        const int e = base + lane;
+        col_lane = a.row_ptr ? (e < e_end ? a.col_idx[e] : 0) : e;
+    };
+    fetch_cols(e_begin);
+    auto tile_of = [&](int n) -> int {
+        const int e = e_begin + n;
+        if (e - col_base >= 64) fetch_cols(e);
+        return __builtin_amdgcn_readlane(col_lane, e - col_base);
+    };
+
+    // LDS: K stages 0/1 then V stages 0/1, one 64-key tile each.
+    auto kst = [&](int st) -> char* { return lds + st * G::TILEB; };
+    auto vst = [&](int st) -> char* { return lds + (2 + st) * G::TILEB; };
+
+    f32x16 dq[DBLK];
+#pragma unroll
+    for (int m = 0; m < DBLK; ++m) dq[m] = (f32x16){};
+
+    int j_cur = 0;
+    if (ntiles > 0) {
+        j_cur = tile_of(0);
+        dma_tile<D, NW, true>(krs, kst(0), j_cur * 64, a.S, wave, lane);
+        dma_tile<D, NW, false>(vrs, vst(0), j_cur * 64, a.S, wave, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+
+    for (int n = 0; n < ntiles; ++n) {
+        const int st = n & 1;
+        const int j_next = (n + 1 < ntiles) ? tile_of(n + 1) : 0;
+        if (n + 1 < ntiles) {  // stage st ^ 1 was last read in step n - 1
+            dma_tile<D, NW, true>(krs, kst(st ^ 1), j_next * 64, a.S, wave, lane);
+            dma_tile<D, NW, false>(vrs, vst(st ^ 1), j_next * 64, a.S, wave, lane);
+        }
+        const char* kt = kst(st);
+        const char* vt = vst(st);
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            s[mb] = (f32x16){};
+            dp[mb] = (f32x16){};
+        }
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                s[mb] = mfma(row_frag<D, true>(kt, 32 * mb + l32, 2 * ks + hf), qf[ks], s[mb]);
+                dp[mb] = mfma(row_frag<D, false>(vt, 32 * mb + l32, 2 * ks + hf), dof[ks], dp[mb]);
+            }
+        // Lane holds query qrow and keys 32 mb + 8 (x / 4) + 4 hf + (x % 4) of the tile at [mb][x].
+        const int key0 = j_cur * 64;
+        const bool need_mask = (a.causal && key0 + 63 > qw0) || (key0 + 64 > a.S);
+        int lim = 63;
+        if (need_mask) {
+            lim = min(63, a.S - 1 - key0);
+            if (a.causal) lim = min(lim, qrow - key0);
+        }
+        bf16x8 dsf[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int mb = kk >> 1, q4 = 8 * (kk & 1);
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                const int off = 32 * mb + 8 * ((q4 + x) >> 2) + 4 * hf + ((q4 + x) & 3);
+                float p = fast_exp2(__builtin_fmaf(s[mb][q4 + x], a.scale_log2, -lse_l2));
+                p = off <= lim ? p : 0.f;
+                dsf[kk][x] = (__bf16)(p * (dp[mb][q4 + x] - delta));
+            }
+        }
+        // dQ^T += K^T dS^T; contraction over keys 16 kk + 4 hf + (0..3), 16 kk + 8 + 4 hf + (0..3).
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int m = 0; m < DBLK; ++m) dq[m] = mfma(tr_frag<D>(kt, 16 * kk, m, lane), dsf[kk], dq[m]);
+        j_cur = j_next;
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        __syncthreads();
+    }
+
+    if (qvalid) {
+        uint16_t* op = (uint16_t*)a.dq + (qhead + qrow) * D;
+#pragma unroll
+        for (int m = 0; m < DBLK; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                bf16x4 w;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) w[x] = (__bf16)(dq[m][4 * q + x] * a.scale);
+                *(bf16x4*)(op + 32 * m + 8 * q + 4 * hf) = w;
+            }
+    }
+}
+
+// ============================================================ dK / dV (MFMA)
+//
+// Workgroup = 4 waves on one kv tile of 64 keys; wave w owns keys 32 (w & 1)
+// .. + 31 and queries 32 (w >> 1) .. + 31 of every 64-query chunk. K and V
+// fragments stay in registers; Q and dO chunks are double-buffered in LDS with
+// their per-query LSE offsets and Delta. At the end the two waves of each key
+// half add their partial dK^T / dV^T through LDS.
+// Workgroups run kv-tile ascending (under causal, early tiles see the most
+// query tiles, so the longest work starts first), kv head next, batch last.
+struct Unit {
+    int hh, e, e_end, c, nch, i;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
+    constexpr int KSTEPS = D / 16;
+    constexpr int DBLK = D / 32;
+    constexpr int NW = 4;
+    using G = Geo<D>;
+    extern __shared__ __attribute__((aligned(1024))) char lds[];
+    // LDS: Q stages 0/1, dO stages 0/1 (TILEB each), then per stage 64 LSE offsets + 64 Delta.
+    auto qst = [&](int st) -> char* { return lds + st * G::TILEB; };
+    auto dost = [&](int st) -> char* { return lds + (2 + st) * G::TILEB; };
+    auto lsest = [&](int st) -> float* { return (float*)(lds + 4 * G::TILEB) + 128 * st; };
+    auto dlst = [&](int st) -> float* { return (float*)(lds + 4 * G::TILEB) + 128 * st + 64; };
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int kb = wave & 1, qs = wave >> 1;
+    const int j = (int)(blockIdx.x % a.NK);
+    const int g = (int)((blockIdx.x / a.NK) % a.Hkv);
+    const int b = (int)(blockIdx.x / ((int64_t)a.NK * a.Hkv));
+    const int GRP = a.Hq / a.Hkv;
+    const int key0 = j * 64;
+    const int mykey = key0 + 32 * kb + l32;
+    const int bq = a.block_q;
+
+    const int head_bytes = a.S * G::ROWB;
+    const int64_t khead = ((int64_t)b * a.Hkv + g) * a.S;
+    bf16x8 kf[KSTEPS], vf[KSTEPS];
+    {
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc((const uint16_t*)a.k + khead * D, head_bytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const uint16_t*)a.v + khead * D, head_bytes);
+        const int off = (mykey * D + 8 * hf) * 2;  // past S: zeros
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            kf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 32 * ks, 0, 0));
+            vf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 32 * ks, 0, 0));
+        }
+    }
+
+    // Cursor over units (query head of the group, entry of its kv-tile list, 64-query chunk).
+    int col_base = 0, col_lane = 0, list_end = 0;
+    auto fetch = [&](int base) {
+        col_base = base;
+        const int e = base + lane;
+        col_lane = e < list_end ? kv_entry(a, e) : 0;
+    };
+    auto entry_at = [&](int e) -> int {
+        if (e - col_base >= 64 || e < col_base) fetch(e);
+        return __builtin_amdgcn_readlane(col_lane, e - col_base);
+    };
+    auto setup_entry = [&](Unit& u) {
+        u.i = entry_at(u.e);
+        const int t0 = u.i * bq;
+        const int rows = min(bq, a.S - t0);
+        u.nch = (rows + 63) >> 6;
+        // Under causal, chunk c can see key0 only if its last query t0 + 64 c + 63 >= key0.
+        u.c = (a.causal && key0 > t0 + 63) ? (key0 - t0) / 64 : 0;
+    };
+    // Advance `u` to the first valid unit at or after its current position.
+    auto settle = [&](Unit& u) -> bool {
+        for (;;) {
+            if (u.e < u.e_end) {
+                if (u.c < u.nch) return true;
+                ++u.e;
+                if (u.e < u.e_end) setup_entry(u);
+                continue;
+            }
+            ++u.hh;
+            if (u.hh >= GRP) return false;
+            const int h = g * GRP + u.hh;
+            const int hs = (a.Hsel == 1) ? 0 : h;
+            kv_tile_range(a, b, hs, j, key0, u.e, u.e_end);
+            list_end = u.e_end;
+            fetch(u.e);
+            if (u.e < u.e_end) setup_entry(u);
+        }
+    };
+    Unit cur;
+    cur.hh = -1;
+    cur.e = cur.e_end = 0;
+    cur.c = cur.nch = 0;
+    cur.i = 0;
+    bool have = settle(cur);
+
+    auto issue = [&](const Unit& u, int st) {
+        const int h = g * GRP + u.hh;
+        const int64_t qhead = ((int64_t)b * a.Hq + h) * a.S;
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc((const uint16_t*)a.q + qhead * D, head_bytes);
+        const __amdgpu_buffer_rsrc_t dors = make_rsrc((const uint16_t*)a.dout + qhead * D, head_bytes);
+        const int row0 = u.i * bq + 64 * u.c;
+        dma_tile<D, NW, true>(qrs, qst(st), row0, a.S, wave, lane);
+        dma_tile<D, NW, true>(dors, dost(st), row0, a.S, wave, lane);
+    };
+    // LSE offset / Delta of the unit's 64 queries: thread t < 64 loads LSE of
+    // query t, thread 64 <= t < 128 Delta of query t - 64; stored after the wait.
+    auto side_load = [&](const Unit& u) -> float {
+        const int h = g * GRP + u.hh;
+        const int64_t qhead = ((int64_t)b * a.Hq + h) * a.S;
+        const int t = u.i * bq + 64 * u.c + (tid & 63);
+        const bool ok = t < a.S && (64 * u.c + (tid & 63)) < bq;
+        if (tid < 64) return ok ? lse_offset(a.lse[qhead + t]) : kPosInf;
+        if (tid < 128) return ok ? a.delta[qhead + t] : 0.f;
+        return 0.f;
+    };
+    auto side_store = [&](float x, int st) {
+        if (tid < 64) lsest(st)[tid] = x;
+        else if (tid < 128) dlst(st)[tid - 64] = x;
+    };
+
+    f32x16 dk[DBLK], dv[DBLK];
+#pragma unroll
+    for (int m = 0; m < DBLK; ++m) {
+        dk[m] = (f32x16){};
+        dv[m] = (f32x16){};
+    }
+
+    if (have) {
+        issue(cur, 0);
+        const float sv = side_load(cur);
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        side_store(sv, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+
+    int st = 0;
+    while (have) {
+        Unit nxt = cur;
+        ++nxt.c;
+        const bool have_next = settle(nxt);
+        float sv = 0.f;
+        if (have_next) {
+            issue(nxt, st ^ 1);
+            sv = side_load(nxt);
+        }
+        const char* qt = qst(st);
+        const char* dt = dost(st);
+        // S = Q K^T and dP = dO V^T for this wave's 32 queries x 32 keys.
+        f32x16 s = (f32x16){}, dp = (f32x16){};
+        const int qr = 32 * qs + l32;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            s = mfma(row_frag<D, true>(qt, qr, 2 * ks + hf), kf[ks], s);
+            dp = mfma(row_frag<D, true>(dt, qr, 2 * ks + hf), vf[ks], dp);
+        }
+        // Lane holds key mykey (column) and queries 32 qs + 8 q + 4 hf + e (chunk rows) at [4 q + e].
+        const int tq0 = cur.i * bq + 64 * cur.c + 32 * qs;
+        const bool need_mask = a.causal && (key0 + 32 * kb + 31 > tq0);
+        const float* lsp = lsest(st) + 32 * qs + 4 * hf;
+        const float* dlp = dlst(st) + 32 * qs + 4 * hf;
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 lo = *(const f32x4*)(lsp + 8 * q);
+            const f32x4 de = *(const f32x4*)(dlp + 8 * q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int x = 4 * q + e;
+                float p = fast_exp2(__builtin_fmaf(s[x], a.scale_log2, -lo[e]));
+                if (need_mask) p = (mykey <= tq0 + 8 * q + 4 * hf + e) ? p : 0.f;
+                const float ds = p * (dp[x] - de[e]);
+                pf[x >> 3][x & 7] = (__bf16)p;
+                dsf[x >> 3][x & 7] = (__bf16)ds;
+            }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS; contraction over this wave's queries,
+        // k-step s covering rows 32 qs + 16 s + 4 hf + (0..3) and + 8.
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int m = 0; m < DBLK; ++m) {
+                dv[m] = mfma(tr_frag<D>(dt, 32 * qs + 16 * s2, m, lane), pf[s2], dv[m]);
+                dk[m] = mfma(tr_frag<D>(qt, 32 * qs + 16 * s2, m, lane), dsf[s2], dk[m]);
+            }
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        if (have_next) side_store(sv, st ^ 1);
+        __syncthreads();
+        cur = nxt;
+        have = have_next;
+        st ^= 1;
+    }
+
+    // Add the query-half partials: waves with qs = 1 park theirs in LDS.
+    float* red = (float*)lds;  // [kb][2][DBLK][16][64] floats = 2 * 2 * DBLK * 4 KiB <= 4 * TILEB
+    if (qs == 1) {
+#pragma unroll
+        for (int m = 0; m < DBLK; ++m)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                red[(((kb * 2 + 0) * DBLK + m) * 16 + x) * 64 + lane] = dk[m][x];
+                red[(((kb * 2 + 1) * DBLK + m) * 16 + x) * 64 + lane] = dv[m][x];
+            }
+    }
+    __syncthreads();
+    if (qs == 0 && mykey < a.S) {
+        uint16_t* kp = (uint16_t*)a.dk + (khead + mykey) * D;
+        uint16_t* vp = (uint16_t*)a.dv + (khead + mykey) * D;
+#pragma unroll
+        for (int m = 0; m < DBLK; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                bf16x4 wk, wv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int x = 4 * q + e;
+                    const float k2 = red[(((kb * 2 + 0) * DBLK + m) * 16 + x) * 64 + lane];
+                    const float v2 = red[(((kb * 2 + 1) * DBLK + m) * 16 + x) * 64 + lane];
+                    wk[e] = (__bf16)((dk[m][x] + k2) * a.scale);
+                    wv[e] = (__bf16)(dv[m][x] + v2);
+                }
+                // rows d = 32 m + 8 q + 4 hf + e of column mykey
+                *(bf16x4*)(kp + 32 * m + 8 * q + 4 * hf) = wk;
+                *(bf16x4*)(vp + 32 * m + 8 * q + 4 * hf) = wv;
+            }
+    }
+}
+
+// ============================================================ SIMT fallback
+//
+// Four lanes per row, each holding a quarter of D in fp32.
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void bwd_dq_simt_kernel(AttnBwdArgs a) {
+    constexpr int QD = D / 4;
+    constexpr int KC = 32;
+    __shared__ float Ks[KC][D + 4];
+    __shared__ float Vs[KC][D + 4];
+    const int tid = threadIdx.x;
+    const int64_t total = (int64_t)a.B * a.Hq * a.NQ;
+    const Work wk = decode_q_work(blockIdx.x, total, a.Hq, a.Hkv, a.NQ);
+    const int t0 = wk.i * a.block_q;
+    const int t_end = min(t0 + a.block_q, a.S);
+    const int64_t qhead = ((int64_t)wk.b * a.Hq + wk.h) * a.S;
+    const int64_t khead = ((int64_t)wk.b * a.Hkv + wk.g) * a.S;
+    const int part = tid & 3;
+
+    for (int rc = t0; rc < t_end; rc += 64) {
+        const int row = rc + (tid >> 2);
+        const bool rvalid = row < t_end;
+        const int chunk_last = min(rc + 64, t_end) - 1;
+        float qv[QD], dov[QD], dqv[QD];
+#pragma unroll
+        for (int d = 0; d < QD; ++d) {
+            const int64_t x = (qhead + row) * D + part * QD + d;
+            qv[d] = rvalid ? load_elem(a.q, x, BF16) : 0.f;
+            dov[d] = rvalid ? load_elem(a.dout, x, BF16) : 0.f;
+            dqv[d] = 0.f;
+        }
+        const float lse_l2 = rvalid ? lse_offset(a.lse[qhead + row]) : kPosInf;
+        const float delta = rvalid ? a.delta[qhead + row] : 0.f;
+        int e_begin, e_end;
+        q_tile_range(a, wk.b, wk.h, wk.i, chunk_last, e_begin, e_end);
+        for (int e = e_begin; e < e_end; ++e) {
+            const int jt = a.row_ptr ? a.col_idx[e] : e;
+            const int k0 = jt * a.block_kv;
+            const int k1 = min(k0 + a.block_kv, a.S);
+            for (int kc = k0; kc < k1; kc += KC) {
+                if (a.causal && kc > chunk_last) break;
+                const int nkeys = min(KC, k1 - kc);
+                __syncthreads();
+                for (int x = tid; x < KC * D; x += 256) {
+                    const int kr = x / D, d = x % D;
+                    const bool ok = kr < nkeys;
+                    Ks[kr][d] = ok ? load_elem(a.k, (khead + kc + kr) * D + d, BF16) : 0.f;
+                    Vs[kr][d] = ok ? load_elem(a.v, (khead + kc + kr) * D + d, BF16) : 0.f;
+                }
+                __syncthreads();
+                for (int kr = 0; kr < nkeys; ++kr) {
+                    float sd = 0.f, pd = 0.f;
+#pragma unroll
+                    for (int d = 0; d < QD; ++d) {
+                        sd += qv[d] * Ks[kr][part * QD + d];
+                        pd += dov[d] * Vs[kr][part * QD + d];
+                    }
+                    sd += __shfl_xor(sd, 1);
+                    sd += __shfl_xor(sd, 2);
+                    pd += __shfl_xor(pd, 1);
+                    pd += __shfl_xor(pd, 2);
+                    const int key = kc + kr;
+                    float p = exp2f(sd * a.scale_log2 - lse_l2);
+                    if (a.causal && key > row) p = 0.f;
+                    const float ds = p * (pd - delta);
+#pragma unroll
+                    for (int d = 0; d < QD; ++d) dqv[d] += ds * Ks[kr][part * QD + d];
+                }
+            }
+        }
+        if (rvalid) {
+            const int64_t o = (qhead + row) * D + part * QD;
+#pragma unroll
+            for (int d = 0; d < QD; ++d) {
+                if constexpr (BF16) ((uint16_t*)a.dq)[o + d] = to_bf16_bits(dqv[d] * a.scale);
+                else ((float*)a.dq)[o + d] = dqv[d] * a.scale;
+            }
+        }
+    }
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void bwd_dkdv_simt_kernel(AttnBwdArgs a) {
+    constexpr int QD = D / 4;
+    constexpr int QC = 32;
+    __shared__ float Qs[QC][D + 4];
+    __shared__ float Ds[QC][D + 4];
+    __shared__ float Ls[QC], Dl[QC];
+    const int tid = threadIdx.x;
+    const int j = (int)(blockIdx.x % a.NK);
+    const int g = (int)((blockIdx.x / a.NK) % a.Hkv);
+    const int b = (int)(blockIdx.x / ((int64_t)a.NK * a.Hkv));
+    const int GRP = a.Hq / a.Hkv;
+    const int k0 = j * a.block_kv;
+    const int k_end = min(k0 + a.block_kv, a.S);
+    const int64_t khead = ((int64_t)b * a.Hkv + g) * a.S;
+    const int part = tid & 3;
+
+    for (int kc0 = k0; kc0 < k_end; kc0 += 64) {
+        const int key = kc0 + (tid >> 2);
+        const bool kvalid = key < k_end;
+        float kv_[QD], vv[QD], dkv[QD], dvv[QD];
+#pragma unroll
+        for (int d = 0; d < QD; ++d) {
+            const int64_t x = (khead + key) * D + part * QD + d;
+            kv_[d] = kvalid ? load_elem(a.k, x, BF16) : 0.f;
+            vv[d] = kvalid ? load_elem(a.v, x, BF16) : 0.f;
+            dkv[d] = 0.f;
+            dvv[d] = 0.f;
+        }
+        for (int hh = 0; hh < GRP; ++hh) {
+            const int h = g * GRP + hh;
+            const int hs = (a.Hsel == 1) ? 0 : h;
+            const int64_t qhead = ((int64_t)b * a.Hq + h) * a.S;
+            int e_begin, e_end;
+            kv_tile_range(a, b, hs, j, kc0, e_begin, e_end);
+            for (int e = e_begin; e < e_end; ++e) {
+                const int i = kv_entry(a, e);
+                const int t0 = i * a.block_q;
+                const int t1 = min(t0 + a.block_q, a.S);
+                for (int tc = t0; tc < t1; tc += QC) {
+                    if (a.causal && tc + QC - 1 < kc0) continue;
+                    const int nq = min(QC, t1 - tc);
+                    __syncthreads();
+                    for (int x = tid; x < QC * D; x += 256) {
+                        const int r = x / D, d = x % D;
+                        const bool ok = r < nq;
+                        Qs[r][d] = ok ? load_elem(a.q, (qhead + tc + r) * D + d, BF16) : 0.f;
+                        Ds[r][d] = ok ? load_elem(a.dout, (qhead + tc + r) * D + d, BF16) : 0.f;
+                    }
+                    if (tid < QC) {
+                        const bool ok = tid < nq;
+                        Ls[tid] = ok ? lse_offset(a.lse[qhead + tc + tid]) : kPosInf;
+                        Dl[tid] = ok ? a.delta[qhead + tc + tid] : 0.f;
+                    }
+                    __syncthreads();
+                    for (int r = 0; r < nq; ++r) {
+                        float sd = 0.f, pd = 0.f;
+#pragma unroll
+                        for (int d = 0; d < QD; ++d) {
+                            sd += Qs[r][part * QD + d] * kv_[d];
+                            pd += Ds[r][part * QD + d] * vv[d];
+                        }
+                        sd += __shfl_xor(sd, 1);
+                        sd += __shfl_xor(sd, 2);
+                        pd += __shfl_xor(pd, 1);
+                        pd += __shfl_xor(pd, 2);
+                        float p = exp2f(sd * a.scale_log2 - Ls[r]);
+                        if (a.causal && key > tc + r) p = 0.f;
+                        const float ds = p * (pd - Dl[r]);
+#pragma unroll
+                        for (int d = 0; d < QD; ++d) {
+                            dvv[d] += p * Ds[r][part * QD + d];
+                            dkv[d] += ds * Qs[r][part * QD + d];
+                        }
+                    }
+                }
+            }
+        }
+        if (kvalid) {
+            const int64_t o = (khead + key) * D + part * QD;
+#pragma unroll
+            for (int d = 0; d < QD; ++d) {
+                if constexpr (BF16) {
+                    ((uint16_t*)a.dk)[o + d] = to_bf16_bits(dkv[d] * a.scale);
+                    ((uint16_t*)a.dv)[o + d] = to_bf16_bits(dvv[d]);
+                } else {
+                    ((float*)a.dk)[o + d] = dkv[d] * a.scale;
+                    ((float*)a.dv)[o + d] = dvv[d];
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// ============================================================ launchers
+
+hipError_t launch_bwd_delta(const void* out, const void* dout, int bf16, int64_t rows, int D, float* delta,
+                            hipStream_t stream) {
+    if (rows == 0) return hipSuccess;
+    const int64_t threads = rows * (D / 8);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+#define NSA_DELTA(DD, BB) hipLaunchKernelGGL((delta_kernel<DD, BB>), grid, dim3(256), 0, stream, out, dout, delta, rows)
+    if (D == 128) {
+        if (bf16) NSA_DELTA(128, true);
+        else NSA_DELTA(128, false);
+    } else if (D == 64) {
+        if (bf16) NSA_DELTA(64, true);
+        else NSA_DELTA(64, false);
+    } else {
+        return hipErrorInvalidValue;
+    }
+#undef NSA_DELTA
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_major_index(const int8_t* keep, int BH, int NQ, int NK, int32_t cap, int32_t* counts,
+                                 int32_t* col_ptr, int32_t* row_idx, hipStream_t stream) {
+    const int64_t n = (int64_t)BH * NK;
+    if (n == 0) {
+        hipLaunchKernelGGL(colscan_kernel, dim3(1), dim3(1024), 0, stream, counts, n, cap, col_ptr);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)((int64_t)BH * ((NK + 255) / 256)));
+    hipLaunchKernelGGL(colcount_kernel, grid, dim3(256), 0, stream, keep, NQ, NK, counts);
+    hipLaunchKernelGGL(colscan_kernel, dim3(1), dim3(1024), 0, stream, counts, n, cap, col_ptr);
+    hipLaunchKernelGGL(colfill_kernel, grid, dim3(256), 0, stream, keep, NQ, NK, col_ptr, row_idx);
+    return hipGetLastError();
+}
+
+bool attn_bwd_mfma_supported(const AttnBwdArgs& a, int bf16) {
+    const bool fits = ((int64_t)a.S + 128) * a.D * 2 < ((int64_t)1 << 31);
+    return bf16 && fits && a.block_kv == 64 && a.block_q % 32 == 0 && a.block_q >= 32 && a.block_q <= 128 &&
+           (a.D == 64 || a.D == 128);
+}
+
+size_t attn_bwd_dkdv_lds_bytes(int D) { return 4 * (size_t)(64 * D * 2) + 4 * 64 * sizeof(float); }
+
+hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t stream) {
+    const int64_t qwork = (int64_t)a.B * a.Hq * a.NQ;
+    const int64_t kvwork = (int64_t)a.B * a.Hkv * a.NK;
+    const int nw = a.block_q / 32;
+    if (qwork > 0) {
+#define NSA_DQ(DD, NWW)                                                                                 \
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<DD, NWW>), dim3((unsigned)qwork), dim3(64 * NWW), \
+                       (size_t)(4 * 64 * DD * 2), stream, a)
+        if (a.D == 128) {
+            if (nw == 4) NSA_DQ(128, 4);
+            else if (nw == 3) NSA_DQ(128, 3);
+            else if (nw == 2) NSA_DQ(128, 2);
+            else NSA_DQ(128, 1);
+        } else {
+            if (nw == 4) NSA_DQ(64, 4);
+            else if (nw == 3) NSA_DQ(64, 3);
+            else if (nw == 2) NSA_DQ(64, 2);
+            else NSA_DQ(64, 1);
+        }
+#undef NSA_DQ
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    if (kvwork > 0) {
+        if (a.D == 128)
+            hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<128>), dim3((unsigned)kvwork), dim3(256),
+                               attn_bwd_dkdv_lds_bytes(128), stream, a);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<64>), dim3((unsigned)kvwork), dim3(256),
+                               attn_bwd_dkdv_lds_bytes(64), stream, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_simt(const AttnBwdArgs& a, int bf16, hipStream_t stream) {
+    const int64_t qwork = (int64_t)a.B * a.Hq * a.NQ;
+    const int64_t kvwork = (int64_t)a.B * a.Hkv * a.NK;
+#define NSA_BSIMT(DD, BB)                                                                                    \
+    do {                                                                                                     \
+        if (qwork > 0)                                                                                       \
+            hipLaunchKernelGGL((bwd_dq_simt_kernel<DD, BB>), dim3((unsigned)qwork), dim3(256), 0, stream, a); \
+        if (kvwork > 0)                                                                                      \
+            hipLaunchKernelGGL((bwd_dkdv_simt_kernel<DD, BB>), dim3((unsigned)kvwork), dim3(256), 0, stream, \
+                               a);                                                                           \
+    } while (0)
+    if (a.D == 64) {
+        if (bf16) NSA_BSIMT(64, true);
+        else NSA_BSIMT(64, false);
+    } else if (a.D == 128) {
+        if (bf16) NSA_BSIMT(128, true);
+        else NSA_BSIMT(128, false);
+    } else {
+        return hipErrorInvalidValue;
+    }
+#undef NSA_BSIMT
+    return hipGetLastError();
+}
+
+}  // namespace nsa

@@ -541,11 +541,13 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream) {
     } while (0)
     if (a.D == 128) {
         if (nw == 4) NSA_ATTN(128, 4);
+        else if (nw == 3) NSA_ATTN(128, 3);
         else if (nw == 2) NSA_ATTN(128, 2);
         else if (nw == 1) NSA_ATTN(128, 1);
         else return hipErrorInvalidValue;
     } else if (a.D == 64) {
         if (nw == 4) NSA_ATTN(64, 4);
+        else if (nw == 3) NSA_ATTN(64, 3);
         else if (nw == 2) NSA_ATTN(64, 2);
         else if (nw == 1) NSA_ATTN(64, 1);
         else return hipErrorInvalidValue;

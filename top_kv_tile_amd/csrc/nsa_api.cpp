@@ -323,6 +323,82 @@ int run_pool(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, con
     return NSA_OK;
 }
 
+
+// ---- attention gradients -----------------------------------------------------
+
+// Selection geometry shared by the forward and the gradients; fills the CSR
+// pointers, selection heads and block sizes of a launch (dense when sel is null).
+int attn_selection(const nsa_tensor* q, const nsa_tensor* k, const nsa_selection* sel, int& Hsel, int& bq,
+                   int& bkv) {
+    if (!sel) {
+        Hsel = q->H;
+        bq = 128;
+        bkv = 64;
+        return NSA_OK;
+    }
+    if (!sel->row_ptr) return NSA_ERR_NULL_ARG;
+    if (sel->nnz > 0 && !sel->col_idx) return NSA_ERR_NULL_ARG;
+    if (sel->nnz < 0 || sel->nnz >= ((int64_t)1 << 31)) return NSA_ERR_BAD_SHAPE;
+    if (sel->block_q <= 0 || sel->block_kv <= 0) return NSA_ERR_BAD_SPEC;
+    if (sel->B != q->B || (sel->H != 1 && sel->H != q->H)) return NSA_ERR_BAD_SHAPE;
+    if (sel->seq_q != q->S || sel->seq_kv != k->S) return NSA_ERR_BAD_SHAPE;
+    if (sel->NQ != ceil_div(q->S, sel->block_q) || sel->NK != ceil_div(k->S, sel->block_kv))
+        return NSA_ERR_BAD_SHAPE;
+    Hsel = sel->H;
+    bq = sel->block_q;
+    bkv = sel->block_kv;
+    return NSA_OK;
+}
+
+// Gradient workspace: Delta (B*Hq*S fp32), then for a sparse selection the
+// per-column counts (B*H'*NK), col_ptr (B*H'*NK + 1) and row_idx (nnz) int32.
+struct BwdLayout {
+    size_t delta = 0, counts = 0, col_ptr = 0, row_idx = 0, total = 0;
+};
+BwdLayout bwd_layout(const nsa_tensor* q, const nsa_selection* sel) {
+    BwdLayout w;
+    size_t off = 0;
+    w.delta = off;
+    off += align256((size_t)numel(q) / (size_t)std::max(1, q->D) * sizeof(float));
+    if (sel) {
+        const size_t cols = (size_t)sel->B * sel->H * sel->NK;
+        w.counts = off;
+        off += align256(cols * sizeof(int32_t));
+        w.col_ptr = off;
+        off += align256((cols + 1) * sizeof(int32_t));
+        w.row_idx = off;
+        off += align256((size_t)std::max<int64_t>(sel->nnz, 0) * sizeof(int32_t));
+    }
+    w.total = off;
+    return w;
+}
+
+int validate_bwd(const nsa_tensor* q, const nsa_tensor* k, const nsa_tensor* v, const nsa_tensor* out,
+                 const float* lse, const nsa_tensor* dout, const nsa_selection* sel, int causal,
+                 const nsa_tensor* dq, const nsa_tensor* dk, const nsa_tensor* dv) {
+    const nsa_tensor* all[8] = {q, k, v, out, dout, dq, dk, dv};
+    for (const nsa_tensor* t : all) {
+        const int st = check_tensor(t);
+        if (st != NSA_OK) return st;
+    }
+    for (const nsa_tensor* t : all)
+        if (t->dtype != q->dtype) return NSA_ERR_BAD_DTYPE;
+    auto same = [](const nsa_tensor* x, const nsa_tensor* y) {
+        return x->B == y->B && x->H == y->H && x->S == y->S && x->D == y->D;
+    };
+    if (!same(out, q) || !same(dout, q) || !same(dq, q)) return NSA_ERR_BAD_SHAPE;
+    if (!same(v, k) || !same(dk, k) || !same(dv, k)) return NSA_ERR_BAD_SHAPE;
+    if (q->B != k->B || q->D != k->D || q->H % k->H != 0) return NSA_ERR_BAD_SHAPE;
+    if (numel(q) > 0 && !lse) return NSA_ERR_NULL_ARG;
+    if (causal && q->S != k->S) return NSA_ERR_UNSUPPORTED;
+    if (q->D != 64 && q->D != 128) return NSA_ERR_UNSUPPORTED;
+    if (q->S != k->S) return NSA_ERR_UNSUPPORTED;
+    int Hsel, bq, bkv;
+    const int st = attn_selection(q, k, sel, Hsel, bq, bkv);
+    if (st != NSA_OK) return st;
+    if (sel && (int64_t)sel->B * sel->H * sel->NQ * sel->NK > 0 && !sel->keep) return NSA_ERR_NULL_ARG;
+    return NSA_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -549,6 +625,77 @@ int nsa_block_sparse_attn(const nsa_tensor* q, const nsa_tensor* k, const nsa_te
     const int bf16 = q->dtype == NSA_BF16;
     hipError_t e = nsa::attn_mfma_supported(a, bf16) ? nsa::launch_attn_mfma(a, stream)
                                                        : nsa::launch_attn_simt(a, bf16, stream);
+    return e == hipSuccess ? NSA_OK : hip_fail(e);
+}
+
+
+int nsa_attn_bwd_workspace_size(const nsa_tensor* q, const nsa_tensor* k, const nsa_selection* sel,
+                                int64_t* bytes) {
+    int st;
+    if (!bytes) return NSA_ERR_NULL_ARG;
+    if ((st = check_tensor(q)) != NSA_OK) return st;
+    if ((st = check_tensor(k)) != NSA_OK) return st;
+    int Hsel, bq, bkv;
+    if ((st = attn_selection(q, k, sel, Hsel, bq, bkv)) != NSA_OK) return st;
+    *bytes = (int64_t)bwd_layout(q, sel).total;
+    return NSA_OK;
+}
+
+int nsa_block_sparse_attn_bwd(const nsa_tensor* q, const nsa_tensor* k, const nsa_tensor* v,
+                              const nsa_tensor* out, const float* lse, const nsa_tensor* dout,
+                              const nsa_selection* sel, int causal, nsa_tensor* dq, nsa_tensor* dk,
+                              nsa_tensor* dv, void* workspace, size_t workspace_bytes, void* stream_) {
+    hipStream_t stream = (hipStream_t)stream_;
+    int st = validate_bwd(q, k, v, out, lse, dout, sel, causal, dq, dk, dv);
+    if (st != NSA_OK) return st;
+    const BwdLayout w = bwd_layout(q, sel);
+    if (workspace_bytes < w.total || (w.total > 0 && !workspace)) return NSA_ERR_WORKSPACE;
+    if (numel(q) == 0) return NSA_OK;  // S == 0 or B == 0: every output is empty
+
+    nsa::AttnBwdArgs a;
+    a.q = q->data;
+    a.k = k->data;
+    a.v = v->data;
+    a.lse = lse;
+    a.dout = dout->data;
+    a.dq = dq->data;
+    a.dk = dk->data;
+    a.dv = dv->data;
+    char* ws = (char*)workspace;
+    float* delta = (float*)(ws + w.delta);
+    a.delta = delta;
+    a.B = q->B;
+    a.Hq = q->H;
+    a.Hkv = k->H;
+    a.S = q->S;
+    a.D = q->D;
+    a.causal = causal ? 1 : 0;
+    a.scale = (float)(1.0 / std::sqrt((double)q->D));
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)q->D));
+    attn_selection(q, k, sel, a.Hsel, a.block_q, a.block_kv);
+    a.NQ = (int)ceil_div(q->S, a.block_q);
+    a.NK = (int)ceil_div(k->S, a.block_kv);
+    const int bf16 = q->dtype == NSA_BF16;
+
+    hipError_t e = nsa::launch_bwd_delta(out->data, dout->data, bf16, (int64_t)q->B * q->H * q->S, q->D, delta,
+                                         stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (sel) {
+        int32_t* counts = (int32_t*)(ws + w.counts);
+        int32_t* col_ptr = (int32_t*)(ws + w.col_ptr);
+        int32_t* row_idx = (int32_t*)(ws + w.row_idx);
+        e = nsa::launch_kv_major_index(sel->keep, sel->B * sel->H, sel->NQ, sel->NK, (int32_t)std::max<int64_t>(sel->nnz, 0),
+                                       counts, col_ptr, row_idx, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        a.row_ptr = sel->row_ptr;
+        a.col_idx = sel->col_idx;
+        a.col_ptr = col_ptr;
+        a.row_idx = row_idx;
+    } else {
+        a.row_ptr = a.col_idx = a.col_ptr = a.row_idx = nullptr;
+    }
+    e = nsa::attn_bwd_mfma_supported(a, bf16) ? nsa::launch_attn_bwd_mfma(a, stream)
+                                               : nsa::launch_attn_bwd_simt(a, bf16, stream);
     return e == hipSuccess ? NSA_OK : hip_fail(e);
 }
 

@@ -59,4 +59,38 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream);
 // General path (fp32 or bf16 inputs, any block sizes, D in {64, 128}).
 hipError_t launch_attn_simt(const AttnArgs& a, int bf16, hipStream_t stream);
 
+// ---- attention gradients ---------------------------------------------------
+
+struct AttnBwdArgs {
+    const void* q;            // (B, Hq, S, D)
+    const void* k;            // (B, Hkv, S, D)
+    const void* v;
+    const float* lse;         // (B, Hq, S), natural log
+    const void* dout;         // (B, Hq, S, D)
+    const float* delta;       // (B, Hq, S): dO . O
+    void* dq;                 // (B, Hq, S, D)
+    void* dk;                 // (B, Hkv, S, D)
+    void* dv;
+    const int32_t* row_ptr;   // query-major CSR; null = dense
+    const int32_t* col_idx;
+    const int32_t* col_ptr;   // kv-tile-major index: (B*Hsel*NK + 1); null = dense
+    const int32_t* row_idx;   // query tiles per (b, h', j), ascending
+    int B, Hq, Hkv, Hsel, S, D, NQ, NK, block_q, block_kv;
+    int causal;
+    float scale;              // D^-1/2
+    float scale_log2;         // D^-1/2 * log2(e)
+};
+// delta[r] = dout[r] . out[r] over D for `rows` rows (D in {64, 128}).
+hipError_t launch_bwd_delta(const void* out, const void* dout, int bf16, int64_t rows, int D, float* delta,
+                            hipStream_t stream);
+// kv-tile-major index of keep (BH slabs of NQ x NK int8): counts (BH*NK),
+// col_ptr (BH*NK + 1), row_idx (cap entries; offsets are clamped to cap).
+hipError_t launch_kv_major_index(const int8_t* keep, int BH, int NQ, int NK, int32_t cap, int32_t* counts,
+                                 int32_t* col_ptr, int32_t* row_idx, hipStream_t stream);
+// bf16 MFMA path: block_q in {32, 64, 96, 128}, block_kv == 64, D in {64, 128}.
+bool attn_bwd_mfma_supported(const AttnBwdArgs& a, int bf16);
+hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t stream);
+// General path (fp32 or bf16, any block sizes, D in {64, 128}).
+hipError_t launch_attn_bwd_simt(const AttnBwdArgs& a, int bf16, hipStream_t stream);
+
 }  // namespace nsa

@@ -20,13 +20,14 @@ import torch
 
 __all__ = [
     "SparseSpec", "Selection", "Sizes", "NsaError", "lib", "nsa_select_sizes", "nsa_select",
-    "nsa_block_sparse_attn", "nsa_pool_blocks", "nsa_score_blocks", "nsa_status_string",
-    "LIB_PATH", "EXPORTS",
+    "nsa_block_sparse_attn", "nsa_block_sparse_attn_bwd", "nsa_attn_bwd_workspace_size",
+    "nsa_pool_blocks", "nsa_score_blocks", "nsa_status_string", "LIB_PATH", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnsa.so")
-EXPORTS = ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_pool_blocks",
-           "nsa_score_blocks", "nsa_status_string", "nsa_last_hip_error", "nsa_version")
+EXPORTS = ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_attn_bwd_workspace_size",
+           "nsa_block_sparse_attn_bwd", "nsa_pool_blocks", "nsa_score_blocks", "nsa_status_string",
+           "nsa_last_hip_error", "nsa_version")
 
 NSA_OK, NSA_DENSE = 0, 1
 NSA_F32, NSA_BF16 = 0, 1
@@ -85,14 +86,18 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.nsa_block_sparse_attn.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Selection), ctypes.c_int,
                                             P(_Tensor), ctypes.c_void_p, ctypes.c_void_p]
+        L.nsa_attn_bwd_workspace_size.argtypes = [P(_Tensor), P(_Tensor), P(_Selection), P(ctypes.c_int64)]
+        L.nsa_block_sparse_attn_bwd.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), P(_Tensor), ctypes.c_void_p,
+                                                P(_Tensor), P(_Selection), ctypes.c_int, P(_Tensor), P(_Tensor),
+                                                P(_Tensor), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.nsa_pool_blocks.argtypes = [P(_Tensor), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
         L.nsa_score_blocks.argtypes = [P(_Tensor), P(_Tensor), P(_Spec), ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_size_t, ctypes.c_void_p]
         L.nsa_status_string.argtypes = [ctypes.c_int]
         L.nsa_status_string.restype = ctypes.c_char_p
         L.nsa_version.restype = ctypes.c_char_p
-        for name in ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_pool_blocks",
-                     "nsa_score_blocks", "nsa_last_hip_error"):
+        for name in ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_attn_bwd_workspace_size",
+                     "nsa_block_sparse_attn_bwd", "nsa_pool_blocks", "nsa_score_blocks", "nsa_last_hip_error"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -248,6 +253,38 @@ def nsa_block_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel
                                        _stream(stream)),
            "nsa_block_sparse_attn")
     return out, lse
+
+
+def nsa_attn_bwd_workspace_size(q: torch.Tensor, k: torch.Tensor, selection: Selection | None) -> int:
+    """Device workspace bytes nsa_block_sparse_attn_bwd needs."""
+    n = ctypes.c_int64(0)
+    csel = ctypes.byref(selection._c()) if selection is not None else None
+    _check(lib().nsa_attn_bwd_workspace_size(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)), csel,
+                                             ctypes.byref(n)), "nsa_attn_bwd_workspace_size")
+    return int(n.value)
+
+
+def nsa_block_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                              lse: torch.Tensor, dout: torch.Tensor, selection: Selection | None, causal: bool,
+                              stream=None, workspace: torch.Tensor | None = None, dq=None, dk=None, dv=None):
+    """Gradients of nsa_block_sparse_attn; returns (dq, dk, dv) in q's dtype."""
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must be contiguous fp32 (B, Hq, S)")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = nsa_attn_bwd_workspace_size(q, k, selection)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    csel = ctypes.byref(selection._c()) if selection is not None else None
+    _check(lib().nsa_block_sparse_attn_bwd(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)),
+                                           ctypes.byref(_tensor(v)), ctypes.byref(_tensor(out)),
+                                           ctypes.c_void_p(lse.data_ptr()), ctypes.byref(_tensor(dout)), csel,
+                                           int(bool(causal)), ctypes.byref(_tensor(dq)), ctypes.byref(_tensor(dk)),
+                                           ctypes.byref(_tensor(dv)), ctypes.c_void_p(workspace.data_ptr()),
+                                           workspace.numel() * workspace.element_size(), _stream(stream)),
+           "nsa_block_sparse_attn_bwd")
+    return dq, dk, dv
 
 
 def nsa_pool_blocks(x: torch.Tensor, block: int, stream=None) -> torch.Tensor:

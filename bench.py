@@ -138,12 +138,50 @@ def cpu_baseline(inp, w: synth.Workload, budget_s: float = 20.0):
     }
 
 
+def backward_timing(q, k, v, out, lse, sel, w: synth.Workload, fwd_flops: float, steps: int):
+    """Times nsa_block_sparse_attn_bwd on the step's selection, outside the step.
+
+    Kept-tile FLOPs of the gradients are 2.5x the forward's (five products per
+    tile: S, dP, dQ, dK, dV against the forward's two); the kernels compute S and
+    dP twice (once per kernel), 3.5x in all, which is not counted."""
+    dev = q.device
+    g = torch.Generator(device=dev).manual_seed(2024)
+    dout = torch.randn(q.shape, generator=g, device=dev, dtype=torch.float32).to(q.dtype)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(1, tkt.nsa_attn_bwd_workspace_size(q, k, sel)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        tkt.nsa_block_sparse_attn_bwd(q, k, v, out, lse, dout, sel, w.causal, workspace=ws, dq=dq, dk=dk, dv=dv)
+
+    log("[bench] backward warmup")
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    log(f"[bench] backward timing {steps} calls")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e in ev:
+        e[0].record(stream)
+        call()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = 2.5 * fwd_flops
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 3), "kept_tile_flops_per_call": flops, "TFLOPs": round(tflops, 2),
+            "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "kernels": "delta, kv-major index (3), bwd_dq_mfma_kernel<128,4>, bwd_dkdv_mfma_kernel<128>"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the separate timing of the attention gradients")
+    ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel 3 times "
@@ -252,6 +290,8 @@ def main():
                    "select_algorithmic_bytes": select_bytes, "attn_ms": round(attn_ms, 4),
                    "attn_TFLOPs": round(attn_tflops, 2)},
     }
+    if not args.no_backward:
+        res["backward"] = backward_timing(q, k, v, out, lse, sel, w, full_flops, args.backward_steps)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample)")
         res["cpu_baseline"] = cpu_baseline(inp, w)

@@ -105,6 +105,10 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, do: to
         for b, g, j in want:
             for h in range(g * group, (g + 1) * group):
                 for i in range(nq):
+                    # under causal, a query tile that ends before the kv tile starts
+                    # adds exactly zero to it and is not evaluated
+                    if causal and j * block_kv > min((i + 1) * block_q, seq_q) - 1:
+                        continue
                     if keep[b if keep.shape[0] == bsz else 0, h if sel_heads == hq else 0, i, j]:
                         work.add((b, h, i))
         work = sorted(work)

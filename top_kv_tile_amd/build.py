@@ -16,7 +16,10 @@ LIB = os.path.join(HERE, "libnsa.so")
 SOURCES = ["nsa_api.cpp", "select_kernels.hip", "attn_kernels.hip", "attn_bwd_kernels.hip"]
 
 # Packed fp32 instructions are kept out of the device code: hipcc -O3 would
-# otherwise form them from plain float code.
+# otherwise form them from plain float code. Matrix-core accumulators are
+# allocated as ordinary VGPRs (gfx950 MFMAs take them there): with the default
+# AGPR form the register allocator shuttled live dK/dV accumulators between
+# AGPRs and VGPRs on every iteration of the gradient kernel.
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
@@ -24,6 +27,7 @@ FLAGS = [
     "-fPIC",
     "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-ffp-contract=fast",
     "-Wno-unused-command-line-argument",
 ]

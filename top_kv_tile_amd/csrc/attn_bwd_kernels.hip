@@ -45,12 +45,20 @@ constexpr float kPosInf = __builtin_huge_valf();
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters at their maximum
+// s_waitcnt immediate for vmcnt(n), n < 64 (gfx9 encoding: low 4 bits, high 2 bits at 14).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
 }
+
+// Uniform load through the constant address space: a scalar load (counted by
+// lgkmcnt) when the index is wave-uniform. Only for data no kernel of the
+// launch writes.
+typedef const __attribute__((address_space(4))) int32_t cint32;
+__device__ __forceinline__ int ld_scalar(const int32_t* p, int64_t i) { return ((cint32*)p)[i]; }
 
 // LSE in log2 units as the exponent offset of P; an empty row (LSE = -inf)
 // maps to +inf so that every P of that row is exactly 0.
@@ -173,13 +181,13 @@ __device__ __forceinline__ void kv_tile_range(const AttnBwdArgs& a, int b, int h
                                               int& end) {
     if (a.col_ptr) {
         const int64_t c = ((int64_t)b * a.Hsel + hs) * a.NK + j;
-        start = a.col_ptr[c];
-        end = a.col_ptr[c + 1];
+        start = ld_scalar(a.col_ptr, c);
+        end = ld_scalar(a.col_ptr, c + 1);
         if (a.causal) {
             int lo = start, hi = end;  // first entry whose tile ends at or after key0
             while (lo < hi) {
                 const int mid = (lo + hi) >> 1;
-                if ((int64_t)a.row_idx[mid] * a.block_q + a.block_q - 1 >= key0) hi = mid;
+                if ((int64_t)ld_scalar(a.row_idx, mid) * a.block_q + a.block_q - 1 >= key0) hi = mid;
                 else lo = mid + 1;
             }
             start = lo;
@@ -189,23 +197,24 @@ __device__ __forceinline__ void kv_tile_range(const AttnBwdArgs& a, int b, int h
         end = a.NQ;
     }
 }
-__device__ __forceinline__ int kv_entry(const AttnBwdArgs& a, int e) { return a.row_idx ? a.row_idx[e] : e; }
+__device__ __forceinline__ int kv_entry(const AttnBwdArgs& a, int e) { return a.row_idx ? ld_scalar(a.row_idx, e) : e; }
 
 // ============================================================ MFMA geometry
 //
 // A 64-row tile of D bf16 per row, row-major in LDS, filled by buffer-to-LDS
 // DMA (1 KiB per wave instruction). Rows are XOR-swizzled in 16-byte chunks.
-// Tiles read only as rows (16 bytes per lane, 16 consecutive rows per pass)
-// use rswz = (row / RPB) % CH. Tiles read both as rows and transposed
-// (ds_read_b64_tr_b16: 4 consecutive rows x 4 columns of 8 bytes per 16
-// lanes) use bswz, a one-bit rotation of the same index: consecutive rows map
-// to distinct chunks (row reads), and the four rows of a transposed read land
-// in distinct chunk pairs (transposed reads). Both are bank-conflict free.
+// Tiles read only as rows (16 bytes per lane, 32 consecutive rows per
+// instruction) use rswz = x = (row / RPB) % CH. Tiles read both as rows and
+// transposed (ds_read_b64_tr_b16: 4 consecutive rows x 4 columns of 8 bytes
+// per 16 lanes) use bswz = x ^ 4 (x % 4) (x % 2 at D = 64): the row-read
+// swizzle combined with the one that makes transposed reads conflict-free.
+// Measured with SQ_LDS_BANK_CONFLICT on gfx950 at D = 128: x alone costs ~6
+// conflict cycles per transposed read, 4 (x % 4) alone ~6 per row read, and
+// x ^ 4 (x % 4) none for either.
 template <int D>
 struct Geo {
     static constexpr int ROWB = D * 2;
     static constexpr int CH = ROWB / 16;
-    static constexpr int CHB = CH == 16 ? 4 : 3;  // log2(CH)
     static constexpr int RPB = 256 / ROWB;
     static constexpr int TILEB = 64 * ROWB;
     static constexpr int RPI = 1024 / ROWB;
@@ -213,7 +222,7 @@ struct Geo {
     __device__ static int rswz(int row) { return (row / RPB) % CH; }
     __device__ static int bswz(int row) {
         const int x = (row / RPB) % CH;
-        return ((x << 1) | (x >> (CHB - 1))) & (CH - 1);
+        return x ^ ((4 * (x % 4)) % CH);
     }
 };
 
@@ -268,6 +277,60 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* tile, int r0, int m, int l
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- explicitly scheduled loads
+//
+// The compiler cannot tell which LDS stage a buffer-to-LDS DMA writes, so after
+// a DMA issued through the builtin it waits for every outstanding load before
+// the next transposing LDS read, and __syncthreads() also waits for all loads.
+// Kernels that keep several units in flight therefore issue their DMA with the
+// instruction itself (it has no register result, so nothing the compiler
+// tracks is left in flight), read their indices with scalar loads (counted by
+// lgkmcnt, not vmcnt), wait with explicit vmcnt counts and synchronise with a
+// bare s_barrier. Such a kernel issues no DMA through the builtin: the
+// compiler assumes it owns M0.
+// Raw buffer resource words (no stride, no swizzle; loads past `bytes` return zeros).
+__device__ __forceinline__ u32x4 rsrc_words(const void* p, uint32_t bytes) {
+    const uint64_t x = (uint64_t)p;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32) & 0xFFFFu);
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+// 16 bytes per lane from voff to LDS address lds + 16 * lane.
+__device__ __forceinline__ void dma16(u32x4 rs, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rs) : "memory");
+}
+// 4 bytes per lane from voff to LDS address lds + 4 * lane.
+__device__ __forceinline__ void dma4(u32x4 rs, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rs) : "memory");
+}
+// Workgroup barrier without the memory fence of __syncthreads(); LDS ordering
+// is the caller's (lgkmcnt / vmcnt waits before it).
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// DMA of one 64-row tile (rows row0 .. row0 + 63 of a head, clamped to S - 1)
+// into LDS byte address dst, by the NW waves of the workgroup (bswz layout).
+template <int D, int NW>
+__device__ __forceinline__ void dma_tile_asm(u32x4 rs, uint32_t dst, int row0, int S, int wave, int lane) {
+    using G = Geo<D>;
+    static_assert(G::NINSTR % NW == 0, "every wave issues the same number of DMA instructions");
+#pragma unroll
+    for (int x = 0; x < G::NINSTR / NW; ++x) {
+        const int ii = wave + NW * x;
+        const int row = ii * G::RPI + lane / G::CH, pc = lane % G::CH;
+        const int chunk = pc ^ G::bswz(row);
+        dma16(rs, dst + ii * 1024, min(row0 + row, S - 1) * G::ROWB + chunk * 16);
+    }
 }
 
 // ============================================================ dQ (MFMA)
@@ -438,14 +501,28 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_mfma_kernel(AttnBwdArgs a) 
 // ============================================================ dK / dV (MFMA)
 //
 // Workgroup = 4 waves on one kv tile of 64 keys; wave w owns keys 32 (w & 1)
-// .. + 31 and queries 32 (w >> 1) .. + 31 of every 64-query chunk. K and V
-// fragments stay in registers; Q and dO chunks are double-buffered in LDS with
-// their per-query LSE offsets and Delta. At the end the two waves of each key
-// half add their partial dK^T / dV^T through LDS.
-// Workgroups run kv-tile ascending (under causal, early tiles see the most
-// query tiles, so the longest work starts first), kv head next, batch last.
+// .. + 31 and queries 32 (w >> 1) .. + 31 of every 64-query chunk ("unit").
+// K and V fragments stay in registers. Units are walked head by head over the
+// group, each head's query tiles ascending, and streamed through three LDS
+// stages (Q chunk, dO chunk, and per wave the LSE and Delta of its 32 queries,
+// all by buffer-to-LDS DMA): unit n + 2 is in flight while unit n is computed,
+// and every wave issues the same number of loads per unit, so a partial vmcnt
+// wait tells unit n has landed. At the end the two waves of each key half add
+// their partial dK^T / dV^T through LDS.
+// Workgroups run kv-tile major (tile 0 of every kv head first): under causal,
+// early tiles are seen by the most query tiles, and a pinned tile (a sink) by
+// every one of them, so the longest work starts first.
 struct Unit {
     int hh, e, e_end, c, nch, i;
+};
+
+template <int D>
+struct DkdvLds {
+    static constexpr int TILEB = 64 * D * 2;
+    static constexpr int NST = 3;
+    static constexpr int SIDE = 4 * 2 * 64 * 4;        // per stage: 4 waves x (LSE, Delta) x 64 floats
+    static constexpr int BYTES = NST * 2 * TILEB + NST * SIDE;
+    static_assert(2 * 2 * (D / 32) * 16 * 64 * 4 <= NST * 2 * TILEB, "reduction buffer fits the stages");
 };
 
 template <int D>
@@ -454,19 +531,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
     constexpr int DBLK = D / 32;
     constexpr int NW = 4;
     using G = Geo<D>;
+    using L = DkdvLds<D>;
+    constexpr int PER_UNIT = 2 * (G::NINSTR / NW) + 2;  // vector memory instructions per wave per unit
     extern __shared__ __attribute__((aligned(1024))) char lds[];
-    // LDS: Q stages 0/1, dO stages 0/1 (TILEB each), then per stage 64 LSE offsets + 64 Delta.
     auto qst = [&](int st) -> char* { return lds + st * G::TILEB; };
-    auto dost = [&](int st) -> char* { return lds + (2 + st) * G::TILEB; };
-    auto lsest = [&](int st) -> float* { return (float*)(lds + 4 * G::TILEB) + 128 * st; };
-    auto dlst = [&](int st) -> float* { return (float*)(lds + 4 * G::TILEB) + 128 * st + 64; };
+    auto dost = [&](int st) -> char* { return lds + (L::NST + st) * G::TILEB; };
+    auto side = [&](int st, int w, int which) -> float* {
+        return (float*)(lds + 2 * L::NST * G::TILEB + st * L::SIDE) + (w * 2 + which) * 64;
+    };
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds);
+    auto lds_off = [&](const void* p) -> uint32_t { return lds0 + (uint32_t)((const char*)p - lds); };
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hf = lane >> 5;
     const int kb = wave & 1, qs = wave >> 1;
-    const int j = (int)(blockIdx.x % a.NK);
-    const int g = (int)((blockIdx.x / a.NK) % a.Hkv);
-    const int b = (int)(blockIdx.x / ((int64_t)a.NK * a.Hkv));
+    const int64_t BH = (int64_t)a.B * a.Hkv;
+    const int j = (int)(blockIdx.x / BH);
+    const int g = (int)(blockIdx.x % BH % a.Hkv);
+    const int b = (int)(blockIdx.x % BH / a.Hkv);
     const int GRP = a.Hq / a.Hkv;
     const int key0 = j * 64;
     const int mykey = key0 + 32 * kb + l32;
@@ -484,28 +567,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
             kf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 32 * ks, 0, 0));
             vf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 32 * ks, 0, 0));
         }
+        // Settle these before any DMA: from here on every vmcnt wait is explicit.
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
     }
 
-    // Cursor over units (query head of the group, entry of its kv-tile list, 64-query chunk).
-    int col_base = 0, col_lane = 0, list_end = 0;
-    auto fetch = [&](int base) {
-        col_base = base;
-        const int e = base + lane;
-        col_lane = e < list_end ? kv_entry(a, e) : 0;
-    };
-    auto entry_at = [&](int e) -> int {
-        if (e - col_base >= 64 || e < col_base) fetch(e);
-        return __builtin_amdgcn_readlane(col_lane, e - col_base);
-    };
+    // Cursor over units (query head of the group, entry of its kv-tile list,
+    // 64-query chunk); indices come from scalar loads.
     auto setup_entry = [&](Unit& u) {
-        u.i = entry_at(u.e);
+        u.i = kv_entry(a, u.e);
         const int t0 = u.i * bq;
         const int rows = min(bq, a.S - t0);
         u.nch = (rows + 63) >> 6;
         // Under causal, chunk c can see key0 only if its last query t0 + 64 c + 63 >= key0.
         u.c = (a.causal && key0 > t0 + 63) ? (key0 - t0) / 64 : 0;
     };
-    // Advance `u` to the first valid unit at or after its current position.
+    // Moves `u` to the first unit at or after its position; false when none is left.
     auto settle = [&](Unit& u) -> bool {
         for (;;) {
             if (u.e < u.e_end) {
@@ -519,41 +595,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
             const int h = g * GRP + u.hh;
             const int hs = (a.Hsel == 1) ? 0 : h;
             kv_tile_range(a, b, hs, j, key0, u.e, u.e_end);
-            list_end = u.e_end;
-            fetch(u.e);
             if (u.e < u.e_end) setup_entry(u);
         }
     };
-    Unit cur;
-    cur.hh = -1;
-    cur.e = cur.e_end = 0;
-    cur.c = cur.nch = 0;
-    cur.i = 0;
-    bool have = settle(cur);
+    auto advance = [&](Unit u, bool& ok) -> Unit {
+        ++u.c;
+        ok = settle(u);
+        return u;
+    };
 
+    // Loads of unit u into stage st: Q and dO chunks (rows clamped to S - 1),
+    // and for this wave's 32 queries the raw LSE and Delta (zeros past S).
+    // Every lane of every wave takes part, so each wave issues PER_UNIT loads.
     auto issue = [&](const Unit& u, int st) {
         const int h = g * GRP + u.hh;
         const int64_t qhead = ((int64_t)b * a.Hq + h) * a.S;
-        const __amdgpu_buffer_rsrc_t qrs = make_rsrc((const uint16_t*)a.q + qhead * D, head_bytes);
-        const __amdgpu_buffer_rsrc_t dors = make_rsrc((const uint16_t*)a.dout + qhead * D, head_bytes);
         const int row0 = u.i * bq + 64 * u.c;
-        dma_tile<D, NW, true>(qrs, qst(st), row0, a.S, wave, lane);
-        dma_tile<D, NW, true>(dors, dost(st), row0, a.S, wave, lane);
-    };
-    // LSE offset / Delta of the unit's 64 queries: thread t < 64 loads LSE of
-    // query t, thread 64 <= t < 128 Delta of query t - 64; stored after the wait.
-    auto side_load = [&](const Unit& u) -> float {
-        const int h = g * GRP + u.hh;
-        const int64_t qhead = ((int64_t)b * a.Hq + h) * a.S;
-        const int t = u.i * bq + 64 * u.c + (tid & 63);
-        const bool ok = t < a.S && (64 * u.c + (tid & 63)) < bq;
-        if (tid < 64) return ok ? lse_offset(a.lse[qhead + t]) : kPosInf;
-        if (tid < 128) return ok ? a.delta[qhead + t] : 0.f;
-        return 0.f;
-    };
-    auto side_store = [&](float x, int st) {
-        if (tid < 64) lsest(st)[tid] = x;
-        else if (tid < 128) dlst(st)[tid - 64] = x;
+        dma_tile_asm<D, NW>(rsrc_words((const uint16_t*)a.q + qhead * D, head_bytes), lds_off(qst(st)), row0, a.S,
+                            wave, lane);
+        dma_tile_asm<D, NW>(rsrc_words((const uint16_t*)a.dout + qhead * D, head_bytes), lds_off(dost(st)), row0,
+                            a.S, wave, lane);
+        const int toff = (row0 + 32 * qs + lane) * 4;  // lanes 32..63 fetch values no one reads
+        dma4(rsrc_words(a.lse + qhead, a.S * 4), lds_off(side(st, wave, 0)), toff);
+        dma4(rsrc_words(a.delta + qhead, a.S * 4), lds_off(side(st, wave, 1)), toff);
     };
 
     f32x16 dk[DBLK], dv[DBLK];
@@ -563,24 +627,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
         dv[m] = (f32x16){};
     }
 
+    Unit cur;
+    cur.hh = -1;
+    cur.e = cur.e_end = 0;
+    cur.c = cur.nch = 0;
+    cur.i = 0;
+    bool have = settle(cur);
+    bool have1 = false;
+    Unit nx1 = cur;
     if (have) {
         issue(cur, 0);
-        const float sv = side_load(cur);
-        __builtin_amdgcn_s_waitcnt(kVmcnt0);
-        side_store(sv, 0);
+        nx1 = advance(cur, have1);
+        if (have1) issue(nx1, 1);
     }
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    __syncthreads();
-
     int st = 0;
     while (have) {
-        Unit nxt = cur;
-        ++nxt.c;
-        const bool have_next = settle(nxt);
-        float sv = 0.f;
-        if (have_next) {
-            issue(nxt, st ^ 1);
-            sv = side_load(nxt);
+        // Unit `cur` (stage st) has landed once at most the next unit's loads are outstanding.
+        if (have1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_UNIT));
+        else __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        bare_barrier();  // all waves: unit cur visible, and stage (st + 2) % 3 no longer read
+        bool have2 = false;
+        Unit nx2 = nx1;
+        if (have1) {
+            nx2 = advance(nx1, have2);
+            if (have2) issue(nx2, st == 0 ? 2 : st - 1);
         }
         const char* qt = qst(st);
         const char* dt = dost(st);
@@ -593,10 +663,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
             dp = mfma(row_frag<D, true>(dt, qr, 2 * ks + hf), vf[ks], dp);
         }
         // Lane holds key mykey (column) and queries 32 qs + 8 q + 4 hf + e (chunk rows) at [4 q + e].
+        // Element masks only where this wave's block is partial: under causal
+        // when a key may follow a query, and past the tile end or S. A query
+        // with LSE = -inf sees no key at all, so under causal every pair of its
+        // row here is masked, and without causal it cannot occur in a kept tile.
         const int tq0 = cur.i * bq + 64 * cur.c + 32 * qs;
-        const bool need_mask = a.causal && (key0 + 32 * kb + 31 > tq0);
-        const float* lsp = lsest(st) + 32 * qs + 4 * hf;
-        const float* dlp = dlst(st) + 32 * qs + 4 * hf;
+        const int t_lim = min(a.S, cur.i * bq + bq);  // queries of this unit are below t_lim
+        const bool need_mask = (a.causal && key0 + 32 * kb + 31 > tq0) || (tq0 + 31 >= t_lim);
+        const int key_lim = a.causal ? mykey : -1;
+        const float* lsp = side(st, wave, 0) + 4 * hf;
+        const float* dlp = side(st, wave, 1) + 4 * hf;
         bf16x8 pf[2], dsf[2];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -605,8 +681,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int x = 4 * q + e;
-                float p = fast_exp2(__builtin_fmaf(s[x], a.scale_log2, -lo[e]));
-                if (need_mask) p = (mykey <= tq0 + 8 * q + 4 * hf + e) ? p : 0.f;
+                float p = fast_exp2(__builtin_fmaf(s[x], a.scale_log2, -kLog2e * lo[e]));
+                if (need_mask) {
+                    const int t = tq0 + 8 * q + 4 * hf + e;
+                    p = (t < t_lim && key_lim <= t) ? p : 0.f;
+                }
                 const float ds = p * (dp[x] - de[e]);
                 pf[x >> 3][x & 7] = (__bf16)p;
                 dsf[x >> 3][x & 7] = (__bf16)ds;
@@ -621,16 +700,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
                 dv[m] = mfma(tr_frag<D>(dt, 32 * qs + 16 * s2, m, lane), pf[s2], dv[m]);
                 dk[m] = mfma(tr_frag<D>(qt, 32 * qs + 16 * s2, m, lane), dsf[s2], dk[m]);
             }
-        __builtin_amdgcn_s_waitcnt(kVmcnt0);
-        if (have_next) side_store(sv, st ^ 1);
-        __syncthreads();
-        cur = nxt;
-        have = have_next;
-        st ^= 1;
+        cur = nx1;
+        have = have1;
+        nx1 = nx2;
+        have1 = have2;
+        st = (st == 2) ? 0 : st + 1;
     }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();  // every wave is done with the stages (nothing is in flight any more)
 
     // Add the query-half partials: waves with qs = 1 park theirs in LDS.
-    float* red = (float*)lds;  // [kb][2][DBLK][16][64] floats = 2 * 2 * DBLK * 4 KiB <= 4 * TILEB
+    float* red = (float*)lds;  // [kb][2][DBLK][16][64] floats
     if (qs == 1) {
 #pragma unroll
         for (int m = 0; m < DBLK; ++m)
@@ -882,7 +962,7 @@ bool attn_bwd_mfma_supported(const AttnBwdArgs& a, int bf16) {
            (a.D == 64 || a.D == 128);
 }
 
-size_t attn_bwd_dkdv_lds_bytes(int D) { return 4 * (size_t)(64 * D * 2) + 4 * 64 * sizeof(float); }
+size_t attn_bwd_dkdv_lds_bytes(int D) { return D == 128 ? DkdvLds<128>::BYTES : DkdvLds<64>::BYTES; }
 
 hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t stream) {
     const int64_t qwork = (int64_t)a.B * a.Hq * a.NQ;

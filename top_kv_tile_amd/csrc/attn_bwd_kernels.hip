@@ -27,38 +27,16 @@
 //  * bwd_dq_simt_kernel / bwd_dkdv_simt_kernel: fp32 FMA fallback for fp32
 //    inputs and block sizes the MFMA kernels do not take.
 #include "nsa_internal.h"
+#include "device_common.h"
 
 #include <math.h>
 
 namespace nsa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef short short8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 constexpr float kPosInf = __builtin_huge_valf();
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr int kVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters at their maximum
-// s_waitcnt immediate for vmcnt(n), n < 64 (gfx9 encoding: low 4 bits, high 2 bits at 14).
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
-}
-
-// Uniform load through the constant address space: a scalar load (counted by
-// lgkmcnt) when the index is wave-uniform. Only for data no kernel of the
-// launch writes.
-typedef const __attribute__((address_space(4))) int32_t cint32;
-__device__ __forceinline__ int ld_scalar(const int32_t* p, int64_t i) { return ((cint32*)p)[i]; }
 
 // LSE in log2 units as the exponent offset of P; an empty row (LSE = -inf)
 // maps to +inf so that every P of that row is exactly 0.
@@ -226,9 +204,6 @@ struct Geo {
     }
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) short4_t lds_s4;
-
 // DMA of one 64-row tile (rows row0 .. row0 + 63 of a head, clamped to S - 1)
 // into `dst`, by the NW waves of the workgroup. `swz` picks the swizzle.
 template <int D, int NW, bool BOTH>
@@ -275,48 +250,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* tile, int r0, int m, int l
     return __builtin_bit_cast(bf16x8, w);
 }
 
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// ---- explicitly scheduled loads
-//
-// The compiler cannot tell which LDS stage a buffer-to-LDS DMA writes, so after
-// a DMA issued through the builtin it waits for every outstanding load before
-// the next transposing LDS read, and __syncthreads() also waits for all loads.
-// Kernels that keep several units in flight therefore issue their DMA with the
-// instruction itself (it has no register result, so nothing the compiler
-// tracks is left in flight), read their indices with scalar loads (counted by
-// lgkmcnt, not vmcnt), wait with explicit vmcnt counts and synchronise with a
-// bare s_barrier. Such a kernel issues no DMA through the builtin: the
-// compiler assumes it owns M0.
-// Raw buffer resource words (no stride, no swizzle; loads past `bytes` return zeros).
-__device__ __forceinline__ u32x4 rsrc_words(const void* p, uint32_t bytes) {
-    const uint64_t x = (uint64_t)p;
-    u32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)x);
-    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32) & 0xFFFFu);
-    r[2] = __builtin_amdgcn_readfirstlane(bytes);
-    r[3] = 0x00020000u;
-    return r;
-}
-// 16 bytes per lane from voff to LDS address lds + 16 * lane.
-__device__ __forceinline__ void dma16(u32x4 rs, uint32_t lds, int voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rs) : "memory");
-}
-// 4 bytes per lane from voff to LDS address lds + 4 * lane.
-__device__ __forceinline__ void dma4(u32x4 rs, uint32_t lds, int voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rs) : "memory");
-}
-// Workgroup barrier without the memory fence of __syncthreads(); LDS ordering
-// is the caller's (lgkmcnt / vmcnt waits before it).
-__device__ __forceinline__ void bare_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) { return mfma32(a, b, c); }
 
 // DMA of one 64-row tile (rows row0 .. row0 + 63 of a head, clamped to S - 1)
 // into LDS byte address dst, by the NW waves of the workgroup (bswz layout).
@@ -539,7 +473,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
     auto side = [&](int st, int w, int which) -> float* {
         return (float*)(lds + 2 * L::NST * G::TILEB + st * L::SIDE) + (w * 2 + which) * 64;
     };
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds);
+    const uint32_t lds0 = lds_address(lds);
     auto lds_off = [&](const void* p) -> uint32_t { return lds0 + (uint32_t)((const char*)p - lds); };
 
     const int tid = threadIdx.x, lane = tid & 63;

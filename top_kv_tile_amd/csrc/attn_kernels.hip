@@ -20,6 +20,7 @@
 //    transposed on its way into LDS.
 //  * attn_simt_kernel: any dtype / block size (fp32 path), plain fp32 FMA.
 #include "nsa_internal.h"
+#include "device_common.h"
 
 #include <float.h>
 #include <math.h>
@@ -27,19 +28,8 @@
 namespace nsa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef short short8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.69314718055994530942f;
-// s_waitcnt immediate for gfx9-family: vmcnt(0), expcnt and lgkmcnt left at their maximum.
-constexpr int kVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
     uint32_t u = __float_as_uint(x);
@@ -47,13 +37,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
     u += 0x7fffu + ((u >> 16) & 1u);                                 // round to nearest even
     return u >> 16;
 }
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Raw buffer resource over `bytes` bytes at p (stride 0, no swizzle): loads
-// at offsets past `bytes` return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
-}
 
 // Work item of a workgroup. Workgroups are dispatched round-robin over the 8
 // XCDs (block n runs on XCD n % 8); inside each run of 64 consecutive blocks,
@@ -149,9 +133,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     using G = MfmaGeo<D>;
     constexpr int IPW = (G::NINSTR + NW - 1) / NW;  // DMA instructions per wave per tile
     extern __shared__ __attribute__((aligned(1024))) char lds[];
-    typedef __attribute__((address_space(3))) void lds_void;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hf = lane >> 5;
     const int64_t total = (int64_t)a.B * a.Hq * a.NQ;
     const Work wk = decode_work(blockIdx.x, total, a.Hq, a.Hkv, a.NQ);
@@ -168,10 +152,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     const int head_bytes = a.S * G::ROWB;
     const __amdgpu_buffer_rsrc_t qrs =
         make_rsrc((const uint16_t*)a.q + (((int64_t)wk.b * a.Hq + wk.h) * a.S) * D, head_bytes);
-    const __amdgpu_buffer_rsrc_t krs =
-        make_rsrc((const uint16_t*)a.k + (((int64_t)wk.b * a.Hkv + wk.g) * a.S) * D, head_bytes);
-    const __amdgpu_buffer_rsrc_t vrs =
-        make_rsrc((const uint16_t*)a.v + (((int64_t)wk.b * a.Hkv + wk.g) * a.S) * D, head_bytes);
+    const u32x4 krs = rsrc_words((const uint16_t*)a.k + (((int64_t)wk.b * a.Hkv + wk.g) * a.S) * D, head_bytes);
+    const u32x4 vrs = rsrc_words((const uint16_t*)a.v + (((int64_t)wk.b * a.Hkv + wk.g) * a.S) * D, head_bytes);
 
     // Q^T operand: lane holds q[qrow][16*ks + 8*hf .. +8] for every ks (zeros past S).
     bf16x8 qf[KSTEPS];
@@ -207,40 +189,34 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     // from the logical chunk given by the row's swizzle.
     // Rows past the end of the sequence (ragged last tile) read row S - 1
     // instead: in range, finite, and masked out (K) or weighted by p = 0 (V).
-    int drow[IPW], kchunk[IPW], vchunk[IPW];
-#pragma unroll
-    for (int x = 0; x < IPW; ++x) {
-        const int ii = wave + NW * x;
-        const int row = ii * G::RPI + lane / G::CH, pc = lane % G::CH;
-        drow[x] = row;
-        kchunk[x] = (pc ^ G::kswz(row)) * 16;
-        vchunk[x] = (pc ^ G::vswz(row)) * 16;
-    }
+    // The DMA is issued by the instruction itself and every wait on it is
+    // explicit (vmcnt(0) at the end of a step), so the tiles of step n + 1 stay
+    // in flight through the whole of step n, transposed V reads included.
+    // (Row and chunk offsets are recomputed from the lane index at each issue
+    // rather than kept in registers: a spilled register's reload is a vector
+    // memory load, and waiting for it would also wait for the tiles in flight.)
     char* kst[2] = {lds, lds + G::TILEB};
     char* vst[2] = {lds + 2 * G::TILEB, lds + 3 * G::TILEB};
-    auto dma = [&](__amdgpu_buffer_rsrc_t rs, const int (&chunk)[IPW], char* stage_base, int j) {
+    const uint32_t lds0 = lds_address(lds);
+    auto dma = [&](u32x4 rs, bool is_v, char* stage_base, int j) {
         const int key0 = j * BKV;
+        const uint32_t base = lds0 + (uint32_t)(stage_base - lds);
 #pragma unroll
         for (int x = 0; x < IPW; ++x) {
             const int ii = wave + NW * x;
             if (G::NINSTR % NW == 0 || ii < G::NINSTR) {
-                const int off = min(key0 + drow[x], a.S - 1) * G::ROWB + chunk[x];
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(stage_base + ii * 1024), 16, off, 0, 0, 0);
+                const int row = ii * G::RPI + lane / G::CH, pc = lane % G::CH;
+                const int chunk = pc ^ (is_v ? G::vswz(row) : G::kswz(row));
+                const int off = min(key0 + row, a.S - 1) * G::ROWB + chunk * 16;
+                dma16(rs, base + ii * 1024, off);
             }
         }
     };
-    auto dma_k = [&](int j, int stage) { dma(krs, kchunk, kst[stage], j); };
-    auto dma_v = [&](int j, int stage) { dma(vrs, vchunk, vst[stage], j); };
+    auto dma_k = [&](int j, int stage) { dma(krs, false, kst[stage], j); };
+    auto dma_v = [&](int j, int stage) { dma(vrs, true, vst[stage], j); };
 
     // LDS read offsets (bytes) that do not depend on the tile.
     // K: lane reads row 32*mb + l32, logical chunk 2*ks + hf.
-    int krow_off[2], kswz_l[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int row = 32 * mb + l32;
-        krow_off[mb] = row * G::ROWB;
-        kswz_l[mb] = G::kswz(row);
-    }
     // V^T: lane (group g = lane/16, s = lane%16) addresses row 16*kk + 4*hf + s/4
     // (+8 for the second half) at d = 32*m + 16*(g%2) + 4*(s%4).
     const int vg = lane >> 4, vs = lane & 15;
@@ -271,8 +247,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     };
     // S^T = K Q^T for the tile in K stage `stage` (raw dot products).
     auto qk_frag = [&](const char* ks, int ks_, int mb) -> bf16x8 {
-        const int chunk = (2 * ks_ + hf) ^ kswz_l[mb];
-        return __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + krow_off[mb] + chunk * 16));
+        const int row = 32 * mb + l32;
+        const int chunk = (2 * ks_ + hf) ^ G::kswz(row);
+        return __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + row * G::ROWB + chunk * 16));
     };
     // One straight-line block: the matrix cores compute S(next) while the
     // vector ALUs turn S(cur) into P (row max, exponentials, bf16 pack, row
@@ -382,8 +359,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
         pv(pf, vst_cur);
         j_cur = j_next;
         j_next = j_after;
-        __builtin_amdgcn_s_waitcnt(kVmcnt0);
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);  // K(n + 2) and V(n + 1) have landed
+        bare_barrier();
     };
     int n = 0;
     for (; n + 1 < ntiles; n += 2) {

@@ -142,7 +142,8 @@ int nsa_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Attention over the kept tiles. For query head h, kv head g = h / (Hq/Hkv)
- * and selection head h' = h (or 0 when sel->H == 1). Key u is visible to query
+ * and selection head h' = h (or 0 when sel->H == 1); a selection with
+ * sel->B == 1 applies to every batch entry (as radial_blocks returns it). Key u is visible to query
  * t iff tile (t / block_q, u / block_kv) is kept in row (b, h', t / block_q)
  * and, when causal != 0, u <= t. With l_tu = D^-1/2 q_t . k_u:
  *   lse[t] = ln sum_{visible u} exp(l_tu)            (fp32, natural log)
@@ -155,6 +156,62 @@ int nsa_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec,
 int nsa_block_sparse_attn(const nsa_tensor* q, const nsa_tensor* k, const nsa_tensor* v,
                           const nsa_selection* sel, int causal, nsa_tensor* out,
                           float* lse, void* stream);
+
+/* ---- Plan reuse --------------------------------------------------------------
+ * selection_plan on the selection page depends only on geometry, the spec and
+ * the pin / drop masks, and the page caches it under a caller-supplied key
+ * that leaves the mask contents out. Here the plan is an explicit handle built
+ * from all of them, so a reused plan can never be stale. */
+typedef struct nsa_plan nsa_plan;
+
+/* Host only. Builds the plan nsa_select would build for tensors shaped like q
+ * and k (read for shape and dtype only) and copies what it needs from pins and
+ * drops (the caller may free them afterwards). Errors as nsa_select_sizes.
+ * The handle is immutable and may be used by several threads at once. */
+int nsa_plan_create(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec,
+                    const nsa_mask* pins, const nsa_mask* drops, nsa_plan** out);
+
+/* Host only. The sizes of the planned selection (as nsa_select_sizes). */
+int nsa_plan_sizes(const nsa_plan* plan, nsa_sizes* out, int32_t* row_ptr_host);
+
+/* nsa_select with a prebuilt plan: q and k must have the plan's shapes and
+ * dtype (BAD_SHAPE / BAD_DTYPE otherwise). Result, outputs, workspace and
+ * errors as nsa_select with the plan's spec, pins and drops. */
+int nsa_select_planned(const nsa_plan* plan, const nsa_tensor* q, const nsa_tensor* k,
+                       nsa_selection* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Frees a plan (NULL is allowed). */
+void nsa_plan_destroy(nsa_plan* plan);
+
+/* ---- Controls (selection page: schedule, radial_blocks, BlockSelection.density) */
+
+/* Host only. Per-step budgets: out[i] = budget, raised to min(1, budget + bump)
+ * on the first and last edge steps, edge = min(bump_steps, ceil(steps / 2)),
+ * when bump > 0, bump_steps > 0 and steps > 0. Writes max(steps, 0) values
+ * (fp64, as the page's Python floats). NULL_ARG if steps > 0 and out is NULL. */
+int nsa_schedule(int32_t steps, double budget, double bump, int32_t bump_steps, double* out);
+
+/* Host only. Sizes of radial_blocks(seq_q, seq_kv, density): NQ, NK,
+ * sel_heads = 1, rows = NQ, nnz; row_ptr_host (NQ + 1 int32) if non-NULL.
+ * BAD_SPEC for block sizes <= 0 or negative lengths. */
+int nsa_radial_sizes(int32_t seq_q, int32_t seq_kv, double density, const nsa_spec* spec,
+                     nsa_sizes* out, int32_t* row_ptr_host);
+
+/* radial_blocks of the selection page: the static control at a given density.
+ * A tile is kept when the centres of its query and kv token ranges are at
+ * most a bandwidth apart; the bandwidth is bisected 40 times over
+ * [0, max(seq_q, seq_kv)] until the kept fraction reaches density (distances
+ * in fp32, the kept fraction an fp32 mean compared in fp64). Computed on the
+ * host (geometry only) and copied on `stream` into out->keep (1, 1, NQ, NK)
+ * int8, out->row_ptr (NQ + 1) and out->col_idx (capacity out->col_capacity);
+ * the other fields of out are set (B = H = 1, budget = density). Errors:
+ * NULL_ARG, BAD_SPEC, CAPACITY, HIP. */
+int nsa_radial_blocks(int32_t seq_q, int32_t seq_kv, double density, const nsa_spec* spec,
+                      nsa_selection* out, void* stream);
+
+/* Host only. BlockSelection.density: kept tiles / (B * H * NQ * NK), from the
+ * selection's nnz (no device readback). 0 for an empty selection. */
+int nsa_selection_density(const nsa_selection* sel, double* out);
 
 /* Device workspace, in bytes, that nsa_block_sparse_attn_bwd needs for these
  * shapes and this selection (sel may be NULL for dense). Host only. */

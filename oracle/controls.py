@@ -49,7 +49,8 @@ def _tile_centre_distance(seq_q: int, seq_kv: int, block_q: int, block_kv: int) 
 def _fraction_within(distance: np.ndarray, width: float) -> float:
     """float32 mean of (distance <= width), width rounded to float32, returned as a float."""
     inside = (distance <= np.float32(width)).astype(np.float32)
-    return float(np.float32(inside.sum(dtype=np.float64)) / np.float32(inside.size))
+    with np.errstate(invalid="ignore"):  # no tiles: NaN, as the mean of an empty tensor
+        return float(np.float32(inside.sum(dtype=np.float64)) / np.float32(inside.size))
 
 
 def radial_blocks(seq_q: int, seq_kv: int, density: float, block_q: int, block_kv: int) -> np.ndarray:

@@ -26,7 +26,7 @@ def L():
 
 def _declared():
     src = open(os.path.join(ROOT, "include", "nsa.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(nsa_\w+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|void|const char\*)\s+(nsa_\w+)\s*\(", src, re.M)))
 
 
 def test_exports_every_declared_symbol(L):

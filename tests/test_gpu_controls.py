@@ -1,0 +1,68 @@
+"""GPU parity of the controls and plan reuse: the radial band (device keep and
+CSR against the oracle, then attention and its gradients over that band with one
+selection broadcast to every batch entry), planned selection against
+nsa_select, and the host-side density."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import top_kv_tile_amd as tkt
+from oracle.attention_bwd import attention_backward
+from parity_util import check_attention, say, to_dev
+from test_gpu_backward import _compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, Hq, Hkv, S, D, seed, dtype=torch.bfloat16):
+    g = torch.Generator().manual_seed(seed)
+    return [torch.randn(B, h, S, D, generator=g).to(dtype) for h in (Hq, Hkv, Hkv, Hq)]
+
+
+@pytest.mark.parametrize("S,bq,bkv,dens,causal", [(1000, 128, 64, 0.15, True), (2048, 64, 64, 0.3, False),
+                                                  (777, 128, 64, 0.5, True)])
+def test_radial_band_attention_and_gradients(S, bq, bkv, dens, causal):
+    say(f"radial S={S} bq={bq} bkv={bkv} density={dens} causal={causal}")
+    spec = tkt.SparseSpec(block_q=bq, block_kv=bkv)
+    sel = tkt.nsa_radial_blocks(S, S, dens, spec)
+    torch.cuda.synchronize()
+    ref_keep = oracle.radial_blocks(S, S, dens, bq, bkv)
+    keep = sel.keep.cpu().numpy()
+    assert np.array_equal(keep, ref_keep)
+    r_ptr, r_col = oracle.keep_to_csr(ref_keep)
+    assert np.array_equal(sel.row_ptr.cpu().numpy(), r_ptr)
+    assert np.array_equal(sel.col_idx.cpu().numpy(), r_col)
+    assert sel.density() == oracle.density(ref_keep)
+    q, k, v, do = _inputs(2, 4, 2, S, 128, seed=S + bq)
+    qd, kd, vd, dod = (to_dev(t) for t in (q, k, v, do))
+    out, lse = tkt.nsa_block_sparse_attn(qd, kd, vd, sel, causal)   # one band for both batch entries
+    ref_o, ref_l = oracle.attention(q, k, v, ref_keep, bq, bkv, causal)
+    check_attention(out, lse, ref_o, ref_l, "bf16", where="radial")
+    dq, dk, dv = tkt.nsa_block_sparse_attn_bwd(qd, kd, vd, out, lse, dod, sel, causal)
+    rq, rk, rv = attention_backward(q, k, v, do, ref_keep, bq, bkv, causal)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        _compare(name, got, ref, "bf16", where="radial")
+
+
+def test_planned_selection_equals_select():
+    say("planned selection")
+    B, Hq, Hkv, S, D = 2, 4, 2, 1024, 128
+    nq, nk = 8, 16
+    rng = np.random.default_rng(12)
+    pins = (rng.random((B, 1, nq, nk)) < 0.1).astype(np.int8)
+    drops = (rng.random((1, Hq, nq, nk)) < 0.1).astype(np.int8)
+    spec = tkt.SparseSpec(budget=0.3)
+    q0, k0, _, _ = _inputs(B, Hq, Hkv, S, D, seed=1)
+    plan = tkt.nsa_plan_create(to_dev(q0), to_dev(k0), spec, pins, drops)
+    for seed in (2, 3, 4):  # same shapes, new values: the plan is reused
+        q, k, _, _ = _inputs(B, Hq, Hkv, S, D, seed=seed)
+        qd, kd = to_dev(q), to_dev(k)
+        a = tkt.nsa_select(qd, kd, spec, pins, drops)
+        b = tkt.nsa_select_planned(plan, qd, kd)
+        torch.cuda.synchronize()
+        assert torch.equal(a.keep, b.keep) and torch.equal(a.row_ptr, b.row_ptr)
+        assert torch.equal(a.col_idx, b.col_idx)
+        assert abs(b.density() - float(b.keep.float().mean().item())) < 1e-12
+    dense_plan = tkt.nsa_plan_create(to_dev(q0), to_dev(k0), tkt.SparseSpec(budget=1.0))
+    assert tkt.nsa_select_planned(dense_plan, to_dev(q0), to_dev(k0)) is None

@@ -8,6 +8,7 @@ from .nsa import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     NsaError,
+    Plan,
     Selection,
     Sizes,
     SparseSpec,
@@ -15,10 +16,15 @@ from .nsa import (  # noqa: F401
     nsa_attn_bwd_workspace_size,
     nsa_block_sparse_attn,
     nsa_block_sparse_attn_bwd,
+    nsa_plan_create,
     nsa_pool_blocks,
+    nsa_radial_blocks,
+    nsa_schedule,
     nsa_score_blocks,
     nsa_select,
+    nsa_select_planned,
     nsa_select_sizes,
+    nsa_selection_density,
     nsa_status_string,
 )
 

@@ -134,7 +134,7 @@ __device__ __forceinline__ void q_tile_range(const AttnBwdArgs& a, int b, int h,
                                              int& end) {
     if (a.row_ptr) {
         const int hs = (a.Hsel == 1) ? 0 : h;
-        const int64_t r = ((int64_t)b * a.Hsel + hs) * a.NQ + i;
+        const int64_t r = ((int64_t)(a.Bsel == 1 ? 0 : b) * a.Hsel + hs) * a.NQ + i;
         start = a.row_ptr[r];
         end = a.row_ptr[r + 1];
         if (a.causal) {
@@ -158,7 +158,7 @@ __device__ __forceinline__ void q_tile_range(const AttnBwdArgs& a, int b, int h,
 __device__ __forceinline__ void kv_tile_range(const AttnBwdArgs& a, int b, int hs, int j, int key0, int& start,
                                               int& end) {
     if (a.col_ptr) {
-        const int64_t c = ((int64_t)b * a.Hsel + hs) * a.NK + j;
+        const int64_t c = ((int64_t)(a.Bsel == 1 ? 0 : b) * a.Hsel + hs) * a.NK + j;
         start = ld_scalar(a.col_ptr, c);
         end = ld_scalar(a.col_ptr, c + 1);
         if (a.causal) {

@@ -77,7 +77,7 @@ __device__ __forceinline__ void tile_range(const AttnArgs& a, int b, int h, int 
                                            int& end) {
     if (a.row_ptr) {
         const int hs = (a.Hsel == 1) ? 0 : h;
-        const int64_t r = ((int64_t)b * a.Hsel + hs) * a.NQ + i;
+        const int64_t r = ((int64_t)(a.Bsel == 1 ? 0 : b) * a.Hsel + hs) * a.NQ + i;
         start = a.row_ptr[r];
         end = a.row_ptr[r + 1];
         if (a.causal) {

@@ -123,6 +123,7 @@ struct Plan {
     std::vector<int32_t> row_ptr;  // rows + 1
     std::vector<uint64_t> pin_words, drop_words;
     int pb = 1, ph = 1, db = 1, dh = 1;
+    bool has_pins = false, has_drops = false;
     int64_t nnz = 0;
     bool dense = true;
 };
@@ -137,6 +138,8 @@ inline int64_t keep_per_row(int64_t c, float budget) {
 int build_plan(const Geo& g, const nsa_spec* spec, const nsa_mask* pins, const nsa_mask* drops, Plan& p,
                bool want_row_ptr) {
     p.g = g;
+    p.has_pins = pins != nullptr;
+    p.has_drops = drops != nullptr;
     if (pins) {
         pack_mask(pins, g.NKW, p.pin_words);
         p.pb = pins->b_dim;
@@ -207,8 +210,8 @@ struct WsLayout {
     int chunk = 1;
 };
 
-WsLayout ws_layout(const Geo& g, const nsa_spec* spec, bool has_pins, const nsa_mask* pins, bool has_drops,
-                   const nsa_mask* drops) {
+WsLayout ws_layout(const Geo& g, const nsa_spec* spec, bool has_pins, int pin_slabs, bool has_drops,
+                   int drop_slabs) {
     WsLayout w;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -227,8 +230,8 @@ WsLayout ws_layout(const Geo& g, const nsa_spec* spec, bool has_pins, const nsa_
     const int64_t per_head = std::max<int64_t>((int64_t)g.NQ * g.NK * 4, 1);
     w.chunk = (int)std::max<int64_t>(1, std::min<int64_t>(g.Hsel, spec->score_chunk_bytes / per_head));
     w.scores = take((size_t)g.B * w.chunk * g.NQ * g.NK * 4);
-    if (has_pins) w.pinw = take((size_t)pins->b_dim * pins->h_dim * g.NQ * g.NKW * 8);
-    if (has_drops) w.dropw = take((size_t)drops->b_dim * drops->h_dim * g.NQ * g.NKW * 8);
+    if (has_pins) w.pinw = take((size_t)pin_slabs * g.NQ * g.NKW * 8);
+    if (has_drops) w.dropw = take((size_t)drop_slabs * g.NQ * g.NKW * 8);
     w.total = off;
     return w;
 }
@@ -324,7 +327,163 @@ int run_pool(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, con
 }
 
 
-// ---- attention gradients -----------------------------------------------------
+WsLayout plan_layout(const Plan& p, const nsa_spec* spec) {
+    return ws_layout(p.g, spec, p.has_pins, p.pb * p.ph, p.has_drops, p.db * p.dh);
+}
+
+void fill_sizes(const Plan& p, const nsa_spec* spec, nsa_sizes* out, int32_t* row_ptr_host) {
+    const WsLayout w = plan_layout(p, spec);
+    out->NQ = p.g.NQ;
+    out->NK = p.g.NK;
+    out->sel_heads = p.g.Hsel;
+    out->dense = (p.dense && !spec->force) ? 1 : 0;
+    out->rows = p.g.rows;
+    out->nnz = p.nnz;
+    out->workspace_bytes = (int64_t)w.total;
+    if (row_ptr_host) std::memcpy(row_ptr_host, p.row_ptr.data(), p.row_ptr.size() * sizeof(int32_t));
+}
+
+// Enqueues the selection of a built plan (row_ptr present) for tensors q, k
+// whose geometry the plan was built from.
+int run_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, const Plan& p, nsa_selection* out,
+               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const Geo& g = p.g;
+    if (p.dense && !spec->force) return NSA_DENSE;
+    if (g.rows > 0 && (!out->keep || !out->row_ptr)) return NSA_ERR_NULL_ARG;
+    if (!out->row_ptr) return NSA_ERR_NULL_ARG;
+    if (p.nnz > 0 && !out->col_idx) return NSA_ERR_NULL_ARG;
+    if (out->col_capacity < p.nnz) return NSA_ERR_CAPACITY;
+    const WsLayout w = plan_layout(p, spec);
+    if (workspace_bytes < w.total) return NSA_ERR_WORKSPACE;
+    if (w.total > 0 && (!workspace || ((uintptr_t)workspace & 255))) return NSA_ERR_WORKSPACE;
+
+    out->nnz = p.nnz;
+    out->B = g.B;
+    out->H = g.Hsel;
+    out->NQ = g.NQ;
+    out->NK = g.NK;
+    out->block_q = spec->block_q;
+    out->block_kv = spec->block_kv;
+    out->seq_q = g.Sq;
+    out->seq_kv = g.Skv;
+    out->budget = spec->budget;
+
+    char* ws = (char*)workspace;
+    {
+        void* dst[3] = {out->row_ptr, ws + w.pinw, ws + w.dropw};
+        const void* src[3] = {p.row_ptr.data(), p.pin_words.data(), p.drop_words.data()};
+        size_t bytes[3] = {p.row_ptr.size() * sizeof(int32_t), p.has_pins ? p.pin_words.size() * 8 : 0,
+                           p.has_drops ? p.drop_words.size() * 8 : 0};
+        hipError_t e = upload(3, dst, src, bytes, stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    if (g.rows == 0 || g.NK == 0) return NSA_OK;
+
+    const float* qh;
+    const float* kh;
+    int Hk;
+    int st;
+    if ((st = run_pool(q, k, spec, g, w, ws, stream, &qh, &kh, &Hk)) != NSA_OK) return st;
+    float* scores = (float*)(ws + w.scores);
+    for (int h0 = 0; h0 < g.Hsel; h0 += w.chunk) {
+        const int nh = std::min(w.chunk, g.Hsel - h0);
+        hipError_t e = nsa::launch_scores(qh, kh, g.B, g.Hsel, Hk, g.group, h0, nh, g.NQ, g.NK, g.D, scores,
+                                          stream);
+        if (e != hipSuccess) return hip_fail(e);
+        nsa::TopkArgs ta;
+        ta.scores = scores;
+        ta.B = g.B;
+        ta.Hsel = g.Hsel;
+        ta.h0 = h0;
+        ta.nh = nh;
+        ta.NQ = g.NQ;
+        ta.NK = g.NK;
+        ta.NKW = g.NKW;
+        ta.block_q = spec->block_q;
+        ta.block_kv = spec->block_kv;
+        ta.budget = spec->budget;
+        ta.pin_words = p.has_pins ? (const uint64_t*)(ws + w.pinw) : nullptr;
+        ta.pb = p.pb;
+        ta.ph = p.ph;
+        ta.drop_words = p.has_drops ? (const uint64_t*)(ws + w.dropw) : nullptr;
+        ta.db = p.db;
+        ta.dh = p.dh;
+        ta.row_ptr = out->row_ptr;
+        ta.keep = out->keep;
+        ta.col_idx = out->col_idx;
+        if ((e = nsa::launch_topk(ta, stream)) != hipSuccess) return hip_fail(e);
+    }
+    return NSA_OK;
+}
+
+// ---- radial band (radial_blocks of the selection page) -------------------------
+
+// Tiles whose query-range and kv-range centres are at most a bandwidth apart,
+// the bandwidth bisected 40 times over [0, max(seq_q, seq_kv)] until the kept
+// fraction reaches `density`. Arithmetic as the page's: centre distances in
+// float32, the trial width rounded to float32 for the comparison, the kept
+// fraction a float32 mean compared with the float64 density. The counts come
+// from the sorted distances instead of a pass per trial (same result).
+struct Band {
+    int NQ = 0, NK = 0;
+    std::vector<int32_t> row_ptr;  // NQ + 1
+    std::vector<int32_t> col_idx;
+    std::vector<int8_t> keep;      // NQ x NK
+};
+int build_band(int seq_q, int seq_kv, double density, int bq, int bkv, Band& band) {
+    band.NQ = (int)ceil_div(seq_q, bq);
+    band.NK = (int)ceil_div(seq_kv, bkv);
+    const int64_t n = (int64_t)band.NQ * band.NK;
+    if (n >= ((int64_t)1 << 31)) return NSA_ERR_UNSUPPORTED;
+    std::vector<float> dist((size_t)n);
+    for (int i = 0; i < band.NQ; ++i) {
+        const float qc = ((float)i + 0.5f) * (float)bq;
+        for (int j = 0; j < band.NK; ++j) {
+            const float kc = ((float)j + 0.5f) * (float)bkv;
+            dist[(size_t)i * band.NK + j] = std::fabs(qc - kc);
+        }
+    }
+    std::vector<float> sorted(dist);
+    std::sort(sorted.begin(), sorted.end());
+    auto fraction = [&](double width) -> double {
+        const float w32 = (float)width;
+        const int64_t cnt = std::upper_bound(sorted.begin(), sorted.end(), w32) - sorted.begin();
+        volatile float frac = (float)cnt / (float)std::max<int64_t>(n, 1);  // one fp32 rounding
+        return (double)frac;
+    };
+    double low = 0.0, high = (double)std::max(seq_q, seq_kv);
+    for (int it = 0; it < 40; ++it) {
+        const double mid = (low + high) / 2;
+        if (fraction(mid) < density) low = mid;
+        else high = mid;
+    }
+    const float h32 = (float)high;
+    band.keep.assign((size_t)n, 0);
+    band.row_ptr.assign((size_t)band.NQ + 1, 0);
+    band.col_idx.clear();
+    for (int i = 0; i < band.NQ; ++i) {
+        for (int j = 0; j < band.NK; ++j)
+            if (dist[(size_t)i * band.NK + j] <= h32) {
+                band.keep[(size_t)i * band.NK + j] = 1;
+                band.col_idx.push_back(j);
+            }
+        band.row_ptr[i + 1] = (int32_t)band.col_idx.size();
+    }
+    return NSA_OK;
+}
+
+}  // namespace
+
+// Opaque host-side selection plan: the geometry, the packed pin / drop masks
+// and the row offsets, built once and reused by nsa_select_planned.
+struct nsa_plan {
+    nsa_spec spec;
+    nsa_tensor qshape, kshape;  // shapes and dtype only
+    Plan p;
+};
+
+namespace {
+
 
 // Selection geometry shared by the forward and the gradients; fills the CSR
 // pointers, selection heads and block sizes of a launch (dense when sel is null).
@@ -340,7 +499,7 @@ int attn_selection(const nsa_tensor* q, const nsa_tensor* k, const nsa_selection
     if (sel->nnz > 0 && !sel->col_idx) return NSA_ERR_NULL_ARG;
     if (sel->nnz < 0 || sel->nnz >= ((int64_t)1 << 31)) return NSA_ERR_BAD_SHAPE;
     if (sel->block_q <= 0 || sel->block_kv <= 0) return NSA_ERR_BAD_SPEC;
-    if (sel->B != q->B || (sel->H != 1 && sel->H != q->H)) return NSA_ERR_BAD_SHAPE;
+    if ((sel->B != q->B && sel->B != 1) || (sel->H != 1 && sel->H != q->H)) return NSA_ERR_BAD_SHAPE;
     if (sel->seq_q != q->S || sel->seq_kv != k->S) return NSA_ERR_BAD_SHAPE;
     if (sel->NQ != ceil_div(q->S, sel->block_q) || sel->NK != ceil_div(k->S, sel->block_kv))
         return NSA_ERR_BAD_SHAPE;
@@ -433,18 +592,8 @@ int nsa_select_sizes(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* s
         Plan p;
         st = build_plan(g, spec, pins, drops, p, row_ptr_host != nullptr);
         if (st != NSA_OK) return st;
-        const WsLayout w = ws_layout(g, spec, pins != nullptr, pins, drops != nullptr, drops);
-        out->NQ = g.NQ;
-        out->NK = g.NK;
-        out->sel_heads = g.Hsel;
-        out->dense = (p.dense && !spec->force) ? 1 : 0;
-        out->rows = g.rows;
-        out->nnz = p.nnz;
-        out->workspace_bytes = (int64_t)w.total;
-        if (row_ptr_host) std::memcpy(row_ptr_host, p.row_ptr.data(), p.row_ptr.size() * sizeof(int32_t));
+        fill_sizes(p, spec, out, row_ptr_host);
         return NSA_OK;
-    } catch (const std::bad_alloc&) {
-        return NSA_ERR_UNSUPPORTED;
     } catch (...) {
         return NSA_ERR_UNSUPPORTED;
     }
@@ -454,7 +603,6 @@ int nsa_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, c
                const nsa_mask* drops, nsa_selection* out, void* workspace, size_t workspace_bytes,
                void* stream_) {
     try {
-        hipStream_t stream = (hipStream_t)stream_;
         if (!out) return NSA_ERR_NULL_ARG;
         Geo g;
         int st = validate_select(q, k, spec, pins, drops, g);
@@ -462,74 +610,134 @@ int nsa_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, c
         Plan p;
         st = build_plan(g, spec, pins, drops, p, true);
         if (st != NSA_OK) return st;
-        if (p.dense && !spec->force) return NSA_DENSE;
-        if (g.rows > 0 && (!out->keep || !out->row_ptr)) return NSA_ERR_NULL_ARG;
-        if (!out->row_ptr) return NSA_ERR_NULL_ARG;
-        if (p.nnz > 0 && !out->col_idx) return NSA_ERR_NULL_ARG;
-        if (out->col_capacity < p.nnz) return NSA_ERR_CAPACITY;
-        const WsLayout w = ws_layout(g, spec, pins != nullptr, pins, drops != nullptr, drops);
-        if (workspace_bytes < w.total) return NSA_ERR_WORKSPACE;
-        if (w.total > 0 && (!workspace || ((uintptr_t)workspace & 255))) return NSA_ERR_WORKSPACE;
+        return run_select(q, k, spec, p, out, workspace, workspace_bytes, (hipStream_t)stream_);
+    } catch (...) {
+        return NSA_ERR_UNSUPPORTED;
+    }
+}
 
-        out->nnz = p.nnz;
-        out->B = g.B;
-        out->H = g.Hsel;
-        out->NQ = g.NQ;
-        out->NK = g.NK;
-        out->block_q = spec->block_q;
-        out->block_kv = spec->block_kv;
-        out->seq_q = g.Sq;
-        out->seq_kv = g.Skv;
-        out->budget = spec->budget;
-
-        char* ws = (char*)workspace;
-        {
-            void* dst[3] = {out->row_ptr, ws + w.pinw, ws + w.dropw};
-            const void* src[3] = {p.row_ptr.data(), p.pin_words.data(), p.drop_words.data()};
-            size_t bytes[3] = {p.row_ptr.size() * sizeof(int32_t), pins ? p.pin_words.size() * 8 : 0,
-                               drops ? p.drop_words.size() * 8 : 0};
-            hipError_t e = upload(3, dst, src, bytes, stream);
-            if (e != hipSuccess) return hip_fail(e);
+int nsa_plan_create(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, const nsa_mask* pins,
+                    const nsa_mask* drops, nsa_plan** out) {
+    try {
+        if (!out) return NSA_ERR_NULL_ARG;
+        *out = nullptr;
+        Geo g;
+        int st = validate_select(q, k, spec, pins, drops, g);
+        if (st != NSA_OK) return st;
+        nsa_plan* plan = new nsa_plan();
+        plan->spec = *spec;
+        plan->qshape = *q;
+        plan->kshape = *k;
+        plan->qshape.data = nullptr;
+        plan->kshape.data = nullptr;
+        st = build_plan(g, spec, pins, drops, plan->p, true);
+        if (st != NSA_OK) {
+            delete plan;
+            return st;
         }
-        if (g.rows == 0 || g.NK == 0) return NSA_OK;
-
-        const float* qh;
-        const float* kh;
-        int Hk;
-        if ((st = run_pool(q, k, spec, g, w, ws, stream, &qh, &kh, &Hk)) != NSA_OK) return st;
-        float* scores = (float*)(ws + w.scores);
-        for (int h0 = 0; h0 < g.Hsel; h0 += w.chunk) {
-            const int nh = std::min(w.chunk, g.Hsel - h0);
-            hipError_t e = nsa::launch_scores(qh, kh, g.B, g.Hsel, Hk, g.group, h0, nh, g.NQ, g.NK, g.D, scores,
-                                              stream);
-            if (e != hipSuccess) return hip_fail(e);
-            nsa::TopkArgs ta;
-            ta.scores = scores;
-            ta.B = g.B;
-            ta.Hsel = g.Hsel;
-            ta.h0 = h0;
-            ta.nh = nh;
-            ta.NQ = g.NQ;
-            ta.NK = g.NK;
-            ta.NKW = g.NKW;
-            ta.block_q = spec->block_q;
-            ta.block_kv = spec->block_kv;
-            ta.budget = spec->budget;
-            ta.pin_words = pins ? (const uint64_t*)(ws + w.pinw) : nullptr;
-            ta.pb = p.pb;
-            ta.ph = p.ph;
-            ta.drop_words = drops ? (const uint64_t*)(ws + w.dropw) : nullptr;
-            ta.db = p.db;
-            ta.dh = p.dh;
-            ta.row_ptr = out->row_ptr;
-            ta.keep = out->keep;
-            ta.col_idx = out->col_idx;
-            if ((e = nsa::launch_topk(ta, stream)) != hipSuccess) return hip_fail(e);
-        }
+        *out = plan;
         return NSA_OK;
     } catch (...) {
         return NSA_ERR_UNSUPPORTED;
     }
+}
+
+int nsa_plan_sizes(const nsa_plan* plan, nsa_sizes* out, int32_t* row_ptr_host) {
+    if (!plan || !out) return NSA_ERR_NULL_ARG;
+    fill_sizes(plan->p, &plan->spec, out, row_ptr_host);
+    return NSA_OK;
+}
+
+int nsa_select_planned(const nsa_plan* plan, const nsa_tensor* q, const nsa_tensor* k, nsa_selection* out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    try {
+        if (!plan || !out) return NSA_ERR_NULL_ARG;
+        int st;
+        if ((st = check_tensor(q)) != NSA_OK) return st;
+        if ((st = check_tensor(k)) != NSA_OK) return st;
+        const nsa_tensor &pq = plan->qshape, &pk = plan->kshape;
+        if (q->dtype != pq.dtype || k->dtype != pk.dtype) return NSA_ERR_BAD_DTYPE;
+        if (q->B != pq.B || q->H != pq.H || q->S != pq.S || q->D != pq.D) return NSA_ERR_BAD_SHAPE;
+        if (k->B != pk.B || k->H != pk.H || k->S != pk.S || k->D != pk.D) return NSA_ERR_BAD_SHAPE;
+        return run_select(q, k, &plan->spec, plan->p, out, workspace, workspace_bytes, (hipStream_t)stream);
+    } catch (...) {
+        return NSA_ERR_UNSUPPORTED;
+    }
+}
+
+void nsa_plan_destroy(nsa_plan* plan) { delete plan; }
+
+int nsa_schedule(int32_t steps, double budget, double bump, int32_t bump_steps, double* out) {
+    if (steps > 0 && !out) return NSA_ERR_NULL_ARG;
+    if (!(bump > 0) || bump_steps <= 0 || steps <= 0) {
+        for (int32_t i = 0; i < steps; ++i) out[i] = budget;
+        return NSA_OK;
+    }
+    const double raised = std::min(1.0, budget + bump);
+    const int32_t edge = std::min<int32_t>(bump_steps, (int32_t)ceil_div(steps, 2));
+    for (int32_t i = 0; i < steps; ++i) out[i] = (i < edge || i >= steps - edge) ? raised : budget;
+    return NSA_OK;
+}
+
+int nsa_radial_sizes(int32_t seq_q, int32_t seq_kv, double density, const nsa_spec* spec, nsa_sizes* out,
+                     int32_t* row_ptr_host) {
+    try {
+        if (!spec || !out) return NSA_ERR_NULL_ARG;
+        if (spec->block_q <= 0 || spec->block_kv <= 0 || seq_q < 0 || seq_kv < 0) return NSA_ERR_BAD_SPEC;
+        Band band;
+        const int st = build_band(seq_q, seq_kv, density, spec->block_q, spec->block_kv, band);
+        if (st != NSA_OK) return st;
+        out->NQ = band.NQ;
+        out->NK = band.NK;
+        out->sel_heads = 1;
+        out->dense = 0;
+        out->rows = band.NQ;
+        out->nnz = (int64_t)band.col_idx.size();
+        out->workspace_bytes = 0;
+        if (row_ptr_host) std::memcpy(row_ptr_host, band.row_ptr.data(), band.row_ptr.size() * sizeof(int32_t));
+        return NSA_OK;
+    } catch (...) {
+        return NSA_ERR_UNSUPPORTED;
+    }
+}
+
+int nsa_radial_blocks(int32_t seq_q, int32_t seq_kv, double density, const nsa_spec* spec, nsa_selection* out,
+                      void* stream) {
+    try {
+        if (!spec || !out) return NSA_ERR_NULL_ARG;
+        if (spec->block_q <= 0 || spec->block_kv <= 0 || seq_q < 0 || seq_kv < 0) return NSA_ERR_BAD_SPEC;
+        Band band;
+        const int st = build_band(seq_q, seq_kv, density, spec->block_q, spec->block_kv, band);
+        if (st != NSA_OK) return st;
+        const int64_t nnz = (int64_t)band.col_idx.size();
+        if (!out->row_ptr || (band.keep.size() > 0 && !out->keep) || (nnz > 0 && !out->col_idx))
+            return NSA_ERR_NULL_ARG;
+        if (out->col_capacity < nnz) return NSA_ERR_CAPACITY;
+        out->nnz = nnz;
+        out->B = 1;
+        out->H = 1;
+        out->NQ = band.NQ;
+        out->NK = band.NK;
+        out->block_q = spec->block_q;
+        out->block_kv = spec->block_kv;
+        out->seq_q = seq_q;
+        out->seq_kv = seq_kv;
+        out->budget = (float)density;
+        void* dst[3] = {out->keep, out->row_ptr, out->col_idx};
+        const void* src[3] = {band.keep.data(), band.row_ptr.data(), band.col_idx.data()};
+        size_t bytes[3] = {band.keep.size(), band.row_ptr.size() * sizeof(int32_t), (size_t)nnz * sizeof(int32_t)};
+        const hipError_t e = upload(3, dst, src, bytes, (hipStream_t)stream);
+        return e == hipSuccess ? NSA_OK : hip_fail(e);
+    } catch (...) {
+        return NSA_ERR_UNSUPPORTED;
+    }
+}
+
+int nsa_selection_density(const nsa_selection* sel, double* out) {
+    if (!sel || !out) return NSA_ERR_NULL_ARG;
+    const int64_t tiles = (int64_t)sel->B * sel->H * sel->NQ * sel->NK;
+    *out = (double)sel->nnz / (double)std::max<int64_t>(tiles, 1);
+    return NSA_OK;
 }
 
 int nsa_pool_blocks(const nsa_tensor* x, int32_t block, float* out, void* stream) {
@@ -551,7 +759,7 @@ int nsa_score_blocks(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* s
         Geo g;
         int st = validate_select(q, k, spec, nullptr, nullptr, g);
         if (st != NSA_OK) return st;
-        const WsLayout w = ws_layout(g, spec, false, nullptr, false, nullptr);
+        const WsLayout w = ws_layout(g, spec, false, 0, false, 0);
         if (workspace_bytes < w.total) return NSA_ERR_WORKSPACE;
         if (w.total > 0 && (!workspace || ((uintptr_t)workspace & 255))) return NSA_ERR_WORKSPACE;
         if (g.rows > 0 && g.NK > 0 && !scores) return NSA_ERR_NULL_ARG;
@@ -603,19 +811,21 @@ int nsa_block_sparse_attn(const nsa_tensor* q, const nsa_tensor* k, const nsa_te
         if (!sel->row_ptr) return NSA_ERR_NULL_ARG;
         if (sel->nnz > 0 && !sel->col_idx) return NSA_ERR_NULL_ARG;
         if (sel->block_q <= 0 || sel->block_kv <= 0) return NSA_ERR_BAD_SPEC;
-        if (sel->B != q->B || (sel->H != 1 && sel->H != q->H)) return NSA_ERR_BAD_SHAPE;
+        if ((sel->B != q->B && sel->B != 1) || (sel->H != 1 && sel->H != q->H)) return NSA_ERR_BAD_SHAPE;
         if (sel->seq_q != q->S || sel->seq_kv != k->S) return NSA_ERR_BAD_SHAPE;
         if (sel->NQ != ceil_div(q->S, sel->block_q) || sel->NK != ceil_div(k->S, sel->block_kv))
             return NSA_ERR_BAD_SHAPE;
         a.row_ptr = sel->row_ptr;
         a.col_idx = sel->col_idx;
         a.Hsel = sel->H;
+        a.Bsel = sel->B;
         a.block_q = sel->block_q;
         a.block_kv = sel->block_kv;
     } else {
         a.row_ptr = nullptr;
         a.col_idx = nullptr;
         a.Hsel = q->H;
+        a.Bsel = q->B;
         a.block_q = 128;
         a.block_kv = 64;
     }
@@ -673,6 +883,7 @@ int nsa_block_sparse_attn_bwd(const nsa_tensor* q, const nsa_tensor* k, const ns
     a.scale = (float)(1.0 / std::sqrt((double)q->D));
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)q->D));
     attn_selection(q, k, sel, a.Hsel, a.block_q, a.block_kv);
+    a.Bsel = sel ? sel->B : q->B;
     a.NQ = (int)ceil_div(q->S, a.block_q);
     a.NK = (int)ceil_div(k->S, a.block_kv);
     const int bf16 = q->dtype == NSA_BF16;

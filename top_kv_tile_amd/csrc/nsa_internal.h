@@ -50,6 +50,7 @@ struct AttnArgs {
     const int32_t* row_ptr;   // null = dense
     const int32_t* col_idx;
     int B, Hq, Hkv, Hsel, S, D, NQ, NK, block_q, block_kv;
+    int Bsel;                 // selection batch: B, or 1 (one selection for every batch entry)
     int causal;
     float scale_log2;         // D^-1/2 * log2(e)
 };
@@ -76,6 +77,7 @@ struct AttnBwdArgs {
     const int32_t* col_ptr;   // kv-tile-major index: (B*Hsel*NK + 1); null = dense
     const int32_t* row_idx;   // query tiles per (b, h', j), ascending
     int B, Hq, Hkv, Hsel, S, D, NQ, NK, block_q, block_kv;
+    int Bsel;                 // selection batch: B, or 1 (one selection for every batch entry)
     int causal;
     float scale;              // D^-1/2
     float scale_log2;         // D^-1/2 * log2(e)

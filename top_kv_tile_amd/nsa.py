@@ -21,13 +21,15 @@ import torch
 __all__ = [
     "SparseSpec", "Selection", "Sizes", "NsaError", "lib", "nsa_select_sizes", "nsa_select",
     "nsa_block_sparse_attn", "nsa_block_sparse_attn_bwd", "nsa_attn_bwd_workspace_size",
-    "nsa_pool_blocks", "nsa_score_blocks", "nsa_status_string", "LIB_PATH", "EXPORTS",
+    "nsa_pool_blocks", "nsa_score_blocks", "nsa_status_string", "Plan", "nsa_plan_create",
+    "nsa_select_planned", "nsa_schedule", "nsa_radial_blocks", "nsa_selection_density", "LIB_PATH", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnsa.so")
 EXPORTS = ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_attn_bwd_workspace_size",
            "nsa_block_sparse_attn_bwd", "nsa_pool_blocks", "nsa_score_blocks", "nsa_status_string",
-           "nsa_last_hip_error", "nsa_version")
+           "nsa_last_hip_error", "nsa_version", "nsa_plan_create", "nsa_plan_sizes", "nsa_select_planned",
+           "nsa_plan_destroy", "nsa_schedule", "nsa_radial_sizes", "nsa_radial_blocks", "nsa_selection_density")
 
 NSA_OK, NSA_DENSE = 0, 1
 NSA_F32, NSA_BF16 = 0, 1
@@ -93,11 +95,27 @@ def lib() -> ctypes.CDLL:
         L.nsa_pool_blocks.argtypes = [P(_Tensor), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
         L.nsa_score_blocks.argtypes = [P(_Tensor), P(_Tensor), P(_Spec), ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_size_t, ctypes.c_void_p]
+        L.nsa_plan_create.argtypes = [P(_Tensor), P(_Tensor), P(_Spec), P(_Mask), P(_Mask),
+                                      P(ctypes.c_void_p)]
+        L.nsa_plan_sizes.argtypes = [ctypes.c_void_p, P(_Sizes), ctypes.c_void_p]
+        L.nsa_select_planned.argtypes = [ctypes.c_void_p, P(_Tensor), P(_Tensor), P(_Selection), ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]
+        L.nsa_plan_destroy.argtypes = [ctypes.c_void_p]
+        L.nsa_plan_destroy.restype = None
+        L.nsa_schedule.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_double, ctypes.c_int32,
+                                   P(ctypes.c_double)]
+        L.nsa_radial_sizes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_double, P(_Spec), P(_Sizes),
+                                       ctypes.c_void_p]
+        L.nsa_radial_blocks.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_double, P(_Spec), P(_Selection),
+                                        ctypes.c_void_p]
+        L.nsa_selection_density.argtypes = [P(_Selection), P(ctypes.c_double)]
         L.nsa_status_string.argtypes = [ctypes.c_int]
         L.nsa_status_string.restype = ctypes.c_char_p
         L.nsa_version.restype = ctypes.c_char_p
         for name in ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_attn_bwd_workspace_size",
-                     "nsa_block_sparse_attn_bwd", "nsa_pool_blocks", "nsa_score_blocks", "nsa_last_hip_error"):
+                     "nsa_block_sparse_attn_bwd", "nsa_pool_blocks", "nsa_score_blocks", "nsa_last_hip_error",
+                     "nsa_plan_create", "nsa_plan_sizes", "nsa_select_planned", "nsa_schedule", "nsa_radial_sizes",
+                     "nsa_radial_blocks", "nsa_selection_density"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -154,8 +172,8 @@ class Selection:
         return int(self.col_idx.numel())
 
     def density(self) -> float:
-        """Fraction of tiles kept; reads back from the device (reporting and tests only)."""
-        return float(self.keep.sum().item()) / max(self.keep.numel(), 1)
+        """Fraction of tiles kept (BlockSelection.density), from the known nnz: no device readback."""
+        return nsa_selection_density(self)
 
     def _c(self) -> _Selection:
         B, H, NQ, NK = self.keep.shape
@@ -305,3 +323,84 @@ def nsa_score_blocks(q: torch.Tensor, k: torch.Tensor, spec: SparseSpec, stream=
                                   ctypes.c_void_p(s.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
                                   _stream(stream)), "nsa_score_blocks")
     return s
+
+
+class Plan:
+    """Host-side selection plan (nsa_plan_create): geometry, spec and mask contents, reusable across calls."""
+
+    def __init__(self, handle: int, spec: SparseSpec, q_shape, k_shape, dtype):
+        self._h = ctypes.c_void_p(handle)
+        self.spec = spec
+        self.q_shape, self.k_shape, self.dtype = tuple(q_shape), tuple(k_shape), dtype
+
+    def sizes(self) -> Sizes:
+        out = _Sizes()
+        _check(lib().nsa_plan_sizes(self._h, ctypes.byref(out), None), "nsa_plan_sizes")
+        return Sizes(out.NQ, out.NK, out.sel_heads, bool(out.dense), out.rows, out.nnz, out.workspace_bytes)
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h is not None and h.value and _LIB is not None:
+            _LIB.nsa_plan_destroy(h)
+
+
+def nsa_plan_create(q: torch.Tensor, k: torch.Tensor, spec: SparseSpec = SparseSpec(), pins=None,
+                    drops=None) -> Plan:
+    """Builds the selection plan for tensors shaped like q and k (read for shape and dtype only)."""
+    h = ctypes.c_void_p()
+    hold = []
+    _check(lib().nsa_plan_create(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)), ctypes.byref(spec._c()),
+                                 _mask(pins, hold), _mask(drops, hold), ctypes.byref(h)), "nsa_plan_create")
+    return Plan(h.value, spec, q.shape, k.shape, q.dtype)
+
+
+def nsa_select_planned(plan: Plan, q: torch.Tensor, k: torch.Tensor, stream=None,
+                       workspace: torch.Tensor | None = None):
+    """nsa_select with a prebuilt plan; returns a Selection, or None when the plan is dense."""
+    sizes = plan.sizes()
+    if sizes.dense:
+        return None
+    dev = q.device
+    keep = torch.empty((q.shape[0], sizes.sel_heads, sizes.NQ, sizes.NK), dtype=torch.int8, device=dev)
+    row_ptr = torch.empty(sizes.rows + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(sizes.nnz, dtype=torch.int32, device=dev)
+    if workspace is None or workspace.numel() < sizes.workspace_bytes:
+        workspace = torch.empty(max(sizes.workspace_bytes, 1), dtype=torch.uint8, device=dev)
+    spec = plan.spec
+    sel = Selection(keep, row_ptr, col_idx, spec.block_q, spec.block_kv, spec.budget, q.shape[2], k.shape[2])
+    csel = sel._c()
+    st = _check(lib().nsa_select_planned(plan._h, ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)),
+                                         ctypes.byref(csel), ctypes.c_void_p(workspace.data_ptr()),
+                                         workspace.numel(), _stream(stream)), "nsa_select_planned")
+    return None if st == NSA_DENSE else sel
+
+
+def nsa_schedule(steps: int, budget: float, bump: float = 0.0, bump_steps: int = 0) -> tuple:
+    """Per-step budgets (schedule of the selection page)."""
+    n = max(int(steps), 0)
+    buf = (ctypes.c_double * max(n, 1))()
+    _check(lib().nsa_schedule(int(steps), float(budget), float(bump), int(bump_steps), buf), "nsa_schedule")
+    return tuple(buf[i] for i in range(n))
+
+
+def nsa_radial_blocks(seq_q: int, seq_kv: int, density: float, spec: SparseSpec = SparseSpec(),
+                      device="cuda:0", stream=None) -> Selection:
+    """radial_blocks: the static band control at `density`; keep is (1, 1, NQ, NK)."""
+    out = _Sizes()
+    _check(lib().nsa_radial_sizes(int(seq_q), int(seq_kv), float(density), ctypes.byref(spec._c()),
+                                  ctypes.byref(out), None), "nsa_radial_sizes")
+    keep = torch.empty((1, 1, out.NQ, out.NK), dtype=torch.int8, device=device)
+    row_ptr = torch.empty(out.NQ + 1, dtype=torch.int32, device=device)
+    col_idx = torch.empty(out.nnz, dtype=torch.int32, device=device)
+    sel = Selection(keep, row_ptr, col_idx, spec.block_q, spec.block_kv, float(density), int(seq_q), int(seq_kv))
+    csel = sel._c()
+    _check(lib().nsa_radial_blocks(int(seq_q), int(seq_kv), float(density), ctypes.byref(spec._c()),
+                                   ctypes.byref(csel), _stream(stream)), "nsa_radial_blocks")
+    return sel
+
+
+def nsa_selection_density(sel: Selection) -> float:
+    """BlockSelection.density from the selection's nnz (host only)."""
+    d = ctypes.c_double()
+    _check(lib().nsa_selection_density(ctypes.byref(sel._c()), ctypes.byref(d)), "nsa_selection_density")
+    return d.value

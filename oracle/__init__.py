@@ -34,3 +34,4 @@ from .select import (  # noqa: F401
 from .attention import attention, attention_dense_literal, visible_key_counts  # noqa: F401
 from .attention_bwd import attention_backward  # noqa: F401
 from .controls import schedule, radial_blocks, density  # noqa: F401
+from .reorder import morton_order, hilbert_order, apply_order, undo_order  # noqa: F401

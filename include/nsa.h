@@ -213,6 +213,32 @@ int nsa_radial_blocks(int32_t seq_q, int32_t seq_kv, double density, const nsa_s
  * selection's nnz (no device readback). 0 for an empty selection. */
 int nsa_selection_density(const nsa_selection* sel, double* out);
 
+/* ---- Token reordering ("Optimal ordering with block mask") -------------------
+ * For tokens on a grid (an image, a video), laying the sequence out along a
+ * space-filling curve before a series of attention calls keeps neighbouring
+ * tokens in the same tiles, so local patterns touch fewer blocks. */
+enum { NSA_CURVE_MORTON = 0, NSA_CURVE_HILBERT = 1 };
+
+/* Host only. perm[m] = raster index (last axis fastest) of the grid point at
+ * position m of the curve, for a grid of ndim (1..4) axes of sizes dims[].
+ * Morton: the key interleaves coordinate bits (bit b of axis a, a = 0 the
+ * last axis, to bit b * ndim + a). Hilbert: J. Skilling's transpose method
+ * on the enclosing 2^p cube ("Programming the Hilbert curve", 2004); a grid
+ * that is not a full cube keeps the cube's order restricted to its points.
+ * perm holds prod(dims) int32. Errors: NULL_ARG, BAD_SPEC (kind),
+ * BAD_SHAPE (negative size), UNSUPPORTED (ndim, or more than 2^31 points). */
+int nsa_curve_order(int32_t kind, int32_t ndim, const int32_t* dims, int32_t* perm);
+
+/* y[b, h, m, :] = x[b, h, perm[m], :] (inverse == 0), or
+ * y[b, h, perm[m], :] = x[b, h, m, :] (inverse != 0), on `stream`.
+ * x, y: device (B, H, S, D), same shape and dtype, not the same buffer,
+ * 16-byte aligned, D * sizeof(dtype) a power of two from 64 to 1024 bytes.
+ * perm: device int32 (S), a permutation of [0, S); rows whose entry is
+ * outside [0, S) are left untouched. Errors: NULL_ARG, BAD_SHAPE, BAD_DTYPE,
+ * UNSUPPORTED, HIP. */
+int nsa_permute_tokens(const nsa_tensor* x, const int32_t* perm, int32_t inverse, nsa_tensor* y,
+                       void* stream);
+
 /* Device workspace, in bytes, that nsa_block_sparse_attn_bwd needs for these
  * shapes and this selection (sel may be NULL for dense). Host only. */
 int nsa_attn_bwd_workspace_size(const nsa_tensor* q, const nsa_tensor* k, const nsa_selection* sel,

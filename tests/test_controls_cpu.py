@@ -107,3 +107,34 @@ def test_selection_density_from_nnz(L):
     assert d.value == 30 / 120
     empty = N._Selection(nnz=0, B=1, H=1, NQ=0, NK=0)
     assert L.nsa_selection_density(ctypes.byref(empty), ctypes.byref(d)) == 0 and d.value == 0.0
+
+
+@pytest.mark.parametrize("dims", [(4, 4), (2, 2, 2), (128, 256), (5, 7), (3, 4, 5), (16, 16, 16), (1, 9), (64,),
+                                  (6, 10, 12)])
+def test_curve_orders_match_oracle(L, dims):
+    assert np.array_equal(tkt.nsa_curve_order(tkt.NSA_CURVE_MORTON, dims), oracle.morton_order(dims))
+    assert np.array_equal(tkt.nsa_curve_order(tkt.NSA_CURVE_HILBERT, dims), oracle.hilbert_order(dims))
+
+
+def test_curve_order_validation(L):
+    d = np.array([4, 4], np.int32)
+    out = np.zeros(16, np.int32)
+    assert L.nsa_curve_order(2, 2, d.ctypes.data, out.ctypes.data) == -6
+    assert L.nsa_curve_order(0, 0, d.ctypes.data, out.ctypes.data) == -4
+    assert L.nsa_curve_order(0, 2, None, out.ctypes.data) == -1
+    assert L.nsa_curve_order(0, 2, np.array([4, -1], np.int32).ctypes.data, out.ctypes.data) == -2
+    assert L.nsa_curve_order(0, 2, np.array([0, 5], np.int32).ctypes.data, None) == 0  # empty grid
+
+
+def test_permute_validation(L):
+    x = N._Tensor(1, N.NSA_BF16, 1, 2, 16, 128)
+    y = N._Tensor(2, N.NSA_BF16, 1, 2, 16, 128)
+    assert L.nsa_permute_tokens(ctypes.byref(x), None, 0, ctypes.byref(y), None) == -1
+    assert L.nsa_permute_tokens(ctypes.byref(x), 1, 0, ctypes.byref(N._Tensor(2, N.NSA_F32, 1, 2, 16, 128)),
+                                None) == -3
+    assert L.nsa_permute_tokens(ctypes.byref(x), 1, 0, ctypes.byref(N._Tensor(2, N.NSA_BF16, 1, 2, 15, 128)),
+                                None) == -2
+    assert L.nsa_permute_tokens(ctypes.byref(x), 1, 0, ctypes.byref(x), None) == -4          # in place
+    odd = N._Tensor(16, N.NSA_BF16, 1, 2, 16, 48)
+    assert L.nsa_permute_tokens(ctypes.byref(odd), 1, 0, ctypes.byref(N._Tensor(32, N.NSA_BF16, 1, 2, 16, 48)),
+                                None) == -4

@@ -6,6 +6,8 @@ package is its thin Python binding. See ``top_kv_tile_amd.nsa``.
 """
 from .nsa import (  # noqa: F401
     EXPORTS,
+    NSA_CURVE_HILBERT,
+    NSA_CURVE_MORTON,
     LIB_PATH,
     NsaError,
     Plan,
@@ -16,6 +18,8 @@ from .nsa import (  # noqa: F401
     nsa_attn_bwd_workspace_size,
     nsa_block_sparse_attn,
     nsa_block_sparse_attn_bwd,
+    nsa_curve_order,
+    nsa_permute_tokens,
     nsa_plan_create,
     nsa_pool_blocks,
     nsa_radial_blocks,

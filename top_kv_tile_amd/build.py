@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnsa.so")
-SOURCES = ["nsa_api.cpp", "select_kernels.hip", "attn_kernels.hip", "attn_bwd_kernels.hip"]
+SOURCES = ["nsa_api.cpp", "select_kernels.hip", "attn_kernels.hip", "attn_bwd_kernels.hip", "reorder_kernels.hip"]
 
 # Packed fp32 instructions are kept out of the device code: hipcc -O3 would
 # otherwise form them from plain float code. Matrix-core accumulators are

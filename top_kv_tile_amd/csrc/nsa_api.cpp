@@ -472,6 +472,45 @@ int build_band(int seq_q, int seq_kv, double density, int bq, int bkv, Band& ban
     return NSA_OK;
 }
 
+// ---- curve orders (token reordering) --------------------------------------------
+
+// Morton key: bit b of axis a (a = 0 the fastest, i.e. last, axis) goes to bit
+// b * n + a. Hilbert key: J. Skilling's transpose method ("Programming the
+// Hilbert curve", 2004) on the enclosing 2^p cube, read level by level with
+// the slowest axis giving the high bit of each level.
+uint64_t morton_key(const int64_t* c, int n, int p) {
+    uint64_t key = 0;
+    for (int b = 0; b < p; ++b)
+        for (int a = 0; a < n; ++a) key |= (uint64_t)((c[n - 1 - a] >> b) & 1) << (b * n + a);
+    return key;
+}
+uint64_t hilbert_key(const int64_t* c, int n, int p) {
+    int64_t x[8];
+    for (int i = 0; i < n; ++i) x[i] = c[i];
+    const int64_t top = (int64_t)1 << (p - 1);
+    for (int64_t q = top; q > 1; q >>= 1) {
+        const int64_t low = q - 1;
+        for (int i = 0; i < n; ++i) {
+            if (x[i] & q) {
+                x[0] ^= low;
+            } else {
+                const int64_t t = (x[0] ^ x[i]) & low;
+                x[0] ^= t;
+                x[i] ^= t;
+            }
+        }
+    }
+    for (int i = 1; i < n; ++i) x[i] ^= x[i - 1];
+    int64_t t = 0;
+    for (int64_t q = top; q > 1; q >>= 1)
+        if (x[n - 1] & q) t ^= q - 1;
+    for (int i = 0; i < n; ++i) x[i] ^= t;
+    uint64_t key = 0;
+    for (int b = p - 1; b >= 0; --b)
+        for (int i = 0; i < n; ++i) key = (key << 1) | (uint64_t)((x[i] >> b) & 1);
+    return key;
+}
+
 }  // namespace
 
 // Opaque host-side selection plan: the geometry, the packed pin / drop masks
@@ -731,6 +770,60 @@ int nsa_radial_blocks(int32_t seq_q, int32_t seq_kv, double density, const nsa_s
     } catch (...) {
         return NSA_ERR_UNSUPPORTED;
     }
+}
+
+
+int nsa_curve_order(int32_t kind, int32_t ndim, const int32_t* dims, int32_t* perm) {
+    try {
+        if (!dims) return NSA_ERR_NULL_ARG;
+        if (kind != NSA_CURVE_MORTON && kind != NSA_CURVE_HILBERT) return NSA_ERR_BAD_SPEC;
+        if (ndim < 1 || ndim > 4) return NSA_ERR_UNSUPPORTED;
+        int64_t n = 1, mx = 1;
+        for (int a = 0; a < ndim; ++a) {
+            if (dims[a] < 0) return NSA_ERR_BAD_SHAPE;
+            n *= dims[a];
+            mx = std::max<int64_t>(mx, dims[a]);
+        }
+        if (n >= ((int64_t)1 << 31)) return NSA_ERR_UNSUPPORTED;
+        if (n > 0 && !perm) return NSA_ERR_NULL_ARG;
+        int p = 1;
+        while (((int64_t)1 << p) < mx) ++p;
+        if (p * ndim > 63) return NSA_ERR_UNSUPPORTED;
+        std::vector<std::pair<uint64_t, int32_t>> order((size_t)n);
+        int64_t c[4];
+        for (int64_t r = 0; r < n; ++r) {
+            int64_t rem = r;
+            for (int a = ndim - 1; a >= 0; --a) {
+                c[a] = rem % dims[a];
+                rem /= dims[a];
+            }
+            const uint64_t key = kind == NSA_CURVE_MORTON ? morton_key(c, ndim, p) : hilbert_key(c, ndim, p);
+            order[(size_t)r] = {key, (int32_t)r};
+        }
+        std::sort(order.begin(), order.end());
+        for (int64_t m = 0; m < n; ++m) perm[m] = order[(size_t)m].second;
+        return NSA_OK;
+    } catch (...) {
+        return NSA_ERR_UNSUPPORTED;
+    }
+}
+
+int nsa_permute_tokens(const nsa_tensor* x, const int32_t* perm, int32_t inverse, nsa_tensor* y, void* stream) {
+    int st;
+    if ((st = check_tensor(x)) != NSA_OK) return st;
+    if ((st = check_tensor(y)) != NSA_OK) return st;
+    if (x->dtype != y->dtype) return NSA_ERR_BAD_DTYPE;
+    if (x->B != y->B || x->H != y->H || x->S != y->S || x->D != y->D) return NSA_ERR_BAD_SHAPE;
+    if (numel(x) == 0) return NSA_OK;
+    if (!perm) return NSA_ERR_NULL_ARG;
+    if (x->data == y->data) return NSA_ERR_UNSUPPORTED;  // not in place
+    const int esz = x->dtype == NSA_BF16 ? 2 : 4;
+    const int row_bytes = x->D * esz;
+    if (row_bytes < 64 || row_bytes > 1024 || (row_bytes & (row_bytes - 1))) return NSA_ERR_UNSUPPORTED;
+    if (((uintptr_t)x->data & 15) || ((uintptr_t)y->data & 15)) return NSA_ERR_UNSUPPORTED;
+    const hipError_t e = nsa::launch_permute_rows(x->data, perm, inverse ? 1 : 0, (int64_t)x->B * x->H, x->S,
+                                                  row_bytes, y->data, (hipStream_t)stream);
+    return e == hipSuccess ? NSA_OK : hip_fail(e);
 }
 
 int nsa_selection_density(const nsa_selection* sel, double* out) {

@@ -95,4 +95,11 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t stream);
 // General path (fp32 or bf16, any block sizes, D in {64, 128}).
 hipError_t launch_attn_bwd_simt(const AttnBwdArgs& a, int bf16, hipStream_t stream);
 
+// ---- token reordering --------------------------------------------------------
+
+// y[bh, m] = x[bh, perm[m]] (inverse = 0) or y[bh, perm[m]] = x[bh, m] (inverse = 1)
+// for `slabs` slabs of S rows of row_bytes bytes (a multiple of 16, at most 1024).
+hipError_t launch_permute_rows(const void* x, const int32_t* perm, int inverse, int64_t slabs, int S,
+                               int row_bytes, void* y, hipStream_t stream);
+
 }  // namespace nsa

@@ -22,17 +22,20 @@ __all__ = [
     "SparseSpec", "Selection", "Sizes", "NsaError", "lib", "nsa_select_sizes", "nsa_select",
     "nsa_block_sparse_attn", "nsa_block_sparse_attn_bwd", "nsa_attn_bwd_workspace_size",
     "nsa_pool_blocks", "nsa_score_blocks", "nsa_status_string", "Plan", "nsa_plan_create",
-    "nsa_select_planned", "nsa_schedule", "nsa_radial_blocks", "nsa_selection_density", "LIB_PATH", "EXPORTS",
+    "nsa_select_planned", "nsa_schedule", "nsa_radial_blocks", "nsa_selection_density", "nsa_curve_order",
+    "nsa_permute_tokens", "NSA_CURVE_MORTON", "NSA_CURVE_HILBERT", "LIB_PATH", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnsa.so")
 EXPORTS = ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_attn_bwd_workspace_size",
            "nsa_block_sparse_attn_bwd", "nsa_pool_blocks", "nsa_score_blocks", "nsa_status_string",
            "nsa_last_hip_error", "nsa_version", "nsa_plan_create", "nsa_plan_sizes", "nsa_select_planned",
-           "nsa_plan_destroy", "nsa_schedule", "nsa_radial_sizes", "nsa_radial_blocks", "nsa_selection_density")
+           "nsa_plan_destroy", "nsa_schedule", "nsa_radial_sizes", "nsa_radial_blocks", "nsa_selection_density",
+           "nsa_curve_order", "nsa_permute_tokens")
 
 NSA_OK, NSA_DENSE = 0, 1
 NSA_F32, NSA_BF16 = 0, 1
+NSA_CURVE_MORTON, NSA_CURVE_HILBERT = 0, 1
 
 
 class NsaError(RuntimeError):
@@ -109,13 +112,15 @@ def lib() -> ctypes.CDLL:
         L.nsa_radial_blocks.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_double, P(_Spec), P(_Selection),
                                         ctypes.c_void_p]
         L.nsa_selection_density.argtypes = [P(_Selection), P(ctypes.c_double)]
+        L.nsa_curve_order.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        L.nsa_permute_tokens.argtypes = [P(_Tensor), ctypes.c_void_p, ctypes.c_int32, P(_Tensor), ctypes.c_void_p]
         L.nsa_status_string.argtypes = [ctypes.c_int]
         L.nsa_status_string.restype = ctypes.c_char_p
         L.nsa_version.restype = ctypes.c_char_p
         for name in ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_attn_bwd_workspace_size",
                      "nsa_block_sparse_attn_bwd", "nsa_pool_blocks", "nsa_score_blocks", "nsa_last_hip_error",
                      "nsa_plan_create", "nsa_plan_sizes", "nsa_select_planned", "nsa_schedule", "nsa_radial_sizes",
-                     "nsa_radial_blocks", "nsa_selection_density"):
+                     "nsa_radial_blocks", "nsa_selection_density", "nsa_curve_order", "nsa_permute_tokens"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -404,3 +409,24 @@ def nsa_selection_density(sel: Selection) -> float:
     d = ctypes.c_double()
     _check(lib().nsa_selection_density(ctypes.byref(sel._c()), ctypes.byref(d)), "nsa_selection_density")
     return d.value
+
+
+def nsa_curve_order(kind, dims) -> np.ndarray:
+    """perm[m] = raster index of the m-th grid point along the curve (NSA_CURVE_MORTON / NSA_CURVE_HILBERT)."""
+    d = np.ascontiguousarray(np.asarray(dims, dtype=np.int32))
+    n = int(np.prod(d.astype(np.int64))) if d.size else 0
+    perm = np.empty(max(n, 1), np.int32)
+    _check(lib().nsa_curve_order(int(kind), int(d.size), d.ctypes.data, perm.ctypes.data), "nsa_curve_order")
+    return perm[:n]
+
+
+def nsa_permute_tokens(x: torch.Tensor, perm: torch.Tensor, inverse: bool = False, out: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """Token rows gathered along perm (inverse=False) or scattered back (inverse=True)."""
+    if perm.dtype != torch.int32 or not perm.is_contiguous():
+        raise ValueError("perm must be contiguous int32")
+    y = torch.empty_like(x) if out is None else out
+    _check(lib().nsa_permute_tokens(ctypes.byref(_tensor(x)), ctypes.c_void_p(perm.data_ptr() if perm.numel() else 0),
+                                    int(bool(inverse)), ctypes.byref(_tensor(y)), _stream(stream)),
+           "nsa_permute_tokens")
+    return y

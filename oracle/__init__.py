@@ -35,3 +35,4 @@ from .attention import attention, attention_dense_literal, visible_key_counts  #
 from .attention_bwd import attention_backward  # noqa: F401
 from .controls import schedule, radial_blocks, density  # noqa: F401
 from .reorder import morton_order, hilbert_order, apply_order, undo_order  # noqa: F401
+from .decode import decode_pool, decode_select, decode_attention  # noqa: F401

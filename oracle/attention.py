@@ -50,19 +50,23 @@ def _row(qt, kk, vv, causal, q_pos, k_pos, scale):
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep, block_q: int,
-              block_kv: int, causal: bool, rows=None):
+              block_kv: int, causal: bool, rows=None, q_offset=None):
     """Block-sparse attention in fp64 over the kept tiles.
 
     q: (B, Hq, S, D); k, v: (B, Hkv, S, D) CPU tensors (fp32 or bf16).
     keep: int8/bool (B, H', NQ, NK) with H' in {1, Hq}, or None for dense (all tiles).
     rows: optional iterable of (b, h, i) query rows to evaluate (others stay
     NaN in the output); default all rows.
+    q_offset (decode reading, not on the pages): query t sits at absolute key
+    position q_offset + t, so causal visibility is u <= q_offset + t; seq_q and
+    seq_kv may then differ. None keeps the top-left alignment with seq_q == seq_kv.
     Returns (O fp64 (B, Hq, S, D), LSE fp64 (B, Hq, S)) as numpy arrays.
     """
     bsz, hq, seq_q, d = q.shape
     hkv, seq_kv = k.shape[1], k.shape[2]
-    if causal and seq_q != seq_kv:
+    if causal and seq_q != seq_kv and q_offset is None:
         raise ValueError("causal attention needs seq_q == seq_kv")
+    off = 0 if q_offset is None else int(q_offset)
     nq = -(-seq_q // block_q)
     nk = -(-seq_kv // block_kv)
     if keep is None:
@@ -88,7 +92,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep, block_q: 
         qt = q[b, h, t0:t1].to(torch.float64).numpy()
         kk = k[b, g, k_pos].to(torch.float64).numpy()
         vv = v[b, g, k_pos].to(torch.float64).numpy()
-        o, l = _row(qt, kk, vv, causal, np.arange(t0, t1), k_pos, scale)
+        o, l = _row(qt, kk, vv, causal, off + np.arange(t0, t1), k_pos, scale)
         out[b, h, t0:t1] = o
         lse[b, h, t0:t1] = l
     return out, lse

@@ -78,17 +78,21 @@ def pool_blocks(x: torch.Tensor, block: int) -> torch.Tensor:
     return out
 
 
-def diagonal_blocks(nq: int, nk: int, block_q: int, block_kv: int) -> np.ndarray:
+def diagonal_blocks(nq: int, nk: int, block_q: int, block_kv: int, q_offset: int = 0) -> np.ndarray:
     """Boolean (nq, nk): query tile i and kv tile j cover intersecting token ranges.
 
     selector.py, ``diagonal_blocks``: tile i spans tokens [i*bq, (i+1)*bq) and
     tile j spans [j*bkv, (j+1)*bkv) (unclipped); the pair is on the diagonal when
     each range starts before the other ends. Keeping these tiles guarantees
     every query row keeps at least one tile.
+
+    ``q_offset`` (decode reading, not on the page): the query tokens sit at
+    absolute positions q_offset + t of the key sequence, so tile i spans
+    [q_offset + i*bq, q_offset + (i+1)*bq). 0 is the page's alignment.
     """
     i = np.arange(nq, dtype=np.int64)[:, None]
     j = np.arange(nk, dtype=np.int64)[None, :]
-    return (i * block_q < (j + 1) * block_kv) & (j * block_kv < (i + 1) * block_q)
+    return (q_offset + i * block_q < (j + 1) * block_kv) & (j * block_kv < q_offset + (i + 1) * block_q)
 
 
 def head_operands(pooled_q: torch.Tensor, pooled_k: torch.Tensor, head_shared: bool):
@@ -154,7 +158,7 @@ def keep_per_row(candidates_per_row: np.ndarray, budget: float) -> np.ndarray:
 
 
 def selection_plan(nq: int, nk: int, block_q: int, block_kv: int, budget: float,
-                   batch: int, heads: int, pins=None, drops=None):
+                   batch: int, heads: int, pins=None, drops=None, q_offset: int = 0):
     """What must be kept, what may be chosen and how many, from geometry and masks only.
 
     selector.py, ``selection_plan``:
@@ -168,7 +172,7 @@ def selection_plan(nq: int, nk: int, block_q: int, block_kv: int, budget: float,
     Returns a dict of numpy arrays broadcast to (B, H', NQ, NK) / (B, H', NQ).
     """
     shape4 = (batch, heads, nq, nk)
-    must = np.broadcast_to(diagonal_blocks(nq, nk, block_q, block_kv), shape4)
+    must = np.broadcast_to(diagonal_blocks(nq, nk, block_q, block_kv, q_offset), shape4)
     p = _as_mask(pins, shape4)
     if p is not None:
         must = must | p
@@ -184,7 +188,7 @@ def selection_plan(nq: int, nk: int, block_q: int, block_kv: int, budget: float,
 
 def select_blocks(q: torch.Tensor, k: torch.Tensor, budget: float = 0.30, block_q: int = 128,
                   block_kv: int = 64, head_shared: bool = False, force: bool = False,
-                  pins=None, drops=None):
+                  pins=None, drops=None, q_offset: int = 0):
     """Per query tile: the diagonal, the pins and the top-``k_r`` candidates, minus drops.
 
     selector.py, ``select_blocks``. q: (B, Hq, Sq, D), k: (B, Hkv, Skv, D), CPU
@@ -203,7 +207,7 @@ def select_blocks(q: torch.Tensor, k: torch.Tensor, budget: float = 0.30, block_
     seq_kv = k.shape[-2]
     nq, nk = block_count(seq_q, block_q), block_count(seq_kv, block_kv)
     heads = 1 if head_shared else hq
-    plan = selection_plan(nq, nk, block_q, block_kv, budget, bsz, heads, pins, drops)
+    plan = selection_plan(nq, nk, block_q, block_kv, budget, bsz, heads, pins, drops, q_offset)
     if plan["dense"] and not force:
         return None
 

@@ -239,6 +239,47 @@ int nsa_curve_order(int32_t kind, int32_t ndim, const int32_t* dims, int32_t* pe
 int nsa_permute_tokens(const nsa_tensor* x, const int32_t* perm, int32_t inverse, nsa_tensor* y,
                        void* stream);
 
+/* ---- Decoding over a KV cache ------------------------------------------------
+ * The inference pathways of "todo" (native-sparse-attention-pytorch issue #1):
+ * a running pooled key sequence, the importance score of the new query tokens
+ * and attention over only the selected blocks of the cache. Reading (the
+ * selection page aligns queries at position 0): n new query tokens sit at
+ * absolute positions q_pos0 .. q_pos0 + n - 1 of the cache, q_pos0 + n <=
+ * length; query tiles are counted from q_pos0, the diagonal is measured at the
+ * queries' absolute positions, and attention is causal in absolute positions. */
+
+/* Keeps pooled (B, Hkv, tiles_capacity, D) fp32 equal to pool_blocks of the
+ * first len_new tokens of k_cache (B, Hkv, capacity, D), given that it held
+ * those of the first len_old: only the kv tiles holding a new token are
+ * recomputed (each averaged over its real length). 0 <= len_old <= len_new
+ * <= capacity; ceil(len_new / block_kv) <= tiles_capacity. Errors: BAD_SHAPE,
+ * BAD_SPEC, BAD_DTYPE, NULL_ARG, UNSUPPORTED (D), HIP. */
+int nsa_decode_pool_update(const nsa_tensor* k_cache, int32_t len_old, int32_t len_new, int32_t block_kv,
+                           float* pooled, int32_t tiles_capacity, void* stream);
+
+/* Host only. Sizes of nsa_decode_select (as nsa_select_sizes); pins / drops
+ * are (1|B, 1|H', ceil(n / block_q), ceil(length / block_kv)). */
+int nsa_decode_select_sizes(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t length, int32_t q_pos0,
+                            const nsa_spec* spec, const nsa_mask* pins, const nsa_mask* drops,
+                            nsa_sizes* out, int32_t* row_ptr_host);
+
+/* select_blocks for the new query tokens q (B, Hq, n, D) against the first
+ * `length` cached keys, whose pooled means are pooled_k (F32 nsa_tensor
+ * (B, Hkv, tiles_capacity, D), kept by nsa_decode_pool_update). Outputs,
+ * workspace, NSA_DENSE and errors as nsa_select; the selection records
+ * seq_q = n and seq_kv = length. */
+int nsa_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t length, int32_t q_pos0,
+                      const nsa_spec* spec, const nsa_mask* pins, const nsa_mask* drops, nsa_selection* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention of the new query tokens q (B, Hq, n, D) over the kept tiles of the
+ * first `length` keys of k_cache / v_cache (B, Hkv, capacity, D): key u is
+ * visible to query t iff its tile is kept and u <= q_pos0 + t. sel from
+ * nsa_decode_select, or NULL for every tile. out (B, Hq, n, D), lse (B, Hq, n)
+ * as nsa_block_sparse_attn. Errors as nsa_block_sparse_attn. */
+int nsa_decode_attn(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa_tensor* v_cache, int32_t length,
+                    int32_t q_pos0, const nsa_selection* sel, nsa_tensor* out, float* lse, void* stream);
+
 /* Device workspace, in bytes, that nsa_block_sparse_attn_bwd needs for these
  * shapes and this selection (sel may be NULL for dense). Host only. */
 int nsa_attn_bwd_workspace_size(const nsa_tensor* q, const nsa_tensor* k, const nsa_selection* sel,

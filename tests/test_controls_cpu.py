@@ -138,3 +138,52 @@ def test_permute_validation(L):
     odd = N._Tensor(16, N.NSA_BF16, 1, 2, 16, 48)
     assert L.nsa_permute_tokens(ctypes.byref(odd), 1, 0, ctypes.byref(N._Tensor(32, N.NSA_BF16, 1, 2, 16, 48)),
                                 None) == -4
+
+
+def _dec_sizes(L, q, pk, length, pos0, spec, pins=None, drops=None, row_ptr=None):
+    hold = []
+    out = N._Sizes()
+    st = L.nsa_decode_select_sizes(ctypes.byref(q), ctypes.byref(pk), length, pos0, ctypes.byref(spec._c()),
+                                   N._mask(pins, hold), N._mask(drops, hold), ctypes.byref(out),
+                                   row_ptr.ctypes.data if row_ptr is not None else None)
+    return st, out
+
+
+@pytest.mark.parametrize("n,length,bq,bkv,budget", [(1, 1000, 128, 64, 0.3), (5, 4097, 128, 64, 0.05),
+                                                    (64, 700, 32, 64, 0.25), (1, 1, 128, 64, 0.3)])
+def test_decode_plan_matches_oracle(L, n, length, bq, bkv, budget):
+    B, Hq, Hkv, D = 1, 4, 2, 128
+    q = N._Tensor(1, N.NSA_BF16, B, Hq, n, D)
+    pk = N._Tensor(1, N.NSA_F32, B, Hkv, 4096, D)
+    pos0 = length - n
+    nq, nk = -(-n // bq), -(-length // bkv)
+    spec = tkt.SparseSpec(budget=budget, block_q=bq, block_kv=bkv, force=True)
+    row_ptr = np.zeros(B * Hq * nq + 1, np.int32)
+    st, out = _dec_sizes(L, q, pk, length, pos0, spec, row_ptr=row_ptr)
+    assert st == 0
+    plan = oracle.selection_plan(nq, nk, bq, bkv, budget, B, Hq, q_offset=pos0)
+    counts = (plan["must"] & ~plan["forbidden"]).sum(-1) + np.minimum(plan["k"], plan["c"])
+    assert (out.NQ, out.NK) == (nq, nk)
+    assert np.array_equal(row_ptr, np.concatenate([[0], np.cumsum(counts.reshape(-1))]))
+
+
+def test_decode_validation(L):
+    q = N._Tensor(1, N.NSA_BF16, 1, 4, 2, 128)
+    pk = N._Tensor(1, N.NSA_F32, 1, 2, 16, 128)
+    spec = tkt.SparseSpec()
+    assert _dec_sizes(L, q, pk, 1000, 998, spec)[0] == 0
+    assert _dec_sizes(L, q, pk, 1000, 999, spec)[0] == -2          # queries past the cache
+    assert _dec_sizes(L, q, pk, 1025, 1000, spec)[0] == -2         # 17 tiles > 16 pooled
+    assert _dec_sizes(L, q, N._Tensor(1, N.NSA_BF16, 1, 2, 16, 128), 1000, 998, spec)[0] == -3
+    assert _dec_sizes(L, q, N._Tensor(1, N.NSA_F32, 1, 3, 16, 128), 1000, 998, spec)[0] == -2
+    kc = N._Tensor(1, N.NSA_BF16, 1, 2, 512, 128)
+    assert L.nsa_decode_pool_update(ctypes.byref(kc), 10, 5, 64, 1, 8, None) == -2
+    assert L.nsa_decode_pool_update(ctypes.byref(kc), 0, 513, 64, 1, 9, None) == -2
+    assert L.nsa_decode_pool_update(ctypes.byref(kc), 0, 512, 64, 1, 7, None) == -2
+    assert L.nsa_decode_pool_update(ctypes.byref(kc), 0, 512, 0, 1, 8, None) == -6
+    assert L.nsa_decode_pool_update(ctypes.byref(kc), 7, 7, 64, None, 8, None) == 0   # nothing appended
+    out = N._Tensor(1, N.NSA_BF16, 1, 4, 2, 128)
+    A = L.nsa_decode_attn
+    assert A(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(kc), 600, 100, None, ctypes.byref(out), 1, None) == -2
+    assert A(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(kc), 500, 499, None, ctypes.byref(out), 1, None) == -2
+    assert A(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(kc), 500, 10, None, ctypes.byref(out), None, None) == -1

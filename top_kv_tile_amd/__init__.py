@@ -19,6 +19,9 @@ from .nsa import (  # noqa: F401
     nsa_block_sparse_attn,
     nsa_block_sparse_attn_bwd,
     nsa_curve_order,
+    nsa_decode_attn,
+    nsa_decode_pool_update,
+    nsa_decode_select,
     nsa_permute_tokens,
     nsa_plan_create,
     nsa_pool_blocks,

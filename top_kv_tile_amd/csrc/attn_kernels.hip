@@ -22,6 +22,7 @@
 #include "nsa_internal.h"
 #include "device_common.h"
 
+#include <algorithm>
 #include <float.h>
 #include <math.h>
 
@@ -70,9 +71,9 @@ __device__ __forceinline__ Work decode_work(int64_t n, int64_t total, int Hq, in
     return wk;
 }
 
-// Range [start, end) of CSR entries to visit for query rows up to q_last
-// (inclusive). Column lists are ascending, so under causal the visited prefix
-// ends at the first tile that starts after q_last.
+// Range [start, end) of CSR entries to visit for query rows up to absolute key
+// position q_last (inclusive). Column lists are ascending, so under causal the
+// visited prefix ends at the first tile that starts after q_last.
 __device__ __forceinline__ void tile_range(const AttnArgs& a, int b, int h, int i, int q_last, int& start,
                                            int& end) {
     if (a.row_ptr) {
@@ -149,11 +150,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     // Per-head buffer resources: 32-bit offsets, and reads past the end of the
     // head return zeros (ragged tails need no branches). The host guarantees
     // (S + 64) * D * 2 < 2^31.
-    const int head_bytes = a.S * G::ROWB;
+    const int head_bytes = a.S * G::ROWB;          // one query head
+    const int kv_bytes = a.Skv * G::ROWB;          // the keys of one kv head
     const __amdgpu_buffer_rsrc_t qrs =
         make_rsrc((const uint16_t*)a.q + (((int64_t)wk.b * a.Hq + wk.h) * a.S) * D, head_bytes);
-    const u32x4 krs = rsrc_words((const uint16_t*)a.k + (((int64_t)wk.b * a.Hkv + wk.g) * a.S) * D, head_bytes);
-    const u32x4 vrs = rsrc_words((const uint16_t*)a.v + (((int64_t)wk.b * a.Hkv + wk.g) * a.S) * D, head_bytes);
+    const u32x4 krs = rsrc_words((const uint16_t*)a.k + ((int64_t)wk.b * a.Hkv + wk.g) * a.kv_rows * D, kv_bytes);
+    const u32x4 vrs = rsrc_words((const uint16_t*)a.v + ((int64_t)wk.b * a.Hkv + wk.g) * a.kv_rows * D, kv_bytes);
 
     // Q^T operand: lane holds q[qrow][16*ks + 8*hf .. +8] for every ks (zeros past S).
     bf16x8 qf[KSTEPS];
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     }
 
     int e_begin, e_end;
-    tile_range(a, wk.b, wk.h, wk.i, q_last, e_begin, e_end);
+    tile_range(a, wk.b, wk.h, wk.i, a.q_off + q_last, e_begin, e_end);
     const int ntiles = e_end - e_begin;
 
     // The row's kv-tile indices, 64 at a time: lane x holds entry base + x and
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
             if (G::NINSTR % NW == 0 || ii < G::NINSTR) {
                 const int row = ii * G::RPI + lane / G::CH, pc = lane % G::CH;
                 const int chunk = pc ^ (is_v ? G::vswz(row) : G::kswz(row));
-                const int off = min(key0 + row, a.S - 1) * G::ROWB + chunk * 16;
+                const int off = min(key0 + row, a.Skv - 1) * G::ROWB + chunk * 16;
                 dma16(rs, base + ii * 1024, off);
             }
         }
@@ -232,10 +234,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     // Masks of a partial tile (causal diagonal or ragged tail): keys past the
     // lane's query row or past S get -inf. Only partial tiles take this branch.
     auto mask_tile = [&](f32x16 (&sacc)[2], int key0) {
-        const bool need_mask = (a.causal && key0 + BKV - 1 > qw0) || (key0 + BKV > a.S);
+        const bool need_mask = (a.causal && key0 + BKV - 1 > a.q_off + qw0) || (key0 + BKV > a.Skv);
         if (need_mask) {
-            int lim = min(BKV - 1, a.S - 1 - key0);           // last visible key offset
-            if (a.causal) lim = min(lim, qrow - key0);
+            int lim = min(BKV - 1, a.Skv - 1 - key0);         // last visible key offset
+            if (a.causal) lim = min(lim, a.q_off + qrow - key0);
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -415,7 +417,7 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a) {
     };
     (void)qbase;
     (void)esz;
-    const int64_t kvoff = ((int64_t)wk.b * a.Hkv + wk.g) * a.S * D;
+    const int64_t kvoff = ((int64_t)wk.b * a.Hkv + wk.g) * a.kv_rows * D;
     const int64_t qoff = ((int64_t)wk.b * a.Hq + wk.h) * a.S * D;
 
     for (int rc = q_tile0; rc < q_tile_end; rc += 128) {
@@ -431,13 +433,13 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a) {
         }
         float m_run = kNegInf, l_run = 0.f;
         int e_begin, e_end;
-        tile_range(a, wk.b, wk.h, wk.i, chunk_last, e_begin, e_end);
+        tile_range(a, wk.b, wk.h, wk.i, a.q_off + chunk_last, e_begin, e_end);
         for (int e = e_begin; e < e_end; ++e) {
             const int j = a.row_ptr ? a.col_idx[e] : e;
             const int kt0 = j * a.block_kv;
-            const int kt1 = min(kt0 + a.block_kv, a.S);
+            const int kt1 = min(kt0 + a.block_kv, a.Skv);
             for (int kc = kt0; kc < kt1; kc += KC) {
-                if (a.causal && kc > chunk_last) break;
+                if (a.causal && kc > a.q_off + chunk_last) break;
                 const int nkeys = min(KC, kt1 - kc);
                 __syncthreads();
                 for (int x = tid; x < KC * D; x += 256) {
@@ -457,7 +459,7 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a) {
                     dot += __shfl_xor(dot, 1);
                     float x = dot * a.scale_log2;
                     const int key = kc + kr;
-                    if (kr >= nkeys || (a.causal && key > row)) x = kNegInf;
+                    if (kr >= nkeys || (a.causal && key > a.q_off + row)) x = kNegInf;
                     sv[kr] = x;
                     mx = fmaxf(mx, x);
                 }
@@ -501,7 +503,7 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a) {
 
 bool attn_mfma_supported(const AttnArgs& a, int bf16) {
     // Buffer offsets are 32-bit: one head plus a tile of slack must stay below 2^31 bytes.
-    const bool fits = ((int64_t)a.S + 64) * a.D * 2 < ((int64_t)1 << 31);
+    const bool fits = ((int64_t)std::max(a.S, a.Skv) + 64) * a.D * 2 < ((int64_t)1 << 31);
     return bf16 && fits && a.block_kv == 64 && a.block_q % 32 == 0 && a.block_q >= 32 && a.block_q <= 128 &&
            (a.D == 64 || a.D == 128);
 }

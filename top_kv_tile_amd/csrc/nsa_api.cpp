@@ -44,6 +44,7 @@ struct Geo {
     int B, Hq, Hkv, Sq, Skv, D, NQ, NK, NKW, Hsel, group;
     int bf16;
     int64_t rows;
+    int64_t q_off = 0;  // absolute key position of query token 0 (decoding); 0 otherwise
 };
 
 int check_spec(const nsa_spec* s) {
@@ -160,10 +161,10 @@ int build_plan(const Geo& g, const nsa_spec* spec, const nsa_mask* pins, const n
             if (slab_key[x] == key) return slab_counts[x];
         std::vector<int32_t> cnt(g.NQ);
         for (int i = 0; i < g.NQ; ++i) {
-            // diagonal: kv tiles j with i*bq < (j+1)*bkv and j*bkv < (i+1)*bq
-            const int64_t lo = ((int64_t)i * spec->block_q) / spec->block_kv;
+            // diagonal: kv tiles j with o + i*bq < (j+1)*bkv and j*bkv < o + (i+1)*bq (o = q_off)
+            const int64_t lo = (g.q_off + (int64_t)i * spec->block_q) / spec->block_kv;
             const int64_t hi = std::min<int64_t>(
-                ceil_div((int64_t)(i + 1) * spec->block_q, spec->block_kv) - 1, g.NK - 1);
+                ceil_div(g.q_off + (int64_t)(i + 1) * spec->block_q, spec->block_kv) - 1, g.NK - 1);
             std::fill(diag.begin(), diag.end(), 0ull);
             for (int64_t j = lo; j <= hi; ++j) diag[j >> 6] |= 1ull << (j & 63);
             const uint64_t* pw = pins ? p.pin_words.data() + ((int64_t)ps * g.NQ + i) * g.NKW : nullptr;
@@ -211,7 +212,7 @@ struct WsLayout {
 };
 
 WsLayout ws_layout(const Geo& g, const nsa_spec* spec, bool has_pins, int pin_slabs, bool has_drops,
-                   int drop_slabs) {
+                   int drop_slabs, bool external_k = false) {
     WsLayout w;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -220,7 +221,7 @@ WsLayout ws_layout(const Geo& g, const nsa_spec* spec, bool has_pins, int pin_sl
         return o;
     };
     w.pq = take((size_t)g.B * g.Hq * g.NQ * g.D * 4);
-    w.pk = take((size_t)g.B * g.Hkv * g.NK * g.D * 4);
+    w.pk = external_k ? 0 : take((size_t)g.B * g.Hkv * g.NK * g.D * 4);
     if (spec->head_shared) {
         w.mq = take((size_t)g.B * g.NQ * g.D * 4);
         w.mk = take((size_t)g.B * g.NK * g.D * 4);
@@ -343,6 +344,9 @@ void fill_sizes(const Plan& p, const nsa_spec* spec, nsa_sizes* out, int32_t* ro
     if (row_ptr_host) std::memcpy(row_ptr_host, p.row_ptr.data(), p.row_ptr.size() * sizeof(int32_t));
 }
 
+int score_and_topk(const Plan& p, const nsa_spec* spec, const float* qh, const float* kh, int Hk, int NKs,
+                   const WsLayout& w, char* ws, nsa_selection* out, hipStream_t stream);
+
 // Enqueues the selection of a built plan (row_ptr present) for tensors q, k
 // whose geometry the plan was built from.
 int run_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, const Plan& p, nsa_selection* out,
@@ -384,11 +388,18 @@ int run_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, c
     int Hk;
     int st;
     if ((st = run_pool(q, k, spec, g, w, ws, stream, &qh, &kh, &Hk)) != NSA_OK) return st;
+    return score_and_topk(p, spec, qh, kh, Hk, g.NK, w, ws, out, stream);
+}
+
+// Scores chunk by chunk of selection heads, each followed by its top-k and CSR.
+int score_and_topk(const Plan& p, const nsa_spec* spec, const float* qh, const float* kh, int Hk, int NKs,
+                   const WsLayout& w, char* ws, nsa_selection* out, hipStream_t stream) {
+    const Geo& g = p.g;
     float* scores = (float*)(ws + w.scores);
     for (int h0 = 0; h0 < g.Hsel; h0 += w.chunk) {
         const int nh = std::min(w.chunk, g.Hsel - h0);
         hipError_t e = nsa::launch_scores(qh, kh, g.B, g.Hsel, Hk, g.group, h0, nh, g.NQ, g.NK, g.D, scores,
-                                          stream);
+                                          stream, NKs);
         if (e != hipSuccess) return hip_fail(e);
         nsa::TopkArgs ta;
         ta.scores = scores;
@@ -401,6 +412,7 @@ int run_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, c
         ta.NKW = g.NKW;
         ta.block_q = spec->block_q;
         ta.block_kv = spec->block_kv;
+        ta.q_off = g.q_off;
         ta.budget = spec->budget;
         ta.pin_words = p.has_pins ? (const uint64_t*)(ws + w.pinw) : nullptr;
         ta.pb = p.pb;
@@ -414,6 +426,46 @@ int run_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, c
         if ((e = nsa::launch_topk(ta, stream)) != hipSuccess) return hip_fail(e);
     }
     return NSA_OK;
+}
+
+// ---- decoding -------------------------------------------------------------------
+
+// Geometry of a decode-time selection: n query tokens q (B, Hq, n, D) at
+// absolute positions q_pos0 .. q_pos0 + n - 1 against the first `length`
+// cached keys, whose pooled means are in pooled_k (B, Hkv, capacity, D) fp32.
+int validate_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t length, int32_t q_pos0,
+                           const nsa_spec* spec, const nsa_mask* pins, const nsa_mask* drops, Geo& g) {
+    int st;
+    if ((st = check_tensor(q)) != NSA_OK) return st;
+    if ((st = check_tensor(pooled_k)) != NSA_OK) return st;
+    if ((st = check_spec(spec)) != NSA_OK) return st;
+    if (pooled_k->dtype != NSA_F32) return NSA_ERR_BAD_DTYPE;
+    if (q->B != pooled_k->B || q->D != pooled_k->D || q->H % pooled_k->H != 0) return NSA_ERR_BAD_SHAPE;
+    if (length < 0 || q_pos0 < 0 || (int64_t)q_pos0 + q->S > length) return NSA_ERR_BAD_SHAPE;
+    g.B = q->B;
+    g.Hq = q->H;
+    g.Hkv = pooled_k->H;
+    g.Sq = q->S;
+    g.Skv = length;
+    g.D = q->D;
+    g.NQ = (int)ceil_div(q->S, spec->block_q);
+    g.NK = (int)ceil_div(length, spec->block_kv);
+    g.NKW = (int)ceil_div(g.NK, 64);
+    g.Hsel = spec->head_shared ? 1 : q->H;
+    g.group = q->H / pooled_k->H;
+    g.bf16 = q->dtype == NSA_BF16;
+    g.rows = (int64_t)g.B * g.Hsel * g.NQ;
+    g.q_off = q_pos0;
+    if (g.NK > pooled_k->S) return NSA_ERR_BAD_SHAPE;  // the cache of pooled keys is too short
+    if ((st = check_mask(pins, g)) != NSA_OK) return st;
+    if ((st = check_mask(drops, g)) != NSA_OK) return st;
+    if (g.D != 64 && g.D != 128 && g.D != 256) return NSA_ERR_UNSUPPORTED;
+    if (g.NK > 4096) return NSA_ERR_UNSUPPORTED;
+    return NSA_OK;
+}
+
+WsLayout decode_layout(const Plan& p, const nsa_spec* spec) {
+    return ws_layout(p.g, spec, p.has_pins, p.pb * p.ph, p.has_drops, p.db * p.dh, true);
 }
 
 // ---- radial band (radial_blocks of the selection page) -------------------------
@@ -826,6 +878,171 @@ int nsa_permute_tokens(const nsa_tensor* x, const int32_t* perm, int32_t inverse
     return e == hipSuccess ? NSA_OK : hip_fail(e);
 }
 
+
+int nsa_decode_pool_update(const nsa_tensor* k_cache, int32_t len_old, int32_t len_new, int32_t block_kv,
+                           float* pooled, int32_t tiles_capacity, void* stream) {
+    int st;
+    if ((st = check_tensor(k_cache)) != NSA_OK) return st;
+    if (block_kv <= 0) return NSA_ERR_BAD_SPEC;
+    if (len_old < 0 || len_new < len_old || len_new > k_cache->S) return NSA_ERR_BAD_SHAPE;
+    if (ceil_div(len_new, block_kv) > tiles_capacity) return NSA_ERR_BAD_SHAPE;
+    if (k_cache->D != 64 && k_cache->D != 128 && k_cache->D != 256) return NSA_ERR_UNSUPPORTED;
+    if (len_new == len_old || (int64_t)k_cache->B * k_cache->H == 0) return NSA_OK;
+    if (!pooled) return NSA_ERR_NULL_ARG;
+    // Tiles holding a new token: from the one containing len_old to the last.
+    const int t0 = len_old / block_kv;
+    const int t1 = (int)ceil_div(len_new, block_kv);
+    const hipError_t e = nsa::launch_pool_range(k_cache->data, k_cache->dtype == NSA_BF16,
+                                                (int64_t)k_cache->B * k_cache->H, len_new, k_cache->S, k_cache->D,
+                                                block_kv, t0, t1 - t0, pooled, tiles_capacity, (hipStream_t)stream);
+    return e == hipSuccess ? NSA_OK : hip_fail(e);
+}
+
+int nsa_decode_select_sizes(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t length, int32_t q_pos0,
+                            const nsa_spec* spec, const nsa_mask* pins, const nsa_mask* drops, nsa_sizes* out,
+                            int32_t* row_ptr_host) {
+    try {
+        if (!out) return NSA_ERR_NULL_ARG;
+        Geo g;
+        int st = validate_decode_select(q, pooled_k, length, q_pos0, spec, pins, drops, g);
+        if (st != NSA_OK) return st;
+        Plan p;
+        if ((st = build_plan(g, spec, pins, drops, p, row_ptr_host != nullptr)) != NSA_OK) return st;
+        fill_sizes(p, spec, out, row_ptr_host);
+        out->workspace_bytes = (int64_t)decode_layout(p, spec).total;
+        return NSA_OK;
+    } catch (...) {
+        return NSA_ERR_UNSUPPORTED;
+    }
+}
+
+int nsa_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t length, int32_t q_pos0,
+                      const nsa_spec* spec, const nsa_mask* pins, const nsa_mask* drops, nsa_selection* out,
+                      void* workspace, size_t workspace_bytes, void* stream_) {
+    try {
+        hipStream_t stream = (hipStream_t)stream_;
+        if (!out) return NSA_ERR_NULL_ARG;
+        Geo g;
+        int st = validate_decode_select(q, pooled_k, length, q_pos0, spec, pins, drops, g);
+        if (st != NSA_OK) return st;
+        Plan p;
+        if ((st = build_plan(g, spec, pins, drops, p, true)) != NSA_OK) return st;
+        if (p.dense && !spec->force) return NSA_DENSE;
+        if (g.rows > 0 && (!out->keep || !out->row_ptr)) return NSA_ERR_NULL_ARG;
+        if (!out->row_ptr) return NSA_ERR_NULL_ARG;
+        if (p.nnz > 0 && !out->col_idx) return NSA_ERR_NULL_ARG;
+        if (out->col_capacity < p.nnz) return NSA_ERR_CAPACITY;
+        const WsLayout w = decode_layout(p, spec);
+        if (workspace_bytes < w.total) return NSA_ERR_WORKSPACE;
+        if (w.total > 0 && (!workspace || ((uintptr_t)workspace & 255))) return NSA_ERR_WORKSPACE;
+        out->nnz = p.nnz;
+        out->B = g.B;
+        out->H = g.Hsel;
+        out->NQ = g.NQ;
+        out->NK = g.NK;
+        out->block_q = spec->block_q;
+        out->block_kv = spec->block_kv;
+        out->seq_q = g.Sq;
+        out->seq_kv = g.Skv;
+        out->budget = spec->budget;
+        char* ws = (char*)workspace;
+        {
+            void* dst[3] = {out->row_ptr, ws + w.pinw, ws + w.dropw};
+            const void* src[3] = {p.row_ptr.data(), p.pin_words.data(), p.drop_words.data()};
+            size_t bytes[3] = {p.row_ptr.size() * sizeof(int32_t), p.has_pins ? p.pin_words.size() * 8 : 0,
+                               p.has_drops ? p.drop_words.size() * 8 : 0};
+            const hipError_t e = upload(3, dst, src, bytes, stream);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        if (g.rows == 0 || g.NK == 0) return NSA_OK;
+        // Pooled queries; the pooled keys are the caller's cache (capacity pooled_k->S tiles per head).
+        float* pq = (float*)(ws + w.pq);
+        hipError_t e = nsa::launch_pool(q->data, g.bf16, (int64_t)g.B * g.Hq, g.Sq, g.D, spec->block_q, pq, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        const float* qh = pq;
+        const float* kh = (const float*)pooled_k->data;
+        int Hk = g.Hkv, NKs = pooled_k->S;
+        if (spec->head_shared) {
+            float* mq = (float*)(ws + w.mq);
+            float* mk = (float*)(ws + w.mk);
+            if ((e = nsa::launch_head_mean(pq, g.B, g.Hq, g.NQ, g.D, mq, stream)) != hipSuccess) return hip_fail(e);
+            if ((e = nsa::launch_head_mean(kh, g.B, g.Hkv, g.NK, g.D, mk, stream, pooled_k->S)) != hipSuccess)
+                return hip_fail(e);
+            qh = mq;
+            kh = mk;
+            Hk = 1;
+            NKs = g.NK;
+        }
+        return score_and_topk(p, spec, qh, kh, Hk, NKs, w, ws, out, stream);
+    } catch (...) {
+        return NSA_ERR_UNSUPPORTED;
+    }
+}
+
+int nsa_decode_attn(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa_tensor* v_cache, int32_t length,
+                    int32_t q_pos0, const nsa_selection* sel, nsa_tensor* out, float* lse, void* stream) {
+    int st;
+    if ((st = check_tensor(q)) != NSA_OK) return st;
+    if ((st = check_tensor(k_cache)) != NSA_OK) return st;
+    if ((st = check_tensor(v_cache)) != NSA_OK) return st;
+    if ((st = check_tensor(out)) != NSA_OK) return st;
+    if (q->dtype != k_cache->dtype || q->dtype != v_cache->dtype || q->dtype != out->dtype)
+        return NSA_ERR_BAD_DTYPE;
+    if (q->B != k_cache->B || k_cache->B != v_cache->B || k_cache->H != v_cache->H || k_cache->S != v_cache->S)
+        return NSA_ERR_BAD_SHAPE;
+    if (q->D != k_cache->D || q->D != v_cache->D || q->H % k_cache->H != 0) return NSA_ERR_BAD_SHAPE;
+    if (out->B != q->B || out->H != q->H || out->S != q->S || out->D != q->D) return NSA_ERR_BAD_SHAPE;
+    if (length < 0 || length > k_cache->S || q_pos0 < 0 || (int64_t)q_pos0 + q->S > length)
+        return NSA_ERR_BAD_SHAPE;
+    if (numel(q) > 0 && !lse) return NSA_ERR_NULL_ARG;
+    if (q->D != 64 && q->D != 128) return NSA_ERR_UNSUPPORTED;
+    nsa::AttnArgs a;
+    a.q = q->data;
+    a.k = k_cache->data;
+    a.v = v_cache->data;
+    a.out = out->data;
+    a.lse = lse;
+    a.B = q->B;
+    a.Hq = q->H;
+    a.Hkv = k_cache->H;
+    a.S = q->S;
+    a.Skv = length;
+    a.kv_rows = k_cache->S;
+    a.q_off = q_pos0;
+    a.D = q->D;
+    a.causal = 1;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)q->D));
+    if (sel) {
+        if (!sel->row_ptr) return NSA_ERR_NULL_ARG;
+        if (sel->nnz > 0 && !sel->col_idx) return NSA_ERR_NULL_ARG;
+        if (sel->block_q <= 0 || sel->block_kv <= 0) return NSA_ERR_BAD_SPEC;
+        if ((sel->B != q->B && sel->B != 1) || (sel->H != 1 && sel->H != q->H)) return NSA_ERR_BAD_SHAPE;
+        if (sel->seq_q != q->S || sel->seq_kv != length) return NSA_ERR_BAD_SHAPE;
+        if (sel->NQ != ceil_div(q->S, sel->block_q) || sel->NK != ceil_div(length, sel->block_kv))
+            return NSA_ERR_BAD_SHAPE;
+        a.row_ptr = sel->row_ptr;
+        a.col_idx = sel->col_idx;
+        a.Hsel = sel->H;
+        a.Bsel = sel->B;
+        a.block_q = sel->block_q;
+        a.block_kv = sel->block_kv;
+    } else {  // dense over the first `length` keys
+        a.row_ptr = nullptr;
+        a.col_idx = nullptr;
+        a.Hsel = q->H;
+        a.Bsel = q->B;
+        a.block_q = q->S <= 32 ? 32 : (q->S <= 64 ? 64 : 128);
+        a.block_kv = 64;
+    }
+    a.NQ = (int)ceil_div(q->S, a.block_q);
+    a.NK = (int)ceil_div(length, a.block_kv);
+    if ((int64_t)a.B * a.Hq * a.NQ == 0) return NSA_OK;
+    const int bf16 = q->dtype == NSA_BF16;
+    const hipError_t e = nsa::attn_mfma_supported(a, bf16) ? nsa::launch_attn_mfma(a, (hipStream_t)stream)
+                                                             : nsa::launch_attn_simt(a, bf16, (hipStream_t)stream);
+    return e == hipSuccess ? NSA_OK : hip_fail(e);
+}
+
 int nsa_selection_density(const nsa_selection* sel, double* out) {
     if (!sel || !out) return NSA_ERR_NULL_ARG;
     const int64_t tiles = (int64_t)sel->B * sel->H * sel->NQ * sel->NK;
@@ -897,6 +1114,9 @@ int nsa_block_sparse_attn(const nsa_tensor* q, const nsa_tensor* k, const nsa_te
     a.Hq = q->H;
     a.Hkv = k->H;
     a.S = q->S;
+    a.Skv = k->S;
+    a.kv_rows = k->S;
+    a.q_off = 0;
     a.D = q->D;
     a.causal = causal ? 1 : 0;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)q->D));

@@ -13,21 +13,28 @@ namespace nsa {
 // Mean over blocks of `block` tokens: x (heads, S, D) -> out (heads, N, D) fp32.
 hipError_t launch_pool(const void* x, int bf16, int64_t heads, int S, int D, int block,
                        float* out, hipStream_t stream);
+// The same for tiles [tile0, tile0 + ntiles) of heads laid out x_head_rows rows
+// apart (S valid rows each), into out tiles laid out out_head_tiles apart.
+hipError_t launch_pool_range(const void* x, int bf16, int64_t heads, int S, int64_t x_head_rows, int D, int block,
+                             int tile0, int ntiles, float* out, int64_t out_head_tiles, hipStream_t stream);
 
-// out[b, n, :] = mean over h of in[b, h, n, :]  (in: (B, H, N, D) fp32).
+// out[b, n, :] = mean over h of in[b, h, n, :]  (in: (B, H, Ns, D) fp32, rows n < N
+// used; Ns = 0 means Ns = N).
 hipError_t launch_head_mean(const float* in, int B, int H, int N, int D, float* out,
-                            hipStream_t stream);
+                            hipStream_t stream, int Ns = 0);
 
 // Scores for selection heads [h0, h0 + nh): s[b, h - h0, i, j] = qh[b, h, i] . kh[b, h / group, j]
 // qh: (B, Hsel, NQ, D) fp32, kh: (B, Hk, NK, D) fp32, s: (B, nh, NQ, NK) fp32.
+// kh rows of one head are NKs apart (NKs = 0 means NK).
 hipError_t launch_scores(const float* qh, const float* kh, int B, int Hsel, int Hk, int group,
-                         int h0, int nh, int NQ, int NK, int D, float* s, hipStream_t stream);
+                         int h0, int nh, int NQ, int NK, int D, float* s, hipStream_t stream, int NKs = 0);
 
 // Per-row top-k over the score chunk of heads [h0, h0 + nh) and CSR emission.
 struct TopkArgs {
     const float* scores;       // (B, nh, NQ, NK)
     int B, Hsel, h0, nh, NQ, NK, NKW;
     int block_q, block_kv;
+    int64_t q_off = 0;         // absolute key position of query token 0 (diagonal)
     float budget;
     const uint64_t* pin_words; // (pb, ph, NQ, NKW) or null; bit (j % 64) of word j / 64
     int pb, ph;
@@ -42,11 +49,14 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 // ---- attention stage -------------------------------------------------------
 
 struct AttnArgs {
-    const void* q;            // (B, Hq, S, D)
-    const void* k;            // (B, Hkv, S, D)
+    const void* q;            // (B, Hq, S, D): S query tokens
+    const void* k;            // (B, Hkv, kv_rows, D): the first Skv rows of each head are keys
     const void* v;
     void* out;                // (B, Hq, S, D), dtype of q
     float* lse;               // (B, Hq, S)
+    int Skv;                  // keys per head (== S outside decoding)
+    int64_t kv_rows;          // rows per kv head in memory (>= Skv; a cache's capacity)
+    int q_off;                // absolute key position of query token 0 (causal: u <= q_off + t)
     const int32_t* row_ptr;   // null = dense
     const int32_t* col_idx;
     int B, Hq, Hkv, Hsel, S, D, NQ, NK, block_q, block_kv;

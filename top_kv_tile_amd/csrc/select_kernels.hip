@@ -53,7 +53,8 @@ __device__ __forceinline__ float wave_max_f(float x) {
 // partial sums are added across lanes and divided by the tile's real length.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ xv, float* __restrict__ out,
-                                                   int S, int block, int ntiles, int64_t total) {
+                                                   int S, int block, int ntiles, int64_t total, int64_t x_head_rows,
+                                                   int tile0, int64_t out_head_tiles) {
     constexpr int ESZ = BF16 ? 2 : 4;
     constexpr int VEC = 16 / ESZ;      // elements per 16-byte chunk
     constexpr int CPR = D / VEC;       // chunks per token row
@@ -63,11 +64,11 @@ __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ xv, 
     const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (tile >= total) return;
     const int64_t head = tile / ntiles;
-    const int i = (int)(tile - head * ntiles);
+    const int i = tile0 + (int)(tile - head * ntiles);  // tile index within the head
     const int c = lane % CPR, rg = lane / CPR;
     const int t0 = i * block;
     const int len = min(block, S - t0);
-    const char* base = (const char*)xv + ((head * S + t0) * (int64_t)D + (int64_t)c * VEC) * ESZ;
+    const char* base = (const char*)xv + ((head * x_head_rows + t0) * (int64_t)D + (int64_t)c * VEC) * ESZ;
     const int64_t row_bytes = (int64_t)D * ESZ;
 
     float acc[VEC];
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ xv, 
     }
     if (rg == 0) {
         const float n = (float)len;
-        float* o = out + tile * D + c * VEC;
+        float* o = out + (head * out_head_tiles + i) * D + c * VEC;
 #pragma unroll
         for (int e = 0; e < VEC; e += 4) {
             f32x4 v = {acc[e] / n, acc[e + 1] / n, acc[e + 2] / n, acc[e + 3] / n};
@@ -116,15 +117,17 @@ __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ xv, 
 }
 
 // ---------------------------------------------------------------- head means
+// in: (B, H, Ns, D) with the first N of Ns rows per head used; out: (B, N, D).
 __global__ __launch_bounds__(256) void head_mean_kernel(const float* __restrict__ in, float* __restrict__ out,
-                                                        int B, int H, int N, int D) {
+                                                        int B, int H, int N, int Ns, int D) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t per_b = (int64_t)N * D;
     if (idx >= (int64_t)B * per_b) return;
     const int64_t b = idx / per_b, nd = idx - b * per_b;
-    const float* p = in + b * H * per_b + nd;
+    const int64_t head_stride = (int64_t)Ns * D;
+    const float* p = in + b * H * head_stride + nd;
     float s = 0.f;
-    for (int h = 0; h < H; ++h) s += p[(int64_t)h * per_b];
+    for (int h = 0; h < H; ++h) s += p[(int64_t)h * head_stride];
     out[idx] = s / (float)H;
 }
 
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(256) void head_mean_kernel(const float* __restrict_
 template <int D>
 __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qh, const float* __restrict__ kh,
                                                     int Hsel, int Hk, int group, int h0, int nh, int NQ,
-                                                    int NK, int nbi, int nbj, float* __restrict__ s) {
+                                                    int NK, int NKs, int nbi, int nbj, float* __restrict__ s) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nbj4 = (nbj + 3) >> 2;
     int64_t wid = blockIdx.x;
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qh
     const int h = h0 + hl;
     const int hk = (Hk == 1) ? 0 : h / group;
     const float* A = qh + ((int64_t)b * Hsel + h) * NQ * D;
-    const float* Bm = kh + ((int64_t)b * Hk + hk) * NK * D;
+    const float* Bm = kh + ((int64_t)b * Hk + hk) * NKs * D;  // NKs >= NK rows per head
     const int i0 = bi * 64, j0 = bj * 64;
     const int l32 = lane & 31, hf = lane >> 5;
     const float* a0p = A + (int64_t)min(i0 + l32, NQ - 1) * D + 8 * hf;
@@ -353,10 +356,11 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
         a.pin_words ? a.pin_words + (((int64_t)(b % a.pb) * a.ph + (h % a.ph)) * a.NQ + i) * a.NKW : nullptr;
     const uint64_t* dw =
         a.drop_words ? a.drop_words + (((int64_t)(b % a.db) * a.dh + (h % a.dh)) * a.NQ + i) * a.NKW : nullptr;
-    // Diagonal: kv tiles j with i*bq < (j+1)*bkv and j*bkv < (i+1)*bq, i.e.
-    // floor(i*bq/bkv) <= j <= ceil((i+1)*bq/bkv) - 1.
-    const int dlo = (int)(((int64_t)i * a.block_q) / a.block_kv);
-    const int dhi = (int)(((int64_t)(i + 1) * a.block_q + a.block_kv - 1) / a.block_kv) - 1;
+    // Diagonal: kv tiles j with o + i*bq < (j+1)*bkv and j*bkv < o + (i+1)*bq
+    // (o = q_off, the absolute position of the first query token), i.e.
+    // floor((o + i*bq)/bkv) <= j <= ceil((o + (i+1)*bq)/bkv) - 1.
+    const int dlo = (int)((a.q_off + (int64_t)i * a.block_q) / a.block_kv);
+    const int dhi = (int)((a.q_off + (int64_t)(i + 1) * a.block_q + a.block_kv - 1) / a.block_kv) - 1;
 
     // Scores: slot t of lane L is element 64t + L (index clamped in range;
     // slots past NK are never candidates).
@@ -412,14 +416,14 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_pool(const void* x, int bf16, int64_t heads, int S, int D, int block, float* out,
-                       hipStream_t stream) {
-    const int ntiles = (S + block - 1) / block;
+hipError_t launch_pool_range(const void* x, int bf16, int64_t heads, int S, int64_t x_head_rows, int D, int block,
+                             int tile0, int ntiles, float* out, int64_t out_head_tiles, hipStream_t stream) {
     const int64_t total = heads * ntiles;
     if (total == 0) return hipSuccess;
     const dim3 grid((unsigned)((total + 3) / 4));
-#define NSA_POOL(DD, BB)                                                                          \
-    hipLaunchKernelGGL((pool_kernel<DD, BB>), grid, dim3(256), 0, stream, x, out, S, block, ntiles, total)
+#define NSA_POOL(DD, BB)                                                                                 \
+    hipLaunchKernelGGL((pool_kernel<DD, BB>), grid, dim3(256), 0, stream, x, out, S, block, ntiles, total, \
+                       x_head_rows, tile0, out_head_tiles)
     if (bf16) {
         if (D == 64) NSA_POOL(64, true);
         else if (D == 128) NSA_POOL(128, true);
@@ -435,23 +439,31 @@ hipError_t launch_pool(const void* x, int bf16, int64_t heads, int S, int D, int
     return hipGetLastError();
 }
 
-hipError_t launch_head_mean(const float* in, int B, int H, int N, int D, float* out, hipStream_t stream) {
+hipError_t launch_pool(const void* x, int bf16, int64_t heads, int S, int D, int block, float* out,
+                       hipStream_t stream) {
+    const int ntiles = (S + block - 1) / block;
+    return launch_pool_range(x, bf16, heads, S, S, D, block, 0, ntiles, out, ntiles, stream);
+}
+
+hipError_t launch_head_mean(const float* in, int B, int H, int N, int D, float* out, hipStream_t stream,
+                            int Ns) {
     const int64_t total = (int64_t)B * N * D;
     if (total == 0) return hipSuccess;
     hipLaunchKernelGGL(head_mean_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, in,
-                       out, B, H, N, D);
+                       out, B, H, N, Ns > 0 ? Ns : N, D);
     return hipGetLastError();
 }
 
 hipError_t launch_scores(const float* qh, const float* kh, int B, int Hsel, int Hk, int group, int h0, int nh,
-                         int NQ, int NK, int D, float* s, hipStream_t stream) {
+                         int NQ, int NK, int D, float* s, hipStream_t stream, int NKs) {
+    if (NKs <= 0) NKs = NK;
     if (NQ == 0 || NK == 0 || nh == 0 || B == 0) return hipSuccess;
     const int nbi = (NQ + 63) / 64, nbj = (NK + 63) / 64;
     const int64_t blocks = (int64_t)B * nh * nbi * ((nbj + 3) / 4);
     const dim3 grid((unsigned)blocks);
 #define NSA_SCORE(DD)                                                                                 \
     hipLaunchKernelGGL((score_kernel<DD>), grid, dim3(256), 0, stream, qh, kh, Hsel, Hk, group, h0, nh, NQ, \
-                       NK, nbi, nbj, s)
+                       NK, NKs, nbi, nbj, s)
     if (D == 64) NSA_SCORE(64);
     else if (D == 128) NSA_SCORE(128);
     else if (D == 256) NSA_SCORE(256);

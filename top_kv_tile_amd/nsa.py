@@ -23,7 +23,8 @@ __all__ = [
     "nsa_block_sparse_attn", "nsa_block_sparse_attn_bwd", "nsa_attn_bwd_workspace_size",
     "nsa_pool_blocks", "nsa_score_blocks", "nsa_status_string", "Plan", "nsa_plan_create",
     "nsa_select_planned", "nsa_schedule", "nsa_radial_blocks", "nsa_selection_density", "nsa_curve_order",
-    "nsa_permute_tokens", "NSA_CURVE_MORTON", "NSA_CURVE_HILBERT", "LIB_PATH", "EXPORTS",
+    "nsa_permute_tokens", "NSA_CURVE_MORTON", "NSA_CURVE_HILBERT", "nsa_decode_pool_update", "nsa_decode_select",
+    "nsa_decode_attn", "LIB_PATH", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnsa.so")
@@ -31,7 +32,8 @@ EXPORTS = ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_attn_
            "nsa_block_sparse_attn_bwd", "nsa_pool_blocks", "nsa_score_blocks", "nsa_status_string",
            "nsa_last_hip_error", "nsa_version", "nsa_plan_create", "nsa_plan_sizes", "nsa_select_planned",
            "nsa_plan_destroy", "nsa_schedule", "nsa_radial_sizes", "nsa_radial_blocks", "nsa_selection_density",
-           "nsa_curve_order", "nsa_permute_tokens")
+           "nsa_curve_order", "nsa_permute_tokens", "nsa_decode_pool_update", "nsa_decode_select_sizes",
+           "nsa_decode_select", "nsa_decode_attn")
 
 NSA_OK, NSA_DENSE = 0, 1
 NSA_F32, NSA_BF16 = 0, 1
@@ -114,13 +116,22 @@ def lib() -> ctypes.CDLL:
         L.nsa_selection_density.argtypes = [P(_Selection), P(ctypes.c_double)]
         L.nsa_curve_order.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
         L.nsa_permute_tokens.argtypes = [P(_Tensor), ctypes.c_void_p, ctypes.c_int32, P(_Tensor), ctypes.c_void_p]
+        L.nsa_decode_pool_update.argtypes = [P(_Tensor), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+        L.nsa_decode_select_sizes.argtypes = [P(_Tensor), P(_Tensor), ctypes.c_int32, ctypes.c_int32, P(_Spec),
+                                              P(_Mask), P(_Mask), P(_Sizes), ctypes.c_void_p]
+        L.nsa_decode_select.argtypes = [P(_Tensor), P(_Tensor), ctypes.c_int32, ctypes.c_int32, P(_Spec), P(_Mask),
+                                        P(_Mask), P(_Selection), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.nsa_decode_attn.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), ctypes.c_int32, ctypes.c_int32,
+                                      P(_Selection), P(_Tensor), ctypes.c_void_p, ctypes.c_void_p]
         L.nsa_status_string.argtypes = [ctypes.c_int]
         L.nsa_status_string.restype = ctypes.c_char_p
         L.nsa_version.restype = ctypes.c_char_p
         for name in ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_attn_bwd_workspace_size",
                      "nsa_block_sparse_attn_bwd", "nsa_pool_blocks", "nsa_score_blocks", "nsa_last_hip_error",
                      "nsa_plan_create", "nsa_plan_sizes", "nsa_select_planned", "nsa_schedule", "nsa_radial_sizes",
-                     "nsa_radial_blocks", "nsa_selection_density", "nsa_curve_order", "nsa_permute_tokens"):
+                     "nsa_radial_blocks", "nsa_selection_density", "nsa_curve_order", "nsa_permute_tokens",
+                     "nsa_decode_pool_update", "nsa_decode_select_sizes", "nsa_decode_select", "nsa_decode_attn"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -430,3 +441,60 @@ def nsa_permute_tokens(x: torch.Tensor, perm: torch.Tensor, inverse: bool = Fals
                                     int(bool(inverse)), ctypes.byref(_tensor(y)), _stream(stream)),
            "nsa_permute_tokens")
     return y
+
+
+def _tensor_f32(t: torch.Tensor) -> _Tensor:
+    if t.dtype != torch.float32 or t.dim() != 4 or not t.is_contiguous():
+        raise ValueError("pooled keys are a contiguous fp32 (B, Hkv, tiles, D) tensor")
+    B, H, S, D = t.shape
+    return _Tensor(t.data_ptr() if t.numel() else None, NSA_F32, B, H, S, D)
+
+
+def nsa_decode_pool_update(k_cache: torch.Tensor, len_old: int, len_new: int, block_kv: int, pooled: torch.Tensor,
+                           stream=None) -> torch.Tensor:
+    """Refreshes the pooled-key cache for the tokens appended between len_old and len_new."""
+    _check(lib().nsa_decode_pool_update(ctypes.byref(_tensor(k_cache)), int(len_old), int(len_new), int(block_kv),
+                                        ctypes.c_void_p(pooled.data_ptr()), int(pooled.shape[2]), _stream(stream)),
+           "nsa_decode_pool_update")
+    return pooled
+
+
+def nsa_decode_select(q: torch.Tensor, pooled_k: torch.Tensor, length: int, q_pos0: int,
+                      spec: SparseSpec = SparseSpec(), pins=None, drops=None, stream=None,
+                      workspace: torch.Tensor | None = None):
+    """Selection for the new query tokens against the cache; a Selection, or None when dense."""
+    hold = []
+    out = _Sizes()
+    pk = _tensor_f32(pooled_k)
+    _check(lib().nsa_decode_select_sizes(ctypes.byref(_tensor(q)), ctypes.byref(pk), int(length), int(q_pos0),
+                                         ctypes.byref(spec._c()), _mask(pins, hold), _mask(drops, hold),
+                                         ctypes.byref(out), None), "nsa_decode_select_sizes")
+    if out.dense:
+        return None
+    dev = q.device
+    keep = torch.empty((q.shape[0], out.sel_heads, out.NQ, out.NK), dtype=torch.int8, device=dev)
+    row_ptr = torch.empty(out.rows + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(out.nnz, dtype=torch.int32, device=dev)
+    if workspace is None or workspace.numel() < out.workspace_bytes:
+        workspace = torch.empty(max(out.workspace_bytes, 1), dtype=torch.uint8, device=dev)
+    sel = Selection(keep, row_ptr, col_idx, spec.block_q, spec.block_kv, spec.budget, q.shape[2], int(length))
+    csel = sel._c()
+    st = _check(lib().nsa_decode_select(ctypes.byref(_tensor(q)), ctypes.byref(pk), int(length), int(q_pos0),
+                                        ctypes.byref(spec._c()), _mask(pins, hold), _mask(drops, hold),
+                                        ctypes.byref(csel), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                        _stream(stream)), "nsa_decode_select")
+    return None if st == NSA_DENSE else sel
+
+
+def nsa_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, length: int, q_pos0: int,
+                    selection: Selection | None, stream=None, out: torch.Tensor | None = None,
+                    lse: torch.Tensor | None = None):
+    """Attention of the new query tokens over the kept tiles of the cache; returns (out, lse)."""
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    csel = ctypes.byref(selection._c()) if selection is not None else None
+    _check(lib().nsa_decode_attn(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k_cache)),
+                                 ctypes.byref(_tensor(v_cache)), int(length), int(q_pos0), csel,
+                                 ctypes.byref(_tensor(out)), ctypes.c_void_p(lse.data_ptr()), _stream(stream)),
+           "nsa_decode_attn")
+    return out, lse

@@ -272,13 +272,24 @@ int nsa_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t l
                       const nsa_spec* spec, const nsa_mask* pins, const nsa_mask* drops, nsa_selection* out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Host only. Device workspace nsa_decode_attn needs for these shapes and this
+ * selection (sel may be NULL). */
+int nsa_decode_attn_workspace_size(const nsa_tensor* q, const nsa_tensor* k_cache, int32_t length, int32_t q_pos0,
+                                   const nsa_selection* sel, int64_t* bytes);
+
 /* Attention of the new query tokens q (B, Hq, n, D) over the kept tiles of the
  * first `length` keys of k_cache / v_cache (B, Hkv, capacity, D): key u is
  * visible to query t iff its tile is kept and u <= q_pos0 + t. sel from
  * nsa_decode_select, or NULL for every tile. out (B, Hq, n, D), lse (B, Hq, n)
- * as nsa_block_sparse_attn. Errors as nsa_block_sparse_attn. */
+ * as nsa_block_sparse_attn. With few query rows, each row's tiles are split
+ * over several workgroups whose partial results (unnormalised output, exponent
+ * reference and sum) go to `workspace` and are then merged, so the whole GPU
+ * streams the cache. workspace: device scratch of
+ * nsa_decode_attn_workspace_size bytes. Errors as nsa_block_sparse_attn, plus
+ * WORKSPACE. */
 int nsa_decode_attn(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa_tensor* v_cache, int32_t length,
-                    int32_t q_pos0, const nsa_selection* sel, nsa_tensor* out, float* lse, void* stream);
+                    int32_t q_pos0, const nsa_selection* sel, nsa_tensor* out, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* Device workspace, in bytes, that nsa_block_sparse_attn_bwd needs for these
  * shapes and this selection (sel may be NULL for dense). Host only. */

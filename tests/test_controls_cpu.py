@@ -184,6 +184,19 @@ def test_decode_validation(L):
     assert L.nsa_decode_pool_update(ctypes.byref(kc), 7, 7, 64, None, 8, None) == 0   # nothing appended
     out = N._Tensor(1, N.NSA_BF16, 1, 4, 2, 128)
     A = L.nsa_decode_attn
-    assert A(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(kc), 600, 100, None, ctypes.byref(out), 1, None) == -2
-    assert A(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(kc), 500, 499, None, ctypes.byref(out), 1, None) == -2
-    assert A(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(kc), 500, 10, None, ctypes.byref(out), None, None) == -1
+    big = 1 << 30
+    assert A(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(kc), 600, 100, None, ctypes.byref(out), 1, 1, big,
+             None) == -2
+    assert A(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(kc), 500, 499, None, ctypes.byref(out), 1, 1, big,
+             None) == -2
+    assert A(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(kc), 500, 10, None, ctypes.byref(out), None, 1, big,
+             None) == -1
+    n = ctypes.c_int64(-1)
+    assert L.nsa_decode_attn_workspace_size(ctypes.byref(q), ctypes.byref(kc), 500, 10, None, ctypes.byref(n)) == 0
+    assert n.value == 0  # 8 tiles per row: too few to split
+    kl = N._Tensor(1, N.NSA_BF16, 1, 2, 2048, 128)
+    assert L.nsa_decode_attn_workspace_size(ctypes.byref(q), ctypes.byref(kl), 2000, 10, None, ctypes.byref(n)) == 0
+    # 4 rows of 32 tiles: 4 splits of 8 tiles, fp32 partials of D values plus (reference, sum) per split
+    assert n.value == 4 * 2 * 4 * 128 * 4 + 256
+    assert A(ctypes.byref(q), ctypes.byref(kl), ctypes.byref(kl), 2000, 10, None, ctypes.byref(out), 1, 1,
+             n.value - 1, None) == -5

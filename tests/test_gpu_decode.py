@@ -57,3 +57,40 @@ def test_dense_decode_attention():
     nk = -(-length // 64)
     ref_o, ref_l = oracle.decode_attention(q, kc, vc, length, length - 3, np.ones((1, 1, 1, nk), np.int8), 32, 64)
     check_attention(out, lse, ref_o, ref_l, "bf16", where="dense decode")
+
+
+@pytest.mark.parametrize("n,shared", [(1, False), (4, False), (3, True)])
+def test_split_decode_attention(n, shared):
+    """Few query rows over a long cache: each row's tiles are split over several
+    workgroups and merged. A head whose tiles are all dropped (empty row), a
+    ragged last tile, and splits that get no tile."""
+    say(f"split decode n={n} shared={shared}")
+    B, Hq, Hkv, cap, D, bq, bkv = 2, 8, 2, 16384, 128, 32, 64
+    length = 15990
+    g = torch.Generator().manual_seed(31 + n)
+    kc, vc = (torch.randn(B, Hkv, cap, D, generator=g).to(torch.bfloat16) for _ in range(2))
+    q = torch.randn(B, Hq, n, D, generator=g).to(torch.bfloat16)
+    pos0 = length - n
+    nk = -(-length // bkv)
+    kd, vd = to_dev(kc), to_dev(vc)
+    pooled = torch.zeros(B, Hkv, cap // bkv, D, dtype=torch.float32, device="cuda:0")
+    tkt.nsa_decode_pool_update(kd, 0, length, bkv, pooled)
+    rng = np.random.default_rng(n)
+    pins = (rng.random((B, 1, 1, nk)) < 0.05).astype(np.int8)
+    drops = np.zeros((1, 1 if shared else Hq, 1, nk), np.int8)
+    if not shared:
+        drops[0, 5] = 1  # every tile of head 5: its rows are empty
+    spec = tkt.SparseSpec(budget=0.25, block_q=bq, block_kv=bkv, head_shared=shared, force=True)
+    qd = to_dev(q)
+    sel = tkt.nsa_decode_select(qd, pooled, length, pos0, spec, pins=pins, drops=drops)
+    ref = oracle.decode_select(q, kc, length, pos0, spec.budget, bq, bkv, shared, True, pins=pins, drops=drops)
+    keep, _ = check_selection(sel, ref, "split select")
+    out, lse = tkt.nsa_decode_attn(qd, kd, vd, length, pos0, sel)
+    ref_o, ref_l = oracle.decode_attention(q, kc, vc, length, pos0, keep, bq, bkv)
+    check_attention(out, lse, ref_o, ref_l, "bf16", where="split decode")
+    if not shared:
+        assert torch.isneginf(lse[:, 5]).all() and (out[:, 5] == 0).all()
+    # dense over the same cache
+    out, lse = tkt.nsa_decode_attn(qd, kd, vd, length, pos0, None)
+    ref_o, ref_l = oracle.decode_attention(q, kc, vc, length, pos0, np.ones((1, 1, 1, nk), np.int8), bq, bkv)
+    check_attention(out, lse, ref_o, ref_l, "bf16", where="split dense decode")

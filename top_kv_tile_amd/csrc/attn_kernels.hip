@@ -139,7 +139,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hf = lane >> 5;
     const int64_t total = (int64_t)a.B * a.Hq * a.NQ;
-    const Work wk = decode_work(blockIdx.x, total, a.Hq, a.Hkv, a.NQ);
+    const int split = (int)(blockIdx.x % a.nsplit);
+    const Work wk = decode_work(blockIdx.x / a.nsplit, total, a.Hq, a.Hkv, a.NQ);
     const int bq = a.block_q;
     const int q0 = wk.i * bq;
     const int qw0 = q0 + wave * 32;                  // first query row of this wave
@@ -168,6 +169,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
 
     int e_begin, e_end;
     tile_range(a, wk.b, wk.h, wk.i, a.q_off + q_last, e_begin, e_end);
+    if (a.nsplit > 1) {  // this workgroup's share of the row's tiles
+        const int per = (e_end - e_begin + a.nsplit - 1) / a.nsplit;
+        e_begin = min(e_end, e_begin + split * per);
+        e_end = min(e_end, e_begin + per);
+    }
     const int ntiles = e_end - e_begin;
 
     // The row's kv-tile indices, 64 at a time: lane x holds entry base + x and
@@ -374,6 +380,24 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     // Finish: combine the two lane halves of the row sum.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const bool empty = !(l_tot > 0.f);
+    if (a.nsplit > 1) {  // partial result of this split: unnormalised O, reference and sum
+        if (qvalid) {
+            const int64_t prow = (((int64_t)wk.b * a.Hq + wk.h) * a.S + qrow) * a.nsplit + split;
+            float* po = a.part_o + prow * D;
+#pragma unroll
+            for (int m = 0; m < DBLK; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 w = {oacc[m][4 * q], oacc[m][4 * q + 1], oacc[m][4 * q + 2], oacc[m][4 * q + 3]};
+                    *(f32x4*)(po + 32 * m + 8 * q + 4 * hf) = w;
+                }
+            if (hf == 0) {
+                a.part_ml[2 * prow] = empty ? kNegInf : m_ref * a.scale_log2;
+                a.part_ml[2 * prow + 1] = l_tot;
+            }
+        }
+        return;
+    }
     const float inv = empty ? 0.f : 1.0f / l_tot;
     if (qvalid) {
         uint16_t* op = (uint16_t*)a.out + (((int64_t)wk.b * a.Hq + wk.h) * a.S + qrow) * D;
@@ -499,7 +523,58 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a) {
     }
 }
 
+// Merges the split partials of one query row: with M the largest reference,
+// w_s = 2^(m_s - M), O = sum_s w_s O_s / sum_s w_s l_s and
+// LSE = (M + log2 sum_s w_s l_s) ln 2. One wave per row, D / 64 elements per lane.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+    constexpr int PER = D / 64;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= (int64_t)a.B * a.Hq * a.S) return;
+    const float* ml = a.part_ml + row * a.nsplit * 2;
+    float M = kNegInf;
+    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, ml[2 * s]);
+    float lsum = 0.f, acc[PER];
+#pragma unroll
+    for (int x = 0; x < PER; ++x) acc[x] = 0.f;
+    for (int s = 0; s < a.nsplit; ++s) {
+        const float m = ml[2 * s];
+        if (m == kNegInf) continue;
+        const float w = exp2f(m - M);
+        lsum += w * ml[2 * s + 1];
+        const float* po = a.part_o + (row * a.nsplit + s) * D;
+#pragma unroll
+        for (int x = 0; x < PER; ++x) acc[x] += w * po[lane + 64 * x];
+    }
+    const bool empty = !(lsum > 0.f);
+    const float inv = empty ? 0.f : 1.0f / lsum;
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+        const float o = acc[x] * inv;
+        if constexpr (BF16) ((__bf16*)a.out)[row * D + lane + 64 * x] = (__bf16)o;
+        else ((float*)a.out)[row * D + lane + 64 * x] = o;
+    }
+    if (lane == 0) a.lse[row] = empty ? kNegInf : (M + __log2f(lsum)) * kLn2;
+}
+
 }  // namespace
+
+hipError_t launch_attn_combine(const AttnArgs& a, int bf16, hipStream_t stream) {
+    const int64_t rows = (int64_t)a.B * a.Hq * a.S;
+    if (rows == 0) return hipSuccess;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (a.D == 128) {
+        if (bf16) hipLaunchKernelGGL((attn_combine_kernel<128, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((attn_combine_kernel<128, false>), grid, dim3(256), 0, stream, a);
+    } else if (a.D == 64) {
+        if (bf16) hipLaunchKernelGGL((attn_combine_kernel<64, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((attn_combine_kernel<64, false>), grid, dim3(256), 0, stream, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 bool attn_mfma_supported(const AttnArgs& a, int bf16) {
     // Buffer offsets are 32-bit: one head plus a tile of slack must stay below 2^31 bytes.
@@ -509,7 +584,7 @@ bool attn_mfma_supported(const AttnArgs& a, int bf16) {
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream) {
-    const int64_t total = (int64_t)a.B * a.Hq * a.NQ;
+    const int64_t total = (int64_t)a.B * a.Hq * a.NQ * std::max(1, a.nsplit);
     if (total == 0) return hipSuccess;
     const dim3 grid((unsigned)total);
     const int nw = a.block_q / 32;

@@ -468,6 +468,87 @@ WsLayout decode_layout(const Plan& p, const nsa_spec* spec) {
     return ws_layout(p.g, spec, p.has_pins, p.pb * p.ph, p.has_drops, p.db * p.dh, true);
 }
 
+// Launch geometry of a decode attention call (everything but out / lse / partials).
+// Rows whose tiles are few and many can be split over several workgroups (MFMA
+// path): enough splits for about 2048 workgroups, each with at least 8 tiles.
+int decode_attn_config(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa_tensor* v_cache,
+                       const nsa_tensor* out, int32_t length, int32_t q_pos0, const nsa_selection* sel,
+                       nsa::AttnArgs& a) {
+    int st;
+    if ((st = check_tensor(q)) != NSA_OK) return st;
+    if ((st = check_tensor(k_cache)) != NSA_OK) return st;
+    if ((st = check_tensor(v_cache)) != NSA_OK) return st;
+    if ((st = check_tensor(out)) != NSA_OK) return st;
+    if (q->dtype != k_cache->dtype || q->dtype != v_cache->dtype || q->dtype != out->dtype)
+        return NSA_ERR_BAD_DTYPE;
+    if (q->B != k_cache->B || k_cache->B != v_cache->B || k_cache->H != v_cache->H || k_cache->S != v_cache->S)
+        return NSA_ERR_BAD_SHAPE;
+    if (q->D != k_cache->D || q->D != v_cache->D || q->H % k_cache->H != 0) return NSA_ERR_BAD_SHAPE;
+    if (out->B != q->B || out->H != q->H || out->S != q->S || out->D != q->D) return NSA_ERR_BAD_SHAPE;
+    if (length < 0 || length > k_cache->S || q_pos0 < 0 || (int64_t)q_pos0 + q->S > length)
+        return NSA_ERR_BAD_SHAPE;
+    if (q->D != 64 && q->D != 128) return NSA_ERR_UNSUPPORTED;
+    a.q = q->data;
+    a.k = k_cache->data;
+    a.v = v_cache->data;
+    a.out = nullptr;
+    a.lse = nullptr;
+    a.B = q->B;
+    a.Hq = q->H;
+    a.Hkv = k_cache->H;
+    a.S = q->S;
+    a.Skv = length;
+    a.kv_rows = k_cache->S;
+    a.q_off = q_pos0;
+    a.D = q->D;
+    a.causal = 1;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)q->D));
+    a.nsplit = 1;
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
+    int64_t tiles_per_row;
+    if (sel) {
+        if (!sel->row_ptr) return NSA_ERR_NULL_ARG;
+        if (sel->nnz > 0 && !sel->col_idx) return NSA_ERR_NULL_ARG;
+        if (sel->block_q <= 0 || sel->block_kv <= 0) return NSA_ERR_BAD_SPEC;
+        if ((sel->B != q->B && sel->B != 1) || (sel->H != 1 && sel->H != q->H)) return NSA_ERR_BAD_SHAPE;
+        if (sel->seq_q != q->S || sel->seq_kv != length) return NSA_ERR_BAD_SHAPE;
+        if (sel->NQ != ceil_div(q->S, sel->block_q) || sel->NK != ceil_div(length, sel->block_kv))
+            return NSA_ERR_BAD_SHAPE;
+        a.row_ptr = sel->row_ptr;
+        a.col_idx = sel->col_idx;
+        a.Hsel = sel->H;
+        a.Bsel = sel->B;
+        a.block_q = sel->block_q;
+        a.block_kv = sel->block_kv;
+        const int64_t rows = std::max<int64_t>((int64_t)sel->B * sel->H * sel->NQ, 1);
+        tiles_per_row = ceil_div(std::max<int64_t>(sel->nnz, 0), rows);
+    } else {  // every tile of the first `length` keys
+        a.row_ptr = nullptr;
+        a.col_idx = nullptr;
+        a.Hsel = q->H;
+        a.Bsel = q->B;
+        a.block_q = q->S <= 32 ? 32 : (q->S <= 64 ? 64 : 128);
+        a.block_kv = 64;
+        tiles_per_row = ceil_div(length, 64);
+    }
+    a.NQ = (int)ceil_div(q->S, a.block_q);
+    a.NK = (int)ceil_div(length, a.block_kv);
+    if (nsa::attn_mfma_supported(a, q->dtype == NSA_BF16)) {
+        const int64_t work = std::max<int64_t>((int64_t)a.B * a.Hq * a.NQ, 1);
+        const int64_t want = ceil_div(2048, work);
+        const int64_t most = std::max<int64_t>(1, tiles_per_row / 8);
+        a.nsplit = (int)std::max<int64_t>(1, std::min<int64_t>({want, most, 64}));
+    }
+    return NSA_OK;
+}
+
+size_t decode_attn_workspace(const nsa::AttnArgs& a) {
+    if (a.nsplit <= 1) return 0;
+    const size_t rows = (size_t)a.B * a.Hq * a.S * a.nsplit;
+    return align256(rows * a.D * 4) + align256(rows * 2 * 4);
+}
+
 // ---- radial band (radial_blocks of the selection page) -------------------------
 
 // Tiles whose query-range and kv-range centres are at most a bandwidth apart,
@@ -979,67 +1060,40 @@ int nsa_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t l
     }
 }
 
-int nsa_decode_attn(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa_tensor* v_cache, int32_t length,
-                    int32_t q_pos0, const nsa_selection* sel, nsa_tensor* out, float* lse, void* stream) {
-    int st;
-    if ((st = check_tensor(q)) != NSA_OK) return st;
-    if ((st = check_tensor(k_cache)) != NSA_OK) return st;
-    if ((st = check_tensor(v_cache)) != NSA_OK) return st;
-    if ((st = check_tensor(out)) != NSA_OK) return st;
-    if (q->dtype != k_cache->dtype || q->dtype != v_cache->dtype || q->dtype != out->dtype)
-        return NSA_ERR_BAD_DTYPE;
-    if (q->B != k_cache->B || k_cache->B != v_cache->B || k_cache->H != v_cache->H || k_cache->S != v_cache->S)
-        return NSA_ERR_BAD_SHAPE;
-    if (q->D != k_cache->D || q->D != v_cache->D || q->H % k_cache->H != 0) return NSA_ERR_BAD_SHAPE;
-    if (out->B != q->B || out->H != q->H || out->S != q->S || out->D != q->D) return NSA_ERR_BAD_SHAPE;
-    if (length < 0 || length > k_cache->S || q_pos0 < 0 || (int64_t)q_pos0 + q->S > length)
-        return NSA_ERR_BAD_SHAPE;
-    if (numel(q) > 0 && !lse) return NSA_ERR_NULL_ARG;
-    if (q->D != 64 && q->D != 128) return NSA_ERR_UNSUPPORTED;
+int nsa_decode_attn_workspace_size(const nsa_tensor* q, const nsa_tensor* k_cache, int32_t length, int32_t q_pos0,
+                                   const nsa_selection* sel, int64_t* bytes) {
+    if (!bytes) return NSA_ERR_NULL_ARG;
     nsa::AttnArgs a;
-    a.q = q->data;
-    a.k = k_cache->data;
-    a.v = v_cache->data;
+    const int st = decode_attn_config(q, k_cache, k_cache, q, length, q_pos0, sel, a);
+    if (st != NSA_OK) return st;
+    *bytes = (int64_t)decode_attn_workspace(a);
+    return NSA_OK;
+}
+
+int nsa_decode_attn(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa_tensor* v_cache, int32_t length,
+                    int32_t q_pos0, const nsa_selection* sel, nsa_tensor* out, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream_) {
+    hipStream_t stream = (hipStream_t)stream_;
+    nsa::AttnArgs a;
+    int st = decode_attn_config(q, k_cache, v_cache, out, length, q_pos0, sel, a);
+    if (st != NSA_OK) return st;
+    if (numel(q) > 0 && !lse) return NSA_ERR_NULL_ARG;
     a.out = out->data;
     a.lse = lse;
-    a.B = q->B;
-    a.Hq = q->H;
-    a.Hkv = k_cache->H;
-    a.S = q->S;
-    a.Skv = length;
-    a.kv_rows = k_cache->S;
-    a.q_off = q_pos0;
-    a.D = q->D;
-    a.causal = 1;
-    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)q->D));
-    if (sel) {
-        if (!sel->row_ptr) return NSA_ERR_NULL_ARG;
-        if (sel->nnz > 0 && !sel->col_idx) return NSA_ERR_NULL_ARG;
-        if (sel->block_q <= 0 || sel->block_kv <= 0) return NSA_ERR_BAD_SPEC;
-        if ((sel->B != q->B && sel->B != 1) || (sel->H != 1 && sel->H != q->H)) return NSA_ERR_BAD_SHAPE;
-        if (sel->seq_q != q->S || sel->seq_kv != length) return NSA_ERR_BAD_SHAPE;
-        if (sel->NQ != ceil_div(q->S, sel->block_q) || sel->NK != ceil_div(length, sel->block_kv))
-            return NSA_ERR_BAD_SHAPE;
-        a.row_ptr = sel->row_ptr;
-        a.col_idx = sel->col_idx;
-        a.Hsel = sel->H;
-        a.Bsel = sel->B;
-        a.block_q = sel->block_q;
-        a.block_kv = sel->block_kv;
-    } else {  // dense over the first `length` keys
-        a.row_ptr = nullptr;
-        a.col_idx = nullptr;
-        a.Hsel = q->H;
-        a.Bsel = q->B;
-        a.block_q = q->S <= 32 ? 32 : (q->S <= 64 ? 64 : 128);
-        a.block_kv = 64;
-    }
-    a.NQ = (int)ceil_div(q->S, a.block_q);
-    a.NK = (int)ceil_div(length, a.block_kv);
     if ((int64_t)a.B * a.Hq * a.NQ == 0) return NSA_OK;
+    const size_t need = decode_attn_workspace(a);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return NSA_ERR_WORKSPACE;
     const int bf16 = q->dtype == NSA_BF16;
-    const hipError_t e = nsa::attn_mfma_supported(a, bf16) ? nsa::launch_attn_mfma(a, (hipStream_t)stream)
-                                                             : nsa::launch_attn_simt(a, bf16, (hipStream_t)stream);
+    hipError_t e;
+    if (a.nsplit > 1) {
+        a.part_o = (float*)workspace;
+        a.part_ml = (float*)((char*)workspace + align256((size_t)a.B * a.Hq * a.S * a.nsplit * a.D * 4));
+        if ((e = nsa::launch_attn_mfma(a, stream)) != hipSuccess) return hip_fail(e);
+        e = nsa::launch_attn_combine(a, bf16, stream);
+    } else {
+        e = nsa::attn_mfma_supported(a, bf16) ? nsa::launch_attn_mfma(a, stream)
+                                              : nsa::launch_attn_simt(a, bf16, stream);
+    }
     return e == hipSuccess ? NSA_OK : hip_fail(e);
 }
 
@@ -1117,6 +1171,9 @@ int nsa_block_sparse_attn(const nsa_tensor* q, const nsa_tensor* k, const nsa_te
     a.Skv = k->S;
     a.kv_rows = k->S;
     a.q_off = 0;
+    a.nsplit = 1;
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
     a.D = q->D;
     a.causal = causal ? 1 : 0;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)q->D));

@@ -57,6 +57,9 @@ struct AttnArgs {
     int Skv;                  // keys per head (== S outside decoding)
     int64_t kv_rows;          // rows per kv head in memory (>= Skv; a cache's capacity)
     int q_off;                // absolute key position of query token 0 (causal: u <= q_off + t)
+    int nsplit;               // > 1: each row's tiles are split over nsplit workgroups (MFMA path)
+    float* part_o;            // split partials: (B*Hq*S, nsplit, D) unnormalised O
+    float* part_ml;           // (B*Hq*S, nsplit, 2): exponent reference (log2 units) and sum
     const int32_t* row_ptr;   // null = dense
     const int32_t* col_idx;
     int B, Hq, Hkv, Hsel, S, D, NQ, NK, block_q, block_kv;
@@ -67,6 +70,8 @@ struct AttnArgs {
 // bf16 MFMA path: block_q in {32, 64, 96, 128}, block_kv == 64, D in {64, 128}.
 bool attn_mfma_supported(const AttnArgs& a, int bf16);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream);
+// Merges the nsplit partials of every query row into out (dtype of q) and lse.
+hipError_t launch_attn_combine(const AttnArgs& a, int bf16, hipStream_t stream);
 // General path (fp32 or bf16 inputs, any block sizes, D in {64, 128}).
 hipError_t launch_attn_simt(const AttnArgs& a, int bf16, hipStream_t stream);
 

@@ -33,7 +33,7 @@ EXPORTS = ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_attn_
            "nsa_last_hip_error", "nsa_version", "nsa_plan_create", "nsa_plan_sizes", "nsa_select_planned",
            "nsa_plan_destroy", "nsa_schedule", "nsa_radial_sizes", "nsa_radial_blocks", "nsa_selection_density",
            "nsa_curve_order", "nsa_permute_tokens", "nsa_decode_pool_update", "nsa_decode_select_sizes",
-           "nsa_decode_select", "nsa_decode_attn")
+           "nsa_decode_select", "nsa_decode_attn", "nsa_decode_attn_workspace_size")
 
 NSA_OK, NSA_DENSE = 0, 1
 NSA_F32, NSA_BF16 = 0, 1
@@ -123,7 +123,10 @@ def lib() -> ctypes.CDLL:
         L.nsa_decode_select.argtypes = [P(_Tensor), P(_Tensor), ctypes.c_int32, ctypes.c_int32, P(_Spec), P(_Mask),
                                         P(_Mask), P(_Selection), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.nsa_decode_attn.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), ctypes.c_int32, ctypes.c_int32,
-                                      P(_Selection), P(_Tensor), ctypes.c_void_p, ctypes.c_void_p]
+                                      P(_Selection), P(_Tensor), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p]
+        L.nsa_decode_attn_workspace_size.argtypes = [P(_Tensor), P(_Tensor), ctypes.c_int32, ctypes.c_int32,
+                                                     P(_Selection), P(ctypes.c_int64)]
         L.nsa_status_string.argtypes = [ctypes.c_int]
         L.nsa_status_string.restype = ctypes.c_char_p
         L.nsa_version.restype = ctypes.c_char_p
@@ -131,7 +134,8 @@ def lib() -> ctypes.CDLL:
                      "nsa_block_sparse_attn_bwd", "nsa_pool_blocks", "nsa_score_blocks", "nsa_last_hip_error",
                      "nsa_plan_create", "nsa_plan_sizes", "nsa_select_planned", "nsa_schedule", "nsa_radial_sizes",
                      "nsa_radial_blocks", "nsa_selection_density", "nsa_curve_order", "nsa_permute_tokens",
-                     "nsa_decode_pool_update", "nsa_decode_select_sizes", "nsa_decode_select", "nsa_decode_attn"):
+                     "nsa_decode_pool_update", "nsa_decode_select_sizes", "nsa_decode_select", "nsa_decode_attn",
+                     "nsa_decode_attn_workspace_size"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -488,13 +492,21 @@ def nsa_decode_select(q: torch.Tensor, pooled_k: torch.Tensor, length: int, q_po
 
 def nsa_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, length: int, q_pos0: int,
                     selection: Selection | None, stream=None, out: torch.Tensor | None = None,
-                    lse: torch.Tensor | None = None):
+                    lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """Attention of the new query tokens over the kept tiles of the cache; returns (out, lse)."""
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
     csel = ctypes.byref(selection._c()) if selection is not None else None
+    need = ctypes.c_int64(0)
+    _check(lib().nsa_decode_attn_workspace_size(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k_cache)),
+                                                int(length), int(q_pos0), csel, ctypes.byref(need)),
+           "nsa_decode_attn_workspace_size")
+    if workspace is None or workspace.numel() * workspace.element_size() < need.value:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=q.device)
     _check(lib().nsa_decode_attn(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k_cache)),
                                  ctypes.byref(_tensor(v_cache)), int(length), int(q_pos0), csel,
-                                 ctypes.byref(_tensor(out)), ctypes.c_void_p(lse.data_ptr()), _stream(stream)),
+                                 ctypes.byref(_tensor(out)), ctypes.c_void_p(lse.data_ptr()),
+                                 ctypes.c_void_p(workspace.data_ptr()),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
            "nsa_decode_attn")
     return out, lse

@@ -15,6 +15,7 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,D,bq,shared", [(torch.bfloat16, 8, 2, 128, 128, False),
                                                       (torch.bfloat16, 4, 4, 64, 32, True),
+                                                      (torch.bfloat16, 8, 4, 128, 64, True),
                                                       (torch.float32, 4, 2, 64, 64, False)])
 def test_decode_loop(dtype, Hq, Hkv, D, bq, shared):
     say(f"decode loop {dtype} Hq={Hq} Hkv={Hkv} D={D} bq={bq} shared={shared}")
@@ -94,3 +95,31 @@ def test_split_decode_attention(n, shared):
     out, lse = tkt.nsa_decode_attn(qd, kd, vd, length, pos0, None)
     ref_o, ref_l = oracle.decode_attention(q, kc, vc, length, pos0, np.ones((1, 1, 1, nk), np.int8), bq, bkv)
     check_attention(out, lse, ref_o, ref_l, "bf16", where="split dense decode")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,n,bq", [(8, 2, 128, 40, 64), (16, 2, 64, 9, 32), (6, 3, 128, 1, 32)])
+def test_packed_gqa_decode(Hq, Hkv, D, n, bq):
+    """A selection shared by the heads (or none): the heads of a GQA group are
+    packed into one workgroup's rows. 40 tokens x 4 heads span two packed
+    tiles; causal masks inside the new tokens; split partials on long rows."""
+    say(f"packed decode Hq={Hq} Hkv={Hkv} D={D} n={n}")
+    B, cap, bkv = 2, 4096, 64
+    length = 3001 + n
+    g = torch.Generator().manual_seed(Hq * 100 + n)
+    kc, vc = (torch.randn(B, Hkv, cap, D, generator=g).to(torch.bfloat16) for _ in range(2))
+    q = torch.randn(B, Hq, n, D, generator=g).to(torch.bfloat16)
+    pos0 = length - n
+    nk = -(-length // bkv)
+    kd, vd, qd = to_dev(kc), to_dev(vc), to_dev(q)
+    pooled = torch.zeros(B, Hkv, cap // bkv, D, dtype=torch.float32, device="cuda:0")
+    tkt.nsa_decode_pool_update(kd, 0, length, bkv, pooled)
+    spec = tkt.SparseSpec(budget=0.2, block_q=bq, block_kv=bkv, head_shared=True, force=True)
+    sel = tkt.nsa_decode_select(qd, pooled, length, pos0, spec)
+    ref = oracle.decode_select(q, kc, length, pos0, spec.budget, bq, bkv, True, True)
+    keep, _ = check_selection(sel, ref, "packed select")
+    out, lse = tkt.nsa_decode_attn(qd, kd, vd, length, pos0, sel)
+    ref_o, ref_l = oracle.decode_attention(q, kc, vc, length, pos0, keep, bq, bkv)
+    check_attention(out, lse, ref_o, ref_l, "bf16", where="packed decode")
+    out, lse = tkt.nsa_decode_attn(qd, kd, vd, length, pos0, None)
+    ref_o, ref_l = oracle.decode_attention(q, kc, vc, length, pos0, np.ones((1, 1, 1, nk), np.int8), bq, bkv)
+    check_attention(out, lse, ref_o, ref_l, "bf16", where="packed dense decode")

@@ -78,7 +78,8 @@ __device__ __forceinline__ void tile_range(const AttnArgs& a, int b, int h, int 
                                            int& end) {
     if (a.row_ptr) {
         const int hs = (a.Hsel == 1) ? 0 : h;
-        const int64_t r = ((int64_t)(a.Bsel == 1 ? 0 : b) * a.Hsel + hs) * a.NQ + i;
+        const int64_t r = a.qpack ? (int64_t)(a.Bsel == 1 ? 0 : b)  // shared selection, one query tile
+                                  : ((int64_t)(a.Bsel == 1 ? 0 : b) * a.Hsel + hs) * a.NQ + i;
         start = a.row_ptr[r];
         end = a.row_ptr[r + 1];
         if (a.causal) {
@@ -167,8 +168,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
             qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff + 32 * ks, 0, 0));
     }
 
+    // Token position of this lane's row and the last position of the tile
+    // (packed heads: every head's tokens 0 .. qpack - 1 may be in the tile).
+    const int qpos = a.qpack ? qrow % a.qpack : qrow;
     int e_begin, e_end;
-    tile_range(a, wk.b, wk.h, wk.i, a.q_off + q_last, e_begin, e_end);
+    tile_range(a, wk.b, wk.h, wk.i, a.q_off + (a.qpack ? a.qpack - 1 : q_last), e_begin, e_end);
     if (a.nsplit > 1) {  // this workgroup's share of the row's tiles
         const int per = (e_end - e_begin + a.nsplit - 1) / a.nsplit;
         e_begin = min(e_end, e_begin + split * per);
@@ -240,10 +244,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     // Masks of a partial tile (causal diagonal or ragged tail): keys past the
     // lane's query row or past S get -inf. Only partial tiles take this branch.
     auto mask_tile = [&](f32x16 (&sacc)[2], int key0) {
-        const bool need_mask = (a.causal && key0 + BKV - 1 > a.q_off + qw0) || (key0 + BKV > a.Skv);
+        const bool need_mask = (a.causal && key0 + BKV - 1 > a.q_off + (a.qpack ? 0 : qw0)) || (key0 + BKV > a.Skv);
         if (need_mask) {
             int lim = min(BKV - 1, a.Skv - 1 - key0);         // last visible key offset
-            if (a.causal) lim = min(lim, a.q_off + qrow - key0);
+            if (a.causal) lim = min(lim, a.q_off + qpos - key0);
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll

@@ -534,6 +534,21 @@ int decode_attn_config(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa
     }
     a.NQ = (int)ceil_div(q->S, a.block_q);
     a.NK = (int)ceil_div(length, a.block_kv);
+    // One selection row shared by the heads (or none): the query heads of a GQA
+    // group are packed into the rows of one workgroup, so each kept K/V tile is
+    // read once per kv head instead of once per query head.
+    const int G = q->H / k_cache->H;
+    if (G > 1 && a.block_kv == 64 && (!sel || (sel->H == 1 && sel->NQ == 1))) {
+        nsa::AttnArgs p = a;
+        const int64_t rows = (int64_t)G * q->S;
+        p.qpack = q->S;
+        p.Hq = k_cache->H;
+        p.Hsel = 1;
+        p.S = (int)rows;
+        p.block_q = rows <= 32 ? 32 : rows <= 64 ? 64 : rows <= 96 ? 96 : 128;
+        p.NQ = (int)ceil_div(rows, p.block_q);
+        if (rows < INT32_MAX && nsa::attn_mfma_supported(p, q->dtype == NSA_BF16)) a = p;
+    }
     if (nsa::attn_mfma_supported(a, q->dtype == NSA_BF16)) {
         const int64_t work = std::max<int64_t>((int64_t)a.B * a.Hq * a.NQ, 1);
         const int64_t want = ceil_div(2048, work);

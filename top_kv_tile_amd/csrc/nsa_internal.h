@@ -57,9 +57,15 @@ struct AttnArgs {
     int Skv;                  // keys per head (== S outside decoding)
     int64_t kv_rows;          // rows per kv head in memory (>= Skv; a cache's capacity)
     int q_off;                // absolute key position of query token 0 (causal: u <= q_off + t)
-    int nsplit;               // > 1: each row's tiles are split over nsplit workgroups (MFMA path)
-    float* part_o;            // split partials: (B*Hq*S, nsplit, D) unnormalised O
-    float* part_ml;           // (B*Hq*S, nsplit, 2): exponent reference (log2 units) and sum
+    int nsplit = 1;           // > 1: each row's tiles are split over nsplit workgroups (MFMA path)
+    float* part_o = nullptr;  // split partials: (B*Hq*S, nsplit, D) unnormalised O
+    float* part_ml = nullptr; // (B*Hq*S, nsplit, 2): exponent reference (log2 units) and sum
+    // > 0 (MFMA path): query heads packed per kv head. The call then describes
+    // Hq = Hkv heads of S = G * qpack rows each, row r being token r % qpack of
+    // query head g * G + r / qpack (the same memory, since a GQA group's heads
+    // are adjacent); every row uses selection row (b, 0, 0), so the selection
+    // is shared by the heads and has one query tile.
+    int qpack = 0;
     const int32_t* row_ptr;   // null = dense
     const int32_t* col_idx;
     int B, Hq, Hkv, Hsel, S, D, NQ, NK, block_q, block_kv;

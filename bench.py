@@ -173,6 +173,105 @@ def backward_timing(q, k, v, out, lse, sel, w: synth.Workload, fwd_flops: float,
             "kernels": "delta, kv-major index (3), bwd_dq_mfma_kernel<128,4>, bwd_dkdv_mfma_kernel<128>"}
 
 
+def _event_ms(fn, calls: int, stream) -> float:
+    """Mean duration of fn() in ms, HIP events around each call on `stream`."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for e in ev:
+        e[0].record(stream)
+        fn()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def decode_timing(q, k, v, w: synth.Workload, calls: int = 20):
+    """One decoding step over the workload's keys and values as a KV cache: the
+    last token attends to the first S - 1 cached tokens plus itself.
+
+    * pool update: the pooled key of the cache's last (partial) tile;
+    * select: scores of the new token's query against every pooled key tile,
+      per query head, with the sink tile pinned, and the top-k;
+    * attention: over the kept tiles (split over workgroups, partials merged).
+    Also the dense attention over the whole cache (query heads of a GQA group
+    packed, so every K/V byte is read once). HBM bytes: the K and V tiles read
+    (each kept tile of each query head, or the whole cache once)."""
+    dev = q.device
+    stream = torch.cuda.current_stream()
+    L = w.S
+    q1 = q[:, :, L - 1:L].contiguous()
+    nk = -(-L // w.block_kv)
+    pooled = torch.zeros(w.B, w.Hkv, nk, w.D, dtype=torch.float32, device=dev)
+    tkt.nsa_decode_pool_update(k, 0, L - 1, w.block_kv, pooled)
+    spec = tkt.SparseSpec(budget=w.budget, block_q=32, block_kv=w.block_kv, head_shared=w.head_shared)
+    pins = np.zeros((1, 1, 1, nk), np.int8)
+    pins[..., 0] = 1
+    sws = torch.empty(1 << 24, dtype=torch.uint8, device=dev)
+    aws = torch.empty(1 << 24, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q1)
+    lse = torch.empty(q1.shape[:3], dtype=torch.float32, device=dev)
+    box = {}
+
+    def upd():
+        tkt.nsa_decode_pool_update(k, L - 1, L, w.block_kv, pooled)
+
+    def sel():
+        box["sel"] = tkt.nsa_decode_select(q1, pooled, L, L - 1, spec, pins=pins, workspace=sws)
+
+    def att():
+        tkt.nsa_decode_attn(q1, k, v, L, L - 1, box["sel"], out=out, lse=lse, workspace=aws)
+
+    def dense():
+        tkt.nsa_decode_attn(q1, k, v, L, L - 1, None, out=out, lse=lse, workspace=aws)
+
+    log("[bench] decode step")
+    for fn in (upd, sel, att, dense):
+        fn()
+    torch.cuda.synchronize()
+    up_ms, sel_ms, att_ms, dense_ms = (_event_ms(fn, calls, stream) for fn in (upd, sel, att, dense))
+    nnz = int(box["sel"].nnz)
+    heads_per_row = w.Hq if w.head_shared else 1
+    tile_bytes = 2 * w.block_kv * w.D * q.element_size()
+    att_bytes = float(nnz * heads_per_row * tile_bytes)
+    dense_bytes = float(2 * w.B * w.Hkv * L * w.D * q.element_size())
+    return {"cache_tokens": L, "new_tokens": 1, "kept_tiles": nnz,
+            "pool_update_us": round(up_ms * 1e3, 1), "select_us": round(sel_ms * 1e3, 1),
+            "attn_us": round(att_ms * 1e3, 1), "step_us": round((up_ms + sel_ms + att_ms) * 1e3, 1),
+            "attn_bytes": att_bytes, "attn_GBps": round(att_bytes / (att_ms * 1e-3) / 1e9, 1),
+            "attn_frac_hbm": round(att_bytes / (att_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "dense_attn_us": round(dense_ms * 1e3, 1), "dense_bytes": dense_bytes,
+            "dense_GBps": round(dense_bytes / (dense_ms * 1e-3) / 1e9, 1),
+            "dense_frac_hbm": round(dense_bytes / (dense_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "kernels": "pool_kernel (tile range), score_kernel, topk_kernel, attn_mfma_kernel<128,1> + "
+                       "attn_combine_kernel"}
+
+
+def reorder_timing(q, w: synth.Workload, calls: int = 10):
+    """Hilbert order of a 256 x 512 token grid (host), then the row gather of q
+    along it and the scatter back on the GPU; HBM bytes = one read and one write of q."""
+    dev = q.device
+    stream = torch.cuda.current_stream()
+    rows = 256
+    cols = w.S // rows
+    t0 = time.perf_counter()
+    perm = torch.from_numpy(tkt.nsa_curve_order(tkt.NSA_CURVE_HILBERT, (rows, cols))).to(dev)
+    host_ms = (time.perf_counter() - t0) * 1e3
+    y = torch.empty_like(q)
+    z = torch.empty_like(q)
+    tkt.nsa_permute_tokens(q, perm, out=y)
+    tkt.nsa_permute_tokens(y, perm, inverse=True, out=z)
+    torch.cuda.synchronize()
+    if not torch.equal(z, q):
+        raise RuntimeError("token reordering did not round-trip")
+    g_ms = _event_ms(lambda: tkt.nsa_permute_tokens(q, perm, out=y), calls, stream)
+    s_ms = _event_ms(lambda: tkt.nsa_permute_tokens(y, perm, inverse=True, out=z), calls, stream)
+    nbytes = float(2 * q.numel() * q.element_size())
+    return {"grid": [rows, cols], "curve": "hilbert", "order_host_ms": round(host_ms, 2),
+            "gather_us": round(g_ms * 1e3, 1), "scatter_us": round(s_ms * 1e3, 1), "bytes": nbytes,
+            "gather_GBps": round(nbytes / (g_ms * 1e-3) / 1e9, 1),
+            "gather_frac_hbm": round(nbytes / (g_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "scatter_GBps": round(nbytes / (s_ms * 1e-3) / 1e9, 1), "kernel": "permute_rows_kernel<16>"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +281,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the separate timing of the attention gradients")
     ap.add_argument("--backward-steps", type=int, default=5)
+    ap.add_argument("--no-decode", action="store_true", help="skip the decoding-step timing")
+    ap.add_argument("--no-reorder", action="store_true", help="skip the token-reordering timing")
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel 3 times "
@@ -292,6 +393,11 @@ def main():
     }
     if not args.no_backward:
         res["backward"] = backward_timing(q, k, v, out, lse, sel, w, full_flops, args.backward_steps)
+    if not args.no_decode:
+        res["decode"] = decode_timing(q, k, v, w)
+    if not args.no_reorder:
+        log("[bench] token reordering")
+        res["reorder"] = reorder_timing(q, w)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample)")
         res["cpu_baseline"] = cpu_baseline(inp, w)

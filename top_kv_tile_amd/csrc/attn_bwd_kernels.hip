@@ -437,9 +437,9 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_mfma_kernel(AttnBwdArgs a) 
 // Workgroup = 4 waves on one kv tile of 64 keys; wave w owns keys 32 (w & 1)
 // .. + 31 and queries 32 (w >> 1) .. + 31 of every 64-query chunk ("unit").
 // K and V fragments stay in registers. Units are walked head by head over the
-// group, each head's query tiles ascending, and streamed through three LDS
+// group, each head's query tiles ascending, and streamed through four LDS
 // stages (Q chunk, dO chunk, and per wave the LSE and Delta of its 32 queries,
-// all by buffer-to-LDS DMA): unit n + 2 is in flight while unit n is computed,
+// all by buffer-to-LDS DMA): units n + 1 .. n + 3 are in flight while unit n is computed,
 // and every wave issues the same number of loads per unit, so a partial vmcnt
 // wait tells unit n has landed. At the end the two waves of each key half add
 // their partial dK^T / dV^T through LDS.
@@ -453,9 +453,10 @@ struct Unit {
 template <int D>
 struct DkdvLds {
     static constexpr int TILEB = 64 * D * 2;
-    static constexpr int NST = 3;
+    static constexpr int NST = 4;  // stages (at most 5: the waits below count up to 3 units in flight)
     static constexpr int SIDE = 4 * 2 * 64 * 4;        // per stage: 4 waves x (LSE, Delta) x 64 floats
     static constexpr int BYTES = NST * 2 * TILEB + NST * SIDE;
+    static_assert(NST >= 3 && NST <= 5, "pipeline depth");
     static_assert(2 * 2 * (D / 32) * 16 * 64 * 4 <= NST * 2 * TILEB, "reduction buffer fits the stages");
 };
 
@@ -561,40 +562,82 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
         dv[m] = (f32x16){};
     }
 
+    // Pipeline: unit `cur` in stage st, the next units nx[0], nx[1], ... in
+    // the following stages (valid while hv[]). NST - 2 of them are in flight
+    // when an iteration starts, and it issues one more into the stage the
+    // previous unit used.
+    constexpr int NST = L::NST;
     Unit cur;
     cur.hh = -1;
     cur.e = cur.e_end = 0;
     cur.c = cur.nch = 0;
     cur.i = 0;
     bool have = settle(cur);
-    bool have1 = false;
-    Unit nx1 = cur;
+    Unit nx[NST - 1];
+    bool hv[NST - 1];
+#pragma unroll
+    for (int x = 0; x < NST - 1; ++x) {
+        nx[x] = cur;
+        hv[x] = false;
+    }
     if (have) {
         issue(cur, 0);
-        nx1 = advance(cur, have1);
-        if (have1) issue(nx1, 1);
+        bool ok = true;
+        Unit prev = cur;
+#pragma unroll
+        for (int x = 0; x < NST - 2; ++x) {
+            if (ok) {
+                prev = advance(prev, ok);
+                if (ok) {
+                    nx[x] = prev;
+                    hv[x] = true;
+                    issue(prev, x + 1);
+                }
+            }
+        }
     }
     int st = 0;
     while (have) {
-        // Unit `cur` (stage st) has landed once at most the next unit's loads are outstanding.
-        if (have1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_UNIT));
-        else __builtin_amdgcn_s_waitcnt(kVmcnt0);
-        bare_barrier();  // all waves: unit cur visible, and stage (st + 2) % 3 no longer read
-        bool have2 = false;
-        Unit nx2 = nx1;
-        if (have1) {
-            nx2 = advance(nx1, have2);
-            if (have2) issue(nx2, st == 0 ? 2 : st - 1);
+        // Unit `cur` (stage st) has landed once at most the loads of the units
+        // issued after it are outstanding (PER_UNIT per unit, in issue order).
+        int pending = 0;
+#pragma unroll
+        for (int x = 0; x < NST - 2; ++x) pending += hv[x] ? 1 : 0;
+        if (pending == 0) __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        else if (pending == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_UNIT));
+        else if (pending == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER_UNIT));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * PER_UNIT));
+        bare_barrier();  // all waves: unit cur visible, and the previous unit's stage no longer read
+        if (hv[NST - 3]) {
+            bool ok = false;
+            const Unit u = advance(nx[NST - 3], ok);
+            if (ok) {
+                nx[NST - 2] = u;
+                hv[NST - 2] = true;
+                issue(u, (st + NST - 1) % NST);
+            }
         }
         const char* qt = qst(st);
         const char* dt = dost(st);
         // S = Q K^T and dP = dO V^T for this wave's 32 queries x 32 keys.
         f32x16 s = (f32x16){}, dp = (f32x16){};
         const int qr = 32 * qs + l32;
+        {
+            // All sixteen row fragments are read before the first product: the
+            // scheduling fence keeps the compiler from placing each read right
+            // before its product, which exposed the LDS latency sixteen times.
+            bf16x8 qa[KSTEPS], da[KSTEPS];
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            s = mfma(row_frag<D, true>(qt, qr, 2 * ks + hf), kf[ks], s);
-            dp = mfma(row_frag<D, true>(dt, qr, 2 * ks + hf), vf[ks], dp);
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                qa[ks] = row_frag<D, true>(qt, qr, 2 * ks + hf);
+                da[ks] = row_frag<D, true>(dt, qr, 2 * ks + hf);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                s = mfma(qa[ks], kf[ks], s);
+                dp = mfma(da[ks], vf[ks], dp);
+            }
         }
         // Lane holds key mykey (column) and queries 32 qs + 8 q + 4 hf + e (chunk rows) at [4 q + e].
         // Element masks only where this wave's block is partial: under causal
@@ -628,17 +671,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
         // dV^T += dO^T P and dK^T += Q^T dS; contraction over this wave's queries,
         // k-step s covering rows 32 qs + 16 s + 4 hf + (0..3) and + 8.
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+        for (int s2 = 0; s2 < 2; ++s2) {
+            bf16x8 ta[DBLK], tb[DBLK];  // read ahead of the products, as above
 #pragma unroll
             for (int m = 0; m < DBLK; ++m) {
-                dv[m] = mfma(tr_frag<D>(dt, 32 * qs + 16 * s2, m, lane), pf[s2], dv[m]);
-                dk[m] = mfma(tr_frag<D>(qt, 32 * qs + 16 * s2, m, lane), dsf[s2], dk[m]);
+                ta[m] = tr_frag<D>(dt, 32 * qs + 16 * s2, m, lane);
+                tb[m] = tr_frag<D>(qt, 32 * qs + 16 * s2, m, lane);
             }
-        cur = nx1;
-        have = have1;
-        nx1 = nx2;
-        have1 = have2;
-        st = (st == 2) ? 0 : st + 1;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < DBLK; ++m) {
+                dv[m] = mfma(ta[m], pf[s2], dv[m]);
+                dk[m] = mfma(tb[m], dsf[s2], dk[m]);
+            }
+        }
+        cur = nx[0];
+        have = hv[0];
+#pragma unroll
+        for (int x = 0; x < NST - 2; ++x) {
+            nx[x] = nx[x + 1];
+            hv[x] = hv[x + 1];
+        }
+        hv[NST - 2] = false;
+        st = (st == NST - 1) ? 0 : st + 1;
     }
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();  // every wave is done with the stages (nothing is in flight any more)

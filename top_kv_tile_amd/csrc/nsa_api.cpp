@@ -345,12 +345,23 @@ void fill_sizes(const Plan& p, const nsa_spec* spec, nsa_sizes* out, int32_t* ro
 }
 
 int score_and_topk(const Plan& p, const nsa_spec* spec, const float* qh, const float* kh, int Hk, int NKs,
-                   const WsLayout& w, char* ws, nsa_selection* out, hipStream_t stream);
+                   const WsLayout& w, char* ws, nsa_selection* out, hipStream_t stream, const uint64_t* pin_words,
+                   const uint64_t* drop_words);
 
 // Enqueues the selection of a built plan (row_ptr present) for tensors q, k
 // whose geometry the plan was built from.
+// Device-resident copy of a plan's row_ptr and mask words (a plan handle keeps
+// one on the device of its first planned selection).
+struct PlanDevice {
+    int dev = -1;
+    void* buf = nullptr;
+    int32_t* row_ptr = nullptr;
+    uint64_t* pin_words = nullptr;
+    uint64_t* drop_words = nullptr;
+};
+
 int run_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, const Plan& p, nsa_selection* out,
-               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+               void* workspace, size_t workspace_bytes, hipStream_t stream, const PlanDevice* pd = nullptr) {
     const Geo& g = p.g;
     if (p.dense && !spec->force) return NSA_DENSE;
     if (g.rows > 0 && (!out->keep || !out->row_ptr)) return NSA_ERR_NULL_ARG;
@@ -373,7 +384,15 @@ int run_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, c
     out->budget = spec->budget;
 
     char* ws = (char*)workspace;
-    {
+    const uint64_t* pin_words = p.has_pins ? (const uint64_t*)(ws + w.pinw) : nullptr;
+    const uint64_t* drop_words = p.has_drops ? (const uint64_t*)(ws + w.dropw) : nullptr;
+    if (pd) {  // the plan is on the device already: only row_ptr is copied, device to device
+        const hipError_t e = hipMemcpyAsync(out->row_ptr, pd->row_ptr, p.row_ptr.size() * sizeof(int32_t),
+                                            hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        pin_words = pd->pin_words;
+        drop_words = pd->drop_words;
+    } else {
         void* dst[3] = {out->row_ptr, ws + w.pinw, ws + w.dropw};
         const void* src[3] = {p.row_ptr.data(), p.pin_words.data(), p.drop_words.data()};
         size_t bytes[3] = {p.row_ptr.size() * sizeof(int32_t), p.has_pins ? p.pin_words.size() * 8 : 0,
@@ -388,12 +407,14 @@ int run_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, c
     int Hk;
     int st;
     if ((st = run_pool(q, k, spec, g, w, ws, stream, &qh, &kh, &Hk)) != NSA_OK) return st;
-    return score_and_topk(p, spec, qh, kh, Hk, g.NK, w, ws, out, stream);
+    return score_and_topk(p, spec, qh, kh, Hk, g.NK, w, ws, out, stream, pin_words, drop_words);
 }
 
 // Scores chunk by chunk of selection heads, each followed by its top-k and CSR.
+// pin_words / drop_words: the plan's bit-packed masks on the device (or null).
 int score_and_topk(const Plan& p, const nsa_spec* spec, const float* qh, const float* kh, int Hk, int NKs,
-                   const WsLayout& w, char* ws, nsa_selection* out, hipStream_t stream) {
+                   const WsLayout& w, char* ws, nsa_selection* out, hipStream_t stream, const uint64_t* pin_words,
+                   const uint64_t* drop_words) {
     const Geo& g = p.g;
     float* scores = (float*)(ws + w.scores);
     for (int h0 = 0; h0 < g.Hsel; h0 += w.chunk) {
@@ -414,10 +435,10 @@ int score_and_topk(const Plan& p, const nsa_spec* spec, const float* qh, const f
         ta.block_kv = spec->block_kv;
         ta.q_off = g.q_off;
         ta.budget = spec->budget;
-        ta.pin_words = p.has_pins ? (const uint64_t*)(ws + w.pinw) : nullptr;
+        ta.pin_words = pin_words;
         ta.pb = p.pb;
         ta.ph = p.ph;
-        ta.drop_words = p.has_drops ? (const uint64_t*)(ws + w.dropw) : nullptr;
+        ta.drop_words = drop_words;
         ta.db = p.db;
         ta.dh = p.dh;
         ta.row_ptr = out->row_ptr;
@@ -667,6 +688,19 @@ struct nsa_plan {
     nsa_spec spec;
     nsa_tensor qshape, kshape;  // shapes and dtype only
     Plan p;
+    // row_ptr and mask words on the device of the first planned selection,
+    // uploaded once (later selections on that device copy nothing from the host)
+    mutable std::mutex mu;
+    mutable PlanDevice d;
+    ~nsa_plan() {
+        if (!d.buf) return;
+        int cur = 0;
+        const bool restore = hipGetDevice(&cur) == hipSuccess && cur != d.dev;
+        if (restore) (void)hipSetDevice(d.dev);
+        (void)hipDeviceSynchronize();  // a planned selection may still read the copy
+        (void)hipFree(d.buf);
+        if (restore) (void)hipSetDevice(cur);
+    }
 };
 
 namespace {
@@ -846,7 +880,38 @@ int nsa_select_planned(const nsa_plan* plan, const nsa_tensor* q, const nsa_tens
         if (q->dtype != pq.dtype || k->dtype != pk.dtype) return NSA_ERR_BAD_DTYPE;
         if (q->B != pq.B || q->H != pq.H || q->S != pq.S || q->D != pq.D) return NSA_ERR_BAD_SHAPE;
         if (k->B != pk.B || k->H != pk.H || k->S != pk.S || k->D != pk.D) return NSA_ERR_BAD_SHAPE;
-        return run_select(q, k, &plan->spec, plan->p, out, workspace, workspace_bytes, (hipStream_t)stream);
+        const Plan& p = plan->p;
+        const PlanDevice* pd = nullptr;
+        if (!(p.dense && !plan->spec.force) && p.g.rows > 0) {
+            int dev = 0;
+            hipError_t e = hipGetDevice(&dev);
+            if (e != hipSuccess) return hip_fail(e);
+            std::lock_guard<std::mutex> lock(plan->mu);
+            if (plan->d.dev < 0) {  // first planned selection: upload the plan to this device
+                const size_t rb = align256(p.row_ptr.size() * sizeof(int32_t));
+                const size_t pb = align256(p.has_pins ? p.pin_words.size() * 8 : 0);
+                const size_t db = align256(p.has_drops ? p.drop_words.size() * 8 : 0);
+                void* buf = nullptr;
+                if ((e = hipMalloc(&buf, rb + pb + db)) != hipSuccess) return hip_fail(e);
+                char* c = (char*)buf;
+                e = hipMemcpy(c, p.row_ptr.data(), p.row_ptr.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+                if (e == hipSuccess && pb)
+                    e = hipMemcpy(c + rb, p.pin_words.data(), p.pin_words.size() * 8, hipMemcpyHostToDevice);
+                if (e == hipSuccess && db)
+                    e = hipMemcpy(c + rb + pb, p.drop_words.data(), p.drop_words.size() * 8, hipMemcpyHostToDevice);
+                if (e != hipSuccess) {
+                    (void)hipFree(buf);
+                    return hip_fail(e);
+                }
+                plan->d.dev = dev;
+                plan->d.buf = buf;
+                plan->d.row_ptr = (int32_t*)c;
+                plan->d.pin_words = pb ? (uint64_t*)(c + rb) : nullptr;
+                plan->d.drop_words = db ? (uint64_t*)(c + rb + pb) : nullptr;
+            }
+            if (plan->d.dev == dev) pd = &plan->d;  // on another device: the host upload path
+        }
+        return run_select(q, k, &plan->spec, p, out, workspace, workspace_bytes, (hipStream_t)stream, pd);
     } catch (...) {
         return NSA_ERR_UNSUPPORTED;
     }
@@ -1069,7 +1134,9 @@ int nsa_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t l
             Hk = 1;
             NKs = g.NK;
         }
-        return score_and_topk(p, spec, qh, kh, Hk, NKs, w, ws, out, stream);
+        return score_and_topk(p, spec, qh, kh, Hk, NKs, w, ws, out, stream,
+                              p.has_pins ? (const uint64_t*)(ws + w.pinw) : nullptr,
+                              p.has_drops ? (const uint64_t*)(ws + w.dropw) : nullptr);
     } catch (...) {
         return NSA_ERR_UNSUPPORTED;
     }

@@ -164,20 +164,32 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qh
     const float* b1p = Bm + (int64_t)min(j0 + 32 + l32, NK - 1) * D + 8 * hf;
 
     f32x16 c00 = {}, c01 = {}, c10 = {}, c11 = {};
-#pragma unroll 2
-    for (int kc = 0; kc < D; kc += 16) {
-        f32x4 a0[2], a1[2], b0[2], b1[2];
+    // Operands of 16 contraction indices per lane-half group: 8 x 16 bytes per
+    // lane. Chunks are loaded two ahead of their products (three buffers),
+    // so the L2 latency of a chunk overlaps the products of the two before it.
+    constexpr int NC = D / 16;
+    f32x4 buf[3][8];
+    auto load = [&](f32x4 (&o)[8], int kc) {
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
-            a0[v] = *(const f32x4*)(a0p + kc + 4 * v);
-            a1[v] = *(const f32x4*)(a1p + kc + 4 * v);
-            b0[v] = *(const f32x4*)(b0p + kc + 4 * v);
-            b1[v] = *(const f32x4*)(b1p + kc + 4 * v);
+            o[0 + v] = *(const f32x4*)(a0p + kc + 4 * v);
+            o[2 + v] = *(const f32x4*)(a1p + kc + 4 * v);
+            o[4 + v] = *(const f32x4*)(b0p + kc + 4 * v);
+            o[6 + v] = *(const f32x4*)(b1p + kc + 4 * v);
         }
+    };
+    load(buf[0], 0);
+    if (NC > 1) load(buf[1], 16);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        if (c + 2 < NC) load(buf[(c + 2) % 3], 16 * (c + 2));
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products
+        const f32x4 (&o)[8] = buf[c % 3];
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
-            const float x0 = a0[st >> 2][st & 3], x1 = a1[st >> 2][st & 3];
-            const float y0 = b0[st >> 2][st & 3], y1 = b1[st >> 2][st & 3];
+            const float x0 = o[0 + (st >> 2)][st & 3], x1 = o[2 + (st >> 2)][st & 3];
+            const float y0 = o[4 + (st >> 2)][st & 3], y1 = o[6 + (st >> 2)][st & 3];
             c00 = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, y0, c00, 0, 0, 0);
             c01 = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, y1, c01, 0, 0, 0);
             c10 = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, y0, c10, 0, 0, 0);

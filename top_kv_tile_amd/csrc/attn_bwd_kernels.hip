@@ -30,6 +30,7 @@
 #include "device_common.h"
 
 #include <math.h>
+#include <type_traits>
 
 namespace nsa {
 namespace {
@@ -674,23 +675,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
         const float* lsp = side(st, wave, 0) + 4 * hf;
         const float* dlp = side(st, wave, 1) + 4 * hf;
         bf16x8 pf[2], dsf[2];
+        auto p_ds = [&](auto masked) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f32x4 lo = *(const f32x4*)(lsp + 8 * q);
-            const f32x4 de = *(const f32x4*)(dlp + 8 * q);
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 lo = *(const f32x4*)(lsp + 8 * q);
+                const f32x4 de = *(const f32x4*)(dlp + 8 * q);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int x = 4 * q + e;
-                float p = fast_exp2(__builtin_fmaf(s[x], a.scale_log2, -kLog2e * lo[e]));
-                if (need_mask) {
-                    const int t = tq0 + 8 * q + 4 * hf + e;
-                    p = (t < t_lim && key_lim <= t) ? p : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    const int x = 4 * q + e;
+                    float p = fast_exp2(__builtin_fmaf(s[x], a.scale_log2, -kLog2e * lo[e]));
+                    if (decltype(masked)::value) {
+                        const int t = tq0 + 8 * q + 4 * hf + e;
+                        p = (t < t_lim && key_lim <= t) ? p : 0.f;
+                    }
+                    const float ds = p * (dp[x] - de[e]);
+                    pf[x >> 3][x & 7] = (__bf16)p;
+                    dsf[x >> 3][x & 7] = (__bf16)ds;
                 }
-                const float ds = p * (dp[x] - de[e]);
-                pf[x >> 3][x & 7] = (__bf16)p;
-                dsf[x >> 3][x & 7] = (__bf16)ds;
             }
-        }
+        };
+        // Two copies, so that full blocks (the common case) carry no mask arithmetic.
+        if (need_mask) p_ds(std::true_type{});
+        else p_ds(std::false_type{});
         // dV^T += dO^T P and dK^T += Q^T dS; contraction over this wave's queries,
         // k-step s covering rows 32 qs + 16 s + 4 hf + (0..3) and + 8.
 #pragma unroll

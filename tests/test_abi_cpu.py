@@ -188,7 +188,10 @@ def test_backward_workspace_size(L):
     sel = N._Selection(keep=1, row_ptr=1, col_idx=1, nnz=300, B=2, H=4, NQ=8, NK=16, block_q=128, block_kv=64,
                        seq_q=1000, seq_kv=1000)
     assert L.nsa_attn_bwd_workspace_size(ctypes.byref(q), ctypes.byref(k), ctypes.byref(sel), ctypes.byref(n)) == 0
-    assert n.value == a(2 * 4 * 1000 * 4) + a(2 * 4 * 16 * 4) + a((2 * 4 * 16 + 1) * 4) + a(300 * 4)
+    # Delta, column counts per quarter of the query tiles, col_ptr, per-2048-column block sums + total, row_idx
+    cols = 2 * 4 * 16
+    assert n.value == (a(2 * 4 * 1000 * 4) + a(cols * 4 * 4) + a((cols + 1) * 4) + a((-(-cols // 2048) + 1) * 4)
+                       + a(300 * 4))
     bad = N._Selection(keep=1, row_ptr=1, col_idx=1, nnz=300, B=2, H=3, NQ=8, NK=16, block_q=128, block_kv=64,
                        seq_q=1000, seq_kv=1000)
     assert L.nsa_attn_bwd_workspace_size(ctypes.byref(q), ctypes.byref(k), ctypes.byref(bad), ctypes.byref(n)) == -2

@@ -74,57 +74,110 @@ __global__ __launch_bounds__(256) void delta_kernel(const void* out, const void*
     if (r < rows && part == 0) delta[r] = acc;
 }
 
-// counts[bh * NK + j] = number of query tiles i with keep[bh, i, j] != 0.
-// Grid: blocks of 256 columns, ceil(NK / 256) per slab bh.
-__global__ __launch_bounds__(256) void colcount_kernel(const int8_t* keep, int NQ, int NK, int32_t* counts) {
-    const int per = (NK + 255) / 256;
+// Column index of the keep flags. A workgroup takes 64 columns of one slab
+// (one lane per column, so each wave load reads 64 consecutive flags) and its
+// four waves take a quarter of the query tiles each.
+// counts4[(bh * NK + j) * 4 + w] = query tiles i of quarter w with keep[bh, i, j] != 0.
+__global__ __launch_bounds__(256) void colcount_kernel(const int8_t* keep, int NQ, int NK, int32_t* counts4) {
+    const int per = (NK + 63) / 64;
     const int64_t bh = blockIdx.x / per;
-    const int j = (int)(blockIdx.x % per) * 256 + threadIdx.x;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int j = (int)(blockIdx.x % per) * 64 + lane;
     if (j >= NK) return;
+    const int q = (NQ + 3) / 4;
+    const int i0 = min(NQ, w * q), i1 = min(NQ, i0 + q);
     const int8_t* col = keep + bh * NQ * (int64_t)NK + j;
     int c = 0;
-    for (int i = 0; i < NQ; ++i) c += col[(int64_t)i * NK] != 0;
-    counts[bh * NK + j] = c;
+#pragma unroll 8
+    for (int i = i0; i < i1; ++i) c += col[(int64_t)i * NK] != 0;
+    counts4[(bh * NK + j) * 4 + w] = c;
 }
 
-// Exclusive prefix sum of n counts into col_ptr[0 .. n] (one workgroup),
-// clamped to cap (the capacity of row_idx) so that flags that disagree with the
-// CSR cannot index past it.
-__global__ __launch_bounds__(1024) void colscan_kernel(const int32_t* counts, int64_t n, int32_t cap,
-                                                       int32_t* col_ptr) {
-    __shared__ int32_t part[1024];
-    const int tid = threadIdx.x;
-    const int64_t per = (n + 1023) / 1024;
-    const int64_t lo = min(n, tid * per), hi = min(n, lo + per);
-    int32_t s = 0;
-    for (int64_t x = lo; x < hi; ++x) s += counts[x];
-    part[tid] = s;
+// Exclusive prefix sum over columns of the column totals (sum of the four
+// quarters): col_ptr[0 .. n], in three launches. Block b of colscan_block
+// scans 2048 columns and writes its total to sums[b]; colscan_sums scans the
+// block totals (one workgroup); colscan_add adds each block's offset. Offsets
+// are clamped to cap (the capacity of row_idx) so that flags that disagree
+// with the CSR cannot index past it.
+__device__ __forceinline__ int32_t block_scan_256(int32_t v, int32_t* sh, int32_t& total) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int32_t x = v;  // inclusive scan within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) sh[w] = x;
     __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan
-        const int32_t v = tid >= o ? part[tid - o] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
+    int32_t off = 0;
+    for (int u = 0; u < w; ++u) off += sh[u];
+    total = sh[0] + sh[1] + sh[2] + sh[3];
+    __syncthreads();
+    return off + x - v;  // exclusive
+}
+__global__ __launch_bounds__(256) void colscan_block_kernel(const int32_t* counts4, int64_t n, int32_t* col_ptr,
+                                                            int32_t* sums) {
+    __shared__ int32_t sh[4];
+    const int64_t base = (int64_t)blockIdx.x * 2048 + threadIdx.x * 8;
+    int32_t v[8], t = 0;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+        const int64_t c = base + x;
+        if (c < n) {
+            const int4 q = *(const int4*)(counts4 + c * 4);
+            v[x] = q.x + q.y + q.z + q.w;
+        } else {
+            v[x] = 0;
+        }
+        t += v[x];
     }
-    int32_t run = part[tid] - s;
-    for (int64_t x = lo; x < hi; ++x) {
-        col_ptr[x] = min(run, cap);
-        run += counts[x];
+    int32_t total;
+    int32_t run = block_scan_256(t, sh, total);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+        if (base + x < n) col_ptr[base + x] = run;
+        run += v[x];
     }
-    if (tid == 1023) col_ptr[n] = min(part[1023], cap);
+    if (threadIdx.x == 0) sums[blockIdx.x] = total;
+}
+__global__ __launch_bounds__(256) void colscan_sums_kernel(int32_t* sums, int nb) {
+    __shared__ int32_t sh[4];
+    int32_t carry = 0;
+    for (int b0 = 0; b0 < nb; b0 += 256) {
+        const int b = b0 + threadIdx.x;
+        const int32_t v = b < nb ? sums[b] : 0;
+        int32_t total;
+        const int32_t ex = block_scan_256(v, sh, total);
+        if (b < nb) sums[b] = carry + ex;  // exclusive offset of block b
+        carry += total;
+    }
+    if (threadIdx.x == 0) sums[nb] = carry;
+}
+__global__ __launch_bounds__(256) void colscan_add_kernel(int32_t* col_ptr, const int32_t* sums, int64_t n,
+                                                          int nb, int32_t cap) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c < n) col_ptr[c] = min(col_ptr[c] + sums[c / 2048], cap);
+    if (c == n) col_ptr[n] = min(sums[nb], cap);
 }
 
-// row_idx[col_ptr[bh * NK + j] ..] = the query tiles keeping (bh, j), ascending.
-__global__ __launch_bounds__(256) void colfill_kernel(const int8_t* keep, int NQ, int NK, const int32_t* col_ptr,
-                                                      int32_t* row_idx) {
-    const int per = (NK + 255) / 256;
+// row_idx[col_ptr[bh * NK + j] ..] = the query tiles keeping (bh, j), ascending:
+// the same geometry as colcount, each wave starting after the flags of the
+// quarters before it.
+__global__ __launch_bounds__(256) void colfill_kernel(const int8_t* keep, int NQ, int NK, const int32_t* counts4,
+                                                      const int32_t* col_ptr, int32_t* row_idx) {
+    const int per = (NK + 63) / 64;
     const int64_t bh = blockIdx.x / per;
-    const int j = (int)(blockIdx.x % per) * 256 + threadIdx.x;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int j = (int)(blockIdx.x % per) * 64 + lane;
     if (j >= NK) return;
+    const int q = (NQ + 3) / 4;
+    const int i0 = min(NQ, w * q), i1 = min(NQ, i0 + q);
+    const int64_t c = bh * NK + j;
+    int32_t p = col_ptr[c];
+    for (int u = 0; u < w; ++u) p += counts4[c * 4 + u];
+    const int32_t p_end = col_ptr[c + 1];
     const int8_t* col = keep + bh * NQ * (int64_t)NK + j;
-    int32_t p = col_ptr[bh * NK + j];
-    const int32_t p_end = col_ptr[bh * NK + j + 1];
-    for (int i = 0; i < NQ && p < p_end; ++i)
+    for (int i = i0; i < i1 && p < p_end; ++i)
         if (col[(int64_t)i * NK] != 0) row_idx[p++] = i;
 }
 
@@ -960,17 +1013,23 @@ hipError_t launch_bwd_delta(const void* out, const void* dout, int bf16, int64_t
     return hipGetLastError();
 }
 
-hipError_t launch_kv_major_index(const int8_t* keep, int BH, int NQ, int NK, int32_t cap, int32_t* counts,
-                                 int32_t* col_ptr, int32_t* row_idx, hipStream_t stream) {
+hipError_t launch_kv_major_index(const int8_t* keep, int BH, int NQ, int NK, int32_t cap, int32_t* counts4,
+                                 int32_t* col_ptr, int32_t* sums, int32_t* row_idx, hipStream_t stream) {
     const int64_t n = (int64_t)BH * NK;
-    if (n == 0) {
-        hipLaunchKernelGGL(colscan_kernel, dim3(1), dim3(1024), 0, stream, counts, n, cap, col_ptr);
-        return hipGetLastError();
+    const int nb = (int)((n + 2047) / 2048);
+    if (n > 0) {
+        const dim3 grid((unsigned)((int64_t)BH * ((NK + 63) / 64)));
+        hipLaunchKernelGGL(colcount_kernel, grid, dim3(256), 0, stream, keep, NQ, NK, counts4);
+        hipLaunchKernelGGL(colscan_block_kernel, dim3((unsigned)nb), dim3(256), 0, stream, counts4, n, col_ptr,
+                           sums);
     }
-    const dim3 grid((unsigned)((int64_t)BH * ((NK + 255) / 256)));
-    hipLaunchKernelGGL(colcount_kernel, grid, dim3(256), 0, stream, keep, NQ, NK, counts);
-    hipLaunchKernelGGL(colscan_kernel, dim3(1), dim3(1024), 0, stream, counts, n, cap, col_ptr);
-    hipLaunchKernelGGL(colfill_kernel, grid, dim3(256), 0, stream, keep, NQ, NK, col_ptr, row_idx);
+    hipLaunchKernelGGL(colscan_sums_kernel, dim3(1), dim3(256), 0, stream, sums, nb);
+    hipLaunchKernelGGL(colscan_add_kernel, dim3((unsigned)((n + 1 + 255) / 256)), dim3(256), 0, stream, col_ptr,
+                       sums, n, nb, cap);
+    if (n > 0) {
+        const dim3 grid((unsigned)((int64_t)BH * ((NK + 63) / 64)));
+        hipLaunchKernelGGL(colfill_kernel, grid, dim3(256), 0, stream, keep, NQ, NK, counts4, col_ptr, row_idx);
+    }
     return hipGetLastError();
 }
 

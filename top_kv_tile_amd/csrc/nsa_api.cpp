@@ -733,7 +733,7 @@ int attn_selection(const nsa_tensor* q, const nsa_tensor* k, const nsa_selection
 // Gradient workspace: Delta (B*Hq*S fp32), then for a sparse selection the
 // per-column counts (B*H'*NK), col_ptr (B*H'*NK + 1) and row_idx (nnz) int32.
 struct BwdLayout {
-    size_t delta = 0, counts = 0, col_ptr = 0, row_idx = 0, total = 0;
+    size_t delta = 0, counts = 0, col_ptr = 0, sums = 0, row_idx = 0, total = 0;
 };
 BwdLayout bwd_layout(const nsa_tensor* q, const nsa_selection* sel) {
     BwdLayout w;
@@ -742,10 +742,12 @@ BwdLayout bwd_layout(const nsa_tensor* q, const nsa_selection* sel) {
     off += align256((size_t)numel(q) / (size_t)std::max(1, q->D) * sizeof(float));
     if (sel) {
         const size_t cols = (size_t)sel->B * sel->H * sel->NK;
-        w.counts = off;
-        off += align256(cols * sizeof(int32_t));
+        w.counts = off;  // per column and quarter of the query tiles
+        off += align256(cols * 4 * sizeof(int32_t));
         w.col_ptr = off;
         off += align256((cols + 1) * sizeof(int32_t));
+        w.sums = off;  // per block of 2048 columns, plus the total
+        off += align256((ceil_div((int64_t)cols, 2048) + 1) * sizeof(int32_t));
         w.row_idx = off;
         off += align256((size_t)std::max<int64_t>(sel->nnz, 0) * sizeof(int32_t));
     }
@@ -1347,8 +1349,10 @@ int nsa_block_sparse_attn_bwd(const nsa_tensor* q, const nsa_tensor* k, const ns
         int32_t* counts = (int32_t*)(ws + w.counts);
         int32_t* col_ptr = (int32_t*)(ws + w.col_ptr);
         int32_t* row_idx = (int32_t*)(ws + w.row_idx);
-        e = nsa::launch_kv_major_index(sel->keep, sel->B * sel->H, sel->NQ, sel->NK, (int32_t)std::max<int64_t>(sel->nnz, 0),
-                                       counts, col_ptr, row_idx, stream);
+        int32_t* sums = (int32_t*)(ws + w.sums);
+        e = nsa::launch_kv_major_index(sel->keep, sel->B * sel->H, sel->NQ, sel->NK,
+                                       (int32_t)std::max<int64_t>(sel->nnz, 0), counts, col_ptr, sums, row_idx,
+                                       stream);
         if (e != hipSuccess) return hip_fail(e);
         a.row_ptr = sel->row_ptr;
         a.col_idx = sel->col_idx;

@@ -106,10 +106,11 @@ struct AttnBwdArgs {
 // delta[r] = dout[r] . out[r] over D for `rows` rows (D in {64, 128}).
 hipError_t launch_bwd_delta(const void* out, const void* dout, int bf16, int64_t rows, int D, float* delta,
                             hipStream_t stream);
-// kv-tile-major index of keep (BH slabs of NQ x NK int8): counts (BH*NK),
-// col_ptr (BH*NK + 1), row_idx (cap entries; offsets are clamped to cap).
-hipError_t launch_kv_major_index(const int8_t* keep, int BH, int NQ, int NK, int32_t cap, int32_t* counts,
-                                 int32_t* col_ptr, int32_t* row_idx, hipStream_t stream);
+// kv-tile-major index of keep (BH slabs of NQ x NK int8): counts4 (BH*NK*4,
+// per column and quarter of the query tiles), col_ptr (BH*NK + 1), sums
+// (ceil(BH*NK / 2048) + 1), row_idx (cap entries; offsets are clamped to cap).
+hipError_t launch_kv_major_index(const int8_t* keep, int BH, int NQ, int NK, int32_t cap, int32_t* counts4,
+                                 int32_t* col_ptr, int32_t* sums, int32_t* row_idx, hipStream_t stream);
 // bf16 MFMA path: block_q in {32, 64, 96, 128}, block_kv == 64, D in {64, 128}.
 bool attn_bwd_mfma_supported(const AttnBwdArgs& a, int bf16);
 hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t stream);

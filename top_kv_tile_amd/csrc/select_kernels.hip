@@ -28,19 +28,34 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    return x;
+// Wavefront reductions and scans on DPP lane moves (no LDS round trips):
+// within each quad by quad permutes, then the half-row and row mirrors give
+// every lane its 16-lane row's result, and the four row results are read out.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) { return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false); }
+template <typename T, typename F>
+__device__ __forceinline__ T wave_reduce(T x, F op) {
+    auto bits = [](T v) { return __builtin_bit_cast(int, v); };
+    auto val = [](int v) { return __builtin_bit_cast(T, v); };
+    x = op(x, val(dpp<0xB1>(bits(x))));   // quad_perm [1, 0, 3, 2]
+    x = op(x, val(dpp<0x4E>(bits(x))));   // quad_perm [2, 3, 0, 1]
+    x = op(x, val(dpp<0x141>(bits(x))));  // row_half_mirror
+    x = op(x, val(dpp<0x140>(bits(x))));  // row_mirror
+    auto rd = [&](int l) -> T { return val(__builtin_amdgcn_readlane(bits(x), l)); };
+    return op(op(rd(0), rd(16)), op(rd(32), rd(48)));
 }
-__device__ __forceinline__ float wave_min_f(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o));
-    return x;
-}
-__device__ __forceinline__ float wave_max_f(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+__device__ __forceinline__ int wave_sum_i(int x) { return wave_reduce(x, [](int a, int b) { return a + b; }); }
+__device__ __forceinline__ float wave_min_f(float x) { return wave_reduce(x, [](float a, float b) { return fminf(a, b); }); }
+__device__ __forceinline__ float wave_max_f(float x) { return wave_reduce(x, [](float a, float b) { return fmaxf(a, b); }); }
+// Inclusive prefix sum over the 64 lanes: shifts within each 16-lane row, then
+// the last lane of rows 0 / 2 is added to rows 1 / 3 and lane 31 to rows 2 and 3.
+__device__ __forceinline__ int wave_prefix_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false); // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false); // row_bcast:31 into rows 2, 3
     return x;
 }
 
@@ -294,13 +309,8 @@ __device__ typename MaskT<EPL>::type select_top(const float (&s)[EPL], typename 
         const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
                        h3 = hist[4 * lane + 3];
         const int own = (int)(h0 + h1 + h2 + h3);
-        int x = own;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_down(x, o);
-            if (lane + o < 64) x += y;
-        }
-        int ab = x - own;  // sum over lanes with a larger index
+        const int incl = wave_prefix_sum(own);
+        int ab = __builtin_amdgcn_readlane(incl, 63) - incl;  // sum over lanes with a larger index
         int found = -1, found_above = 0;
         const uint32_t hh[4] = {h3, h2, h1, h0};
 #pragma unroll
@@ -314,8 +324,8 @@ __device__ typename MaskT<EPL>::type select_top(const float (&s)[EPL], typename 
         wave_lds_sync();
         const uint64_t who = __ballot(found >= 0);
         const int src = __builtin_ctzll(who);
-        const int bstar = __shfl(found, src);
-        const int above = __shfl(found_above, src);
+        const int bstar = __builtin_amdgcn_readlane(found, src);
+        const int above = __builtin_amdgcn_readlane(found_above, src);
         M next = 0;
 #pragma unroll
         for (int t = 0; t < EPL; ++t) {
@@ -348,7 +358,10 @@ __device__ typename MaskT<EPL>::type select_top(const float (&s)[EPL], typename 
 }
 
 template <int EPL>
-__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+// Up to 2048 kv tiles per row the register budget is held to four waves per
+// SIMD (a few values spill): the kernel waits on LDS atomics and loads, and
+// more resident waves hide that better than the spills cost.
+__global__ __launch_bounds__(256, (EPL <= 32 ? 4 : 1)) void topk_kernel(TopkArgs a) {
     typedef typename MaskT<EPL>::type M;
     __shared__ uint32_t hist_all[4][256 + 64];  // 256 buckets + one spare bin per lane
     const int lane = threadIdx.x & 63;

@@ -452,6 +452,237 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     }
 }
 
+// ============================================================ decode kernel
+//
+// Few query rows over many kv tiles (decoding): one wave of 32 query rows per
+// workgroup, as attn_mfma_kernel<D, 1>, but with K read straight into
+// registers (in the A-operand layout of S^T = K Q^T: lane (l32, hf) takes 16
+// bytes of key row 32*mb + l32 per k-step) and only V staged in LDS (two
+// stages, for the transposed reads). A workgroup then needs 2 * 64 * D * 2
+// bytes of LDS, so five fit a CU where two of attn_mfma_kernel do, and five
+// tile pairs are in flight per CU.
+// Per tile n: S(n) from the K(n) registers; V(n+1) is issued into the free V
+// stage and K(n+1) into the K registers; then the softmax of tile n and
+// O^T += V(n)^T P(n)^T. The compiler's wait for K(n+1) before the next S also
+// covers V(n+1), which was issued just before it.
+template <int D>
+__global__ __launch_bounds__(64, 2) void attn_decode_kernel(AttnArgs a) {
+    constexpr int BKV = 64;
+    constexpr int KSTEPS = D / 16;
+    constexpr int DBLK = D / 32;
+    using G = MfmaGeo<D>;
+    extern __shared__ __attribute__((aligned(1024))) char lds[];
+
+    const int lane = threadIdx.x & 63;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int64_t total = (int64_t)a.B * a.Hq * a.NQ;
+    const int split = (int)(blockIdx.x % a.nsplit);
+    const Work wk = decode_work(blockIdx.x / a.nsplit, total, a.Hq, a.Hkv, a.NQ);
+    const int q0 = wk.i * a.block_q;              // a tile holds at most 32 rows (host-checked)
+    const int q_last = min(q0 + 32, a.S) - 1;
+    const int qrow = q0 + l32;
+    const bool qvalid = qrow < a.S;
+
+    const int head_bytes = a.S * G::ROWB;
+    const int kv_bytes = a.Skv * G::ROWB;
+    const __amdgpu_buffer_rsrc_t qrs =
+        make_rsrc((const uint16_t*)a.q + (((int64_t)wk.b * a.Hq + wk.h) * a.S) * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t krs =
+        make_rsrc((const uint16_t*)a.k + ((int64_t)wk.b * a.Hkv + wk.g) * a.kv_rows * D, kv_bytes);
+    const u32x4 vrs = rsrc_words((const uint16_t*)a.v + ((int64_t)wk.b * a.Hkv + wk.g) * a.kv_rows * D, kv_bytes);
+
+    bf16x8 qf[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, (qrow * D + 8 * hf) * 2 + 32 * ks,
+                                                                                   0, 0));
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);  // Q settled before any tile DMA
+
+    const int qpos = a.qpack ? qrow % a.qpack : qrow;
+    int e_begin, e_end;
+    tile_range_wave(a, wk.b, wk.h, wk.i, a.q_off + (a.qpack ? a.qpack - 1 : q_last), lane, e_begin, e_end);
+    if (a.nsplit > 1) {
+        const int per = (e_end - e_begin + a.nsplit - 1) / a.nsplit;
+        e_begin = min(e_end, e_begin + split * per);
+        e_end = min(e_end, e_begin + per);
+    }
+    const int ntiles = e_end - e_begin;
+
+    int col_base = e_begin, col_lane = 0;
+    auto fetch_cols = [&](int base) {
+        col_base = base;
+        const int e = base + lane;
+        col_lane = a.row_ptr ? (e < e_end ? a.col_idx[e] : 0) : e;
+    };
+    fetch_cols(e_begin);
+    auto tile_of = [&](int n) -> int {
+        const int e = e_begin + n;
+        if (e - col_base >= 64) fetch_cols(e);
+        return __builtin_amdgcn_readlane(col_lane, e - col_base);
+    };
+
+    // V DMA into stage st (rows past Skv read row Skv - 1, weighted by p = 0).
+    const uint32_t lds0 = lds_address(lds);
+    auto dma_v = [&](int j, int st) {
+        const int key0 = j * BKV;
+        const uint32_t base = lds0 + st * G::TILEB;
+#pragma unroll
+        for (int ii = 0; ii < G::NINSTR; ++ii) {
+            const int row = ii * G::RPI + lane / G::CH, pc = lane % G::CH;
+            const int chunk = pc ^ G::vswz(row);
+            dma16(vrs, base + ii * 1024, min(key0 + row, a.Skv - 1) * G::ROWB + chunk * 16);
+        }
+    };
+    // K(j) into registers: kf[mb][ks] = key row 32*mb + l32, elements 16*ks + 8*hf .. + 8.
+    bf16x8 kf[2][KSTEPS];
+    auto load_k = [&](int j) {
+        const int key0 = j * BKV;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int off = min(key0 + 32 * mb + l32, a.Skv - 1) * G::ROWB + 16 * hf;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+                kf[mb][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 32 * ks, 0, 0));
+        }
+    };
+
+    const int vg = lane >> 4, vs = lane & 15;
+    const int v_e = vs >> 2, v_q = vs & 3;
+    int voff[DBLK];
+#pragma unroll
+    for (int m = 0; m < DBLK; ++m) {
+        const int r = 4 * hf + v_e;
+        const int d = 32 * m + 16 * (vg & 1) + 4 * v_q;
+        voff[m] = r * G::ROWB + (((d >> 3) ^ G::vswz(r)) * 16) + (d & 7) * 2;
+    }
+
+    f32x16 oacc[DBLK];
+#pragma unroll
+    for (int m = 0; m < DBLK; ++m) oacc[m] = (f32x16){};
+    float m_ref = kNegInf, l_run = 0.f;
+    const float tau_raw = 8.0f / a.scale_log2;
+
+    int j_cur = 0, j_next = 0;
+    if (ntiles > 0) {
+        j_cur = tile_of(0);
+        dma_v(j_cur, 0);
+        load_k(j_cur);
+    }
+    for (int n = 0; n < ntiles; ++n) {
+        // S^T(n) = K(n) Q^T (the compiler waits here for K(n), and with it for V(n)).
+        f32x16 sc[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            sc[mb] = (f32x16){};
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) sc[mb] = mfma32(kf[mb][ks], qf[ks], sc[mb]);
+        }
+        if (n + 1 < ntiles) {
+            j_next = tile_of(n + 1);
+            dma_v(j_next, (n + 1) & 1);  // that stage was last read by PV(n - 1)
+            load_k(j_next);
+        }
+        // Masks of a partial tile (causal diagonal or ragged tail).
+        const int key0 = j_cur * BKV;
+        if ((a.causal && key0 + BKV - 1 > a.q_off + (a.qpack ? 0 : q0)) || (key0 + BKV > a.Skv)) {
+            int lim = min(BKV - 1, a.Skv - 1 - key0);
+            if (a.causal) lim = min(lim, a.q_off + qpos - key0);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    const int off = 32 * mb + 8 * (x >> 2) + 4 * hf + (x & 3);
+                    sc[mb][x] = off <= lim ? sc[mb][x] : kNegInf;
+                }
+        }
+        // Online softmax with a lazy reference (as attn_mfma_kernel).
+        float mx = kNegInf;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sc[mb][x]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool grow = mx > m_ref + tau_raw;
+        const float m_new = grow ? mx : m_ref;
+        const float alpha = grow ? fast_exp2((m_ref - m_new) * a.scale_log2) : 1.0f;
+        const float mref_s = (m_new == kNegInf) ? 0.f : m_new * a.scale_log2;
+        bf16x8 pf[4];
+        float psum = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int mb = kk >> 1, q4 = 8 * (kk & 1);
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                const float pv = fast_exp2(__builtin_fmaf(sc[mb][q4 + x], a.scale_log2, -mref_s));
+                psum += pv;
+                pf[kk][x] = (__bf16)pv;
+            }
+        }
+        l_run = l_run * alpha + psum;
+        m_ref = m_new;
+        if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+            for (int m = 0; m < DBLK; ++m) oacc[m] *= alpha;
+        }
+        // O^T += V(n)^T P(n)^T
+        const char* vt = lds + (n & 1) * G::TILEB;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+            for (int m = 0; m < DBLK; ++m) {
+                const char* p0 = vt + 16 * kk * G::ROWB + voff[m];
+                const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p0);
+                const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0 + 8 * G::ROWB));
+                const short8_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                oacc[m] = mfma32(__builtin_bit_cast(bf16x8, w), pf[kk], oacc[m]);
+            }
+        }
+        // The V stage read here is refilled two tiles on: its reads must be
+        // done before that DMA is issued.
+        __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+        j_cur = j_next;
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const bool empty = !(l_tot > 0.f);
+    if (a.nsplit > 1) {
+        if (qvalid) {
+            const int64_t prow = (((int64_t)wk.b * a.Hq + wk.h) * a.S + qrow) * a.nsplit + split;
+            float* po = a.part_o + prow * D;
+#pragma unroll
+            for (int m = 0; m < DBLK; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 w = {oacc[m][4 * q], oacc[m][4 * q + 1], oacc[m][4 * q + 2], oacc[m][4 * q + 3]};
+                    *(f32x4*)(po + 32 * m + 8 * q + 4 * hf) = w;
+                }
+            if (hf == 0) {
+                a.part_ml[2 * prow] = empty ? kNegInf : m_ref * a.scale_log2;
+                a.part_ml[2 * prow + 1] = l_tot;
+            }
+        }
+        return;
+    }
+    const float inv = empty ? 0.f : 1.0f / l_tot;
+    if (qvalid) {
+        uint16_t* op = (uint16_t*)a.out + (((int64_t)wk.b * a.Hq + wk.h) * a.S + qrow) * D;
+#pragma unroll
+        for (int m = 0; m < DBLK; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                bf16x4 w;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) w[x] = (__bf16)(oacc[m][4 * q + x] * inv);
+                *(bf16x4*)(op + 32 * m + 8 * q + 4 * hf) = w;
+            }
+        if (hf == 0) {
+            a.lse[((int64_t)wk.b * a.Hq + wk.h) * a.S + qrow] =
+                empty ? kNegInf : (m_ref * a.scale_log2 + __log2f(l_tot)) * kLn2;
+        }
+    }
+}
+
 // ============================================================ SIMT kernel
 //
 // General fallback (fp32 inputs, or block sizes the MFMA kernel does not take).
@@ -594,6 +825,25 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 }
 
 }  // namespace
+
+bool attn_decode_supported(const AttnArgs& a, int bf16) {
+    return attn_mfma_supported(a, bf16) && (a.block_q == 32 || (a.NQ == 1 && a.S <= 32));
+}
+
+hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t stream) {
+    const int64_t total = (int64_t)a.B * a.Hq * a.NQ * std::max(1, a.nsplit);
+    if (total == 0) return hipSuccess;
+    if (!(a.block_q == 32 || (a.NQ == 1 && a.S <= 32))) return hipErrorInvalidValue;
+    if (a.D == 128)
+        hipLaunchKernelGGL((attn_decode_kernel<128>), dim3((unsigned)total), dim3(64), 2 * MfmaGeo<128>::TILEB,
+                           stream, a);
+    else if (a.D == 64)
+        hipLaunchKernelGGL((attn_decode_kernel<64>), dim3((unsigned)total), dim3(64), 2 * MfmaGeo<64>::TILEB,
+                           stream, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_attn_combine(const AttnArgs& a, int bf16, hipStream_t stream) {
     const int64_t rows = (int64_t)a.B * a.Hq * a.S;

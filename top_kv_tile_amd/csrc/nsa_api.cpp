@@ -549,7 +549,7 @@ int decode_attn_config(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa
         a.col_idx = nullptr;
         a.Hsel = q->H;
         a.Bsel = q->B;
-        a.block_q = q->S <= 32 ? 32 : (q->S <= 64 ? 64 : 128);
+        a.block_q = 32;  // the decode kernel's row tile
         a.block_kv = 64;
         tiles_per_row = ceil_div(length, 64);
     }
@@ -566,13 +566,13 @@ int decode_attn_config(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa
         p.Hq = k_cache->H;
         p.Hsel = 1;
         p.S = (int)rows;
-        p.block_q = rows <= 32 ? 32 : rows <= 64 ? 64 : rows <= 96 ? 96 : 128;
+        p.block_q = 32;  // packed rows follow no selection tile: the decode kernel's 32-row tile
         p.NQ = (int)ceil_div(rows, p.block_q);
         if (rows < INT32_MAX && nsa::attn_mfma_supported(p, q->dtype == NSA_BF16)) a = p;
     }
     if (nsa::attn_mfma_supported(a, q->dtype == NSA_BF16)) {
         const int64_t work = std::max<int64_t>((int64_t)a.B * a.Hq * a.NQ, 1);
-        const int64_t want = ceil_div(2048, work);
+        const int64_t want = ceil_div(nsa::attn_decode_supported(a, q->dtype == NSA_BF16) ? 2560 : 2048, work);
         const int64_t most = std::max<int64_t>(1, tiles_per_row / 8);
         a.nsplit = (int)std::max<int64_t>(1, std::min<int64_t>({want, most, 64}));
     }
@@ -1169,11 +1169,15 @@ int nsa_decode_attn(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa_te
     if (workspace_bytes < need || (need > 0 && !workspace)) return NSA_ERR_WORKSPACE;
     const int bf16 = q->dtype == NSA_BF16;
     hipError_t e;
+    const bool dec = nsa::attn_decode_supported(a, bf16);
     if (a.nsplit > 1) {
         a.part_o = (float*)workspace;
         a.part_ml = (float*)((char*)workspace + align256((size_t)a.B * a.Hq * a.S * a.nsplit * a.D * 4));
-        if ((e = nsa::launch_attn_mfma(a, stream)) != hipSuccess) return hip_fail(e);
+        if ((e = dec ? nsa::launch_attn_decode(a, stream) : nsa::launch_attn_mfma(a, stream)) != hipSuccess)
+            return hip_fail(e);
         e = nsa::launch_attn_combine(a, bf16, stream);
+    } else if (dec) {
+        e = nsa::launch_attn_decode(a, stream);
     } else {
         e = nsa::attn_mfma_supported(a, bf16) ? nsa::launch_attn_mfma(a, stream)
                                               : nsa::launch_attn_simt(a, bf16, stream);

@@ -76,6 +76,10 @@ struct AttnArgs {
 // bf16 MFMA path: block_q in {32, 64, 96, 128}, block_kv == 64, D in {64, 128}.
 bool attn_mfma_supported(const AttnArgs& a, int bf16);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t stream);
+// Decoding: one wave of 32 query rows per workgroup with K read into registers
+// (bf16, block_q == 32, block_kv == 64, D in {64, 128}); split rows as above.
+bool attn_decode_supported(const AttnArgs& a, int bf16);
+hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t stream);
 // Merges the nsplit partials of every query row into out (dtype of q) and lse.
 hipError_t launch_attn_combine(const AttnArgs& a, int bf16, hipStream_t stream);
 // General path (fp32 or bf16 inputs, any block sizes, D in {64, 128}).

@@ -241,7 +241,7 @@ def decode_timing(q, k, v, w: synth.Workload, calls: int = 20):
             "dense_attn_us": round(dense_ms * 1e3, 1), "dense_bytes": dense_bytes,
             "dense_GBps": round(dense_bytes / (dense_ms * 1e-3) / 1e9, 1),
             "dense_frac_hbm": round(dense_bytes / (dense_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "kernels": "pool_kernel (tile range), score_kernel, topk_kernel, attn_mfma_kernel<128,1> + "
+            "kernels": "pool_kernel (tile range), score_kernel, topk_kernel, attn_decode_kernel<128> + "
                        "attn_combine_kernel"}
 
 

@@ -791,37 +791,52 @@ __global__ __launch_bounds__(256) void attn_simt_kernel(AttnArgs a) {
 
 // Merges the split partials of one query row: with M the largest reference,
 // w_s = 2^(m_s - M), O = sum_s w_s O_s / sum_s w_s l_s and
-// LSE = (M + log2 sum_s w_s l_s) ln 2. One wave per row, D / 64 elements per lane.
+// LSE = (M + log2 sum_s w_s l_s) ln 2. One workgroup per row: its four waves
+// take every fourth split (D / 64 elements per lane) and add up through LDS.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     constexpr int PER = D / 64;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (row >= (int64_t)a.B * a.Hq * a.S) return;
-    const float* ml = a.part_ml + row * a.nsplit * 2;
-    float M = kNegInf;
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, ml[2 * s]);
+    __shared__ float sm[4], sl[4];
+    __shared__ float so[4][D];
+    const int64_t row = blockIdx.x;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int ns = a.nsplit;
+    const float* ml = a.part_ml + row * ns * 2;
+    float m = kNegInf;
+    for (int s = threadIdx.x; s < ns; s += 256) m = fmaxf(m, ml[2 * s]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) sm[w] = m;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
     float lsum = 0.f, acc[PER];
 #pragma unroll
     for (int x = 0; x < PER; ++x) acc[x] = 0.f;
-    for (int s = 0; s < a.nsplit; ++s) {
-        const float m = ml[2 * s];
-        if (m == kNegInf) continue;
-        const float w = exp2f(m - M);
-        lsum += w * ml[2 * s + 1];
-        const float* po = a.part_o + (row * a.nsplit + s) * D;
+#pragma unroll 4
+    for (int s = w; s < ns; s += 4) {
+        const float ms = ml[2 * s];
+        const float ws = ms == kNegInf ? 0.f : exp2f(ms - M);  // splits that saw no key add nothing
+        lsum += ws * ml[2 * s + 1];
+        const float* po = a.part_o + (row * ns + s) * D;
 #pragma unroll
-        for (int x = 0; x < PER; ++x) acc[x] += w * po[lane + 64 * x];
+        for (int x = 0; x < PER; ++x) acc[x] += ws * po[lane + 64 * x];
     }
-    const bool empty = !(lsum > 0.f);
-    const float inv = empty ? 0.f : 1.0f / lsum;
+#pragma unroll
+    for (int x = 0; x < PER; ++x) so[w][lane + 64 * x] = acc[x];
+    if (lane == 0) sl[w] = lsum;
+    __syncthreads();
+    if (w != 0) return;
+    const float L = (sl[0] + sl[1]) + (sl[2] + sl[3]);
+    const bool empty = !(L > 0.f);
+    const float inv = empty ? 0.f : 1.0f / L;
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
-        const float o = acc[x] * inv;
-        if constexpr (BF16) ((__bf16*)a.out)[row * D + lane + 64 * x] = (__bf16)o;
-        else ((float*)a.out)[row * D + lane + 64 * x] = o;
+        const int d = lane + 64 * x;
+        const float o = ((so[0][d] + so[1][d]) + (so[2][d] + so[3][d])) * inv;
+        if constexpr (BF16) ((__bf16*)a.out)[row * D + d] = (__bf16)o;
+        else ((float*)a.out)[row * D + d] = o;
     }
-    if (lane == 0) a.lse[row] = empty ? kNegInf : (M + __log2f(lsum)) * kLn2;
+    if (lane == 0) a.lse[row] = empty ? kNegInf : (M + __log2f(L)) * kLn2;
 }
 
 }  // namespace
@@ -848,7 +863,7 @@ hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_attn_combine(const AttnArgs& a, int bf16, hipStream_t stream) {
     const int64_t rows = (int64_t)a.B * a.Hq * a.S;
     if (rows == 0) return hipSuccess;
-    const dim3 grid((unsigned)((rows + 3) / 4));
+    const dim3 grid((unsigned)rows);
     if (a.D == 128) {
         if (bf16) hipLaunchKernelGGL((attn_combine_kernel<128, true>), grid, dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((attn_combine_kernel<128, false>), grid, dim3(256), 0, stream, a);

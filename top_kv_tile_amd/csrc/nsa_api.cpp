@@ -491,7 +491,8 @@ WsLayout decode_layout(const Plan& p, const nsa_spec* spec) {
 
 // Launch geometry of a decode attention call (everything but out / lse / partials).
 // Rows whose tiles are few and many can be split over several workgroups (MFMA
-// path): enough splits for about 2048 workgroups, each with at least 8 tiles.
+// paths); the partials are merged afterwards. The decode kernel (32-row tiles)
+// is used where it applies.
 int decode_attn_config(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa_tensor* v_cache,
                        const nsa_tensor* out, int32_t length, int32_t q_pos0, const nsa_selection* sel,
                        nsa::AttnArgs& a) {
@@ -572,6 +573,8 @@ int decode_attn_config(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa
     }
     if (nsa::attn_mfma_supported(a, q->dtype == NSA_BF16)) {
         const int64_t work = std::max<int64_t>((int64_t)a.B * a.Hq * a.NQ, 1);
+        // about two rounds of workgroups (five per CU for the decode kernel), at
+        // least 8 tiles per split and at most 64 splits (measured at 128k)
         const int64_t want = ceil_div(nsa::attn_decode_supported(a, q->dtype == NSA_BF16) ? 2560 : 2048, work);
         const int64_t most = std::max<int64_t>(1, tiles_per_row / 8);
         a.nsplit = (int)std::max<int64_t>(1, std::min<int64_t>({want, most, 64}));

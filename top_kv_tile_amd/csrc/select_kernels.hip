@@ -231,6 +231,51 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qh
     store(c11, 32, 32);
 }
 
+// Scores of a few query rows (NQ <= 8, e.g. while decoding): a 64 x 64 MFMA
+// block would be almost all padding, so one thread takes one kv tile and
+// forms its dot products with the (at most 8) pooled query rows held in LDS.
+template <int D>
+__global__ __launch_bounds__(256) void score_rows_kernel(const float* __restrict__ qh, const float* __restrict__ kh,
+                                                         int Hsel, int Hk, int group, int h0, int nh, int NQ,
+                                                         int NK, int NKs, float* __restrict__ s) {
+    __shared__ float qs[8 * D];
+    const int nbj = (NK + 255) / 256;
+    int64_t wid = blockIdx.x;
+    const int jb = (int)(wid % nbj);
+    wid /= nbj;
+    const int hl = (int)(wid % nh);
+    const int b = (int)(wid / nh);
+    const int h = h0 + hl;
+    const int hk = (Hk == 1) ? 0 : h / group;
+    const float* A = qh + ((int64_t)b * Hsel + h) * NQ * D;
+    for (int x = threadIdx.x; x < NQ * D; x += 256) qs[x] = A[x];
+    __syncthreads();
+    const int j = jb * 256 + threadIdx.x;
+    if (j >= NK) return;
+    const float* krow = kh + ((int64_t)b * Hk + hk) * NKs * D + (int64_t)j * D;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll 4
+    for (int d = 0; d < D; d += 4) {
+        const f32x4 kv = *(const f32x4*)(krow + d);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i < NQ) {
+                const float* qv = qs + i * D + d;
+                acc[i] = __builtin_fmaf(qv[0], kv[0], acc[i]);
+                acc[i] = __builtin_fmaf(qv[1], kv[1], acc[i]);
+                acc[i] = __builtin_fmaf(qv[2], kv[2], acc[i]);
+                acc[i] = __builtin_fmaf(qv[3], kv[3], acc[i]);
+            }
+        }
+    }
+    float* out = s + ((int64_t)b * nh + hl) * NQ * NK;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i < NQ) out[(int64_t)i * NK + j] = acc[i];
+}
+
 // ---------------------------------------------------------------- top-k
 //
 // One wavefront per selection row. Element j = 64*t + lane sits in register
@@ -483,6 +528,18 @@ hipError_t launch_scores(const float* qh, const float* kh, int B, int Hsel, int 
                          int NQ, int NK, int D, float* s, hipStream_t stream, int NKs) {
     if (NKs <= 0) NKs = NK;
     if (NQ == 0 || NK == 0 || nh == 0 || B == 0) return hipSuccess;
+    if (NQ <= 8) {
+        const dim3 g((unsigned)((int64_t)B * nh * ((NK + 255) / 256)));
+#define NSA_ROWS(DD)                                                                                         \
+    hipLaunchKernelGGL((score_rows_kernel<DD>), g, dim3(256), 0, stream, qh, kh, Hsel, Hk, group, h0, nh, NQ, NK, \
+                       NKs, s)
+        if (D == 64) NSA_ROWS(64);
+        else if (D == 128) NSA_ROWS(128);
+        else if (D == 256) NSA_ROWS(256);
+        else return hipErrorInvalidValue;
+#undef NSA_ROWS
+        return hipGetLastError();
+    }
     const int nbi = (NQ + 63) / 64, nbj = (NK + 63) / 64;
     const int64_t blocks = (int64_t)B * nh * nbi * ((nbj + 3) / 4);
     const dim3 grid((unsigned)blocks);

@@ -123,3 +123,33 @@ def test_packed_gqa_decode(Hq, Hkv, D, n, bq):
     out, lse = tkt.nsa_decode_attn(qd, kd, vd, length, pos0, None)
     ref_o, ref_l = oracle.decode_attention(q, kc, vc, length, pos0, np.ones((1, 1, 1, nk), np.int8), bq, bkv)
     check_attention(out, lse, ref_o, ref_l, "bf16", where="packed dense decode")
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_decode_128k_cache(shared):
+    """The decoding step bench.py times, at its size: one new token over a
+    131 072-token cache, 64 query heads over 8 kv heads, per-head or shared
+    selection with the sink tile pinned; every head against the oracle, and
+    the dense call too."""
+    say(f"decode 128k shared={shared}")
+    B, Hq, Hkv, L, D, bkv = 1, 64, 8, 131072, 128, 64
+    g = torch.Generator().manual_seed(77 + shared)
+    kc, vc = (torch.randn(B, Hkv, L, D, generator=g).to(torch.bfloat16) for _ in range(2))
+    q = torch.randn(B, Hq, 1, D, generator=g).to(torch.bfloat16)
+    nk = L // bkv
+    kd, vd, qd = to_dev(kc), to_dev(vc), to_dev(q)
+    pooled = torch.zeros(B, Hkv, nk, D, dtype=torch.float32, device="cuda:0")
+    tkt.nsa_decode_pool_update(kd, 0, L - 1, bkv, pooled)
+    tkt.nsa_decode_pool_update(kd, L - 1, L, bkv, pooled)  # the step's own token
+    pins = np.zeros((1, 1, 1, nk), np.int8)
+    pins[..., 0] = 1
+    spec = tkt.SparseSpec(budget=0.05, block_q=32, block_kv=bkv, head_shared=shared)
+    sel = tkt.nsa_decode_select(qd, pooled, L, L - 1, spec, pins=pins)
+    ref = oracle.decode_select(q, kc, L, L - 1, spec.budget, 32, bkv, shared, False, pins=pins)
+    keep, _ = check_selection(sel, ref, "128k select")
+    out, lse = tkt.nsa_decode_attn(qd, kd, vd, L, L - 1, sel)
+    ref_o, ref_l = oracle.decode_attention(q, kc, vc, L, L - 1, keep, 32, bkv)
+    check_attention(out, lse, ref_o, ref_l, "bf16", where="128k decode")
+    out, lse = tkt.nsa_decode_attn(qd, kd, vd, L, L - 1, None)
+    ref_o, ref_l = oracle.decode_attention(q, kc, vc, L, L - 1, np.ones((1, 1, 1, nk), np.int8), 32, bkv)
+    check_attention(out, lse, ref_o, ref_l, "bf16", where="128k dense decode")

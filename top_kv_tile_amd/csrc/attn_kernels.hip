@@ -287,12 +287,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
         if (need_mask) {
             int lim = min(BKV - 1, a.Skv - 1 - key0);         // last visible key offset
             if (a.causal) lim = min(lim, a.q_off + qpos - key0);
+            // Key offset of element x is c(x) + 4 * hf: compare c(x), a
+            // compile-time constant, with lim - 4 * hf.
+            const int limh = lim - 4 * hf;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int x = 0; x < 16; ++x) {
-                    const int off = 32 * mb + 8 * (x >> 2) + 4 * hf + (x & 3);
-                    sacc[mb][x] = off <= lim ? sacc[mb][x] : kNegInf;
+                    const int c = 32 * mb + 8 * (x >> 2) + (x & 3);
+                    sacc[mb][x] = c <= limh ? sacc[mb][x] : kNegInf;
                 }
         }
     };
@@ -316,17 +319,30 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int x = 0; x < 16; ++x) mx = fmaxf(mx, scur[mb][x]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        {  // the other half-wave holds the row's other keys
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+        }
         const bool grow = mx > m_ref + tau_raw;
         const float m_new = grow ? mx : m_ref;
         const float alpha = grow ? fast_exp2((m_ref - m_new) * a.scale_log2) : 1.0f;  // 0 when m_ref = -inf
         const float mref_s = (m_new == kNegInf) ? 0.f : m_new * a.scale_log2;
         float psum = 0.f;
+        // K fragments one k-step ahead of their products (two buffers),
+        // fenced so the reads of step ks + 1 are in flight under step ks.
+        bf16x8 kf[2][2];
+        kf[0][0] = qk_frag(ks, 0, 0);
+        kf[0][1] = qk_frag(ks, 0, 1);
 #pragma unroll
         for (int ks_ = 0; ks_ < KSTEPS; ++ks_) {
+            if (ks_ + 1 < KSTEPS) {
+                kf[(ks_ + 1) & 1][0] = qk_frag(ks, ks_ + 1, 0);
+                kf[(ks_ + 1) & 1][1] = qk_frag(ks, ks_ + 1, 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
-                snext[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qk_frag(ks, ks_, mb), qf[ks_], snext[mb], 0, 0, 0);
+                snext[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks_ & 1][mb], qf[ks_], snext[mb], 0, 0, 0);
             if (ks_ < 4) {  // four of the eight k-steps carry the softmax of one P fragment each
                 const int kk = ks_, mb = kk >> 1, q4 = 8 * (kk & 1);
 #pragma unroll
@@ -335,7 +351,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
                     psum += pv;
                     pf[kk][x] = (__bf16)pv;
                 }
+                // Keep this fragment's exponentials here, under the products,
+                // rather than sunk to their use in O^T += V^T P^T.
+                u32x4 pw = __builtin_bit_cast(u32x4, pf[kk]);
+                asm volatile("" : "+v"(pw), "+v"(psum));
+                pf[kk] = __builtin_bit_cast(bf16x8, pw);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         l_run = l_run * alpha + psum;
         m_ref = m_new;
@@ -345,17 +367,30 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     // transposed reads: keys 16kk + 4hf + (0..3) and 16kk + 8 + 4hf + (0..3).
     auto pv = [&](const bf16x8 (&pf)[4], int vstage) {
         const char* vt = vst[vstage];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        // V^T fragments of k-step kk + 1 are read while the products of k-step
+        // kk run (two buffers, fenced as the K fragments above).
+        short4_t vlo[2][DBLK], vhi[2][DBLK];
+        auto load_v = [&](int kk, int buf) {
 #pragma unroll
             for (int m = 0; m < DBLK; ++m) {
                 const char* p0 = vt + 16 * kk * G::ROWB + voff[m];
-                const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p0);
-                const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0 + 8 * G::ROWB));
+                vlo[buf][m] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p0);
+                vhi[buf][m] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0 + 8 * G::ROWB));
+            }
+        };
+        load_v(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk + 1 < 4) load_v(kk + 1, (kk + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < DBLK; ++m) {
+                const short4_t lo = vlo[kk & 1][m], hi = vhi[kk & 1][m];
                 const short8_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[kk],
                                                                    oacc[m], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -601,7 +636,10 @@ __global__ __launch_bounds__(64, 2) void attn_decode_kernel(AttnArgs a) {
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sc[mb][x]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        {  // the other half-wave holds the row's other keys
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+        }
         const bool grow = mx > m_ref + tau_raw;
         const float m_new = grow ? mx : m_ref;
         const float alpha = grow ? fast_exp2((m_ref - m_new) * a.scale_log2) : 1.0f;

@@ -434,21 +434,44 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_mfma_kernel(AttnBwdArgs a) 
 #pragma unroll
     for (int m = 0; m < DBLK; ++m) dq[m] = (f32x16){};
 
+    // Tile DMA through the instruction itself (the compiler does not track it,
+    // so the transposed K reads of step n do not wait for the tiles of step
+    // n + 1); every wait on it is explicit.
+    const u32x4 krw = rsrc_words((const uint16_t*)a.k + khead * D, head_bytes);
+    const u32x4 vrw = rsrc_words((const uint16_t*)a.v + khead * D, head_bytes);
+    const uint32_t lds0 = lds_address(lds);
+    auto dma = [&](u32x4 rs, bool both, int st_off, int row0) {
+#pragma unroll
+        for (int x = 0; x < (G::NINSTR + NW - 1) / NW; ++x) {
+            const int ii = wave + NW * x;
+            if (G::NINSTR % NW == 0 || ii < G::NINSTR) {
+                const int row = ii * G::RPI + lane / G::CH, pc = lane % G::CH;
+                const int chunk = pc ^ (both ? G::bswz(row) : G::rswz(row));
+                dma16(rs, lds0 + st_off + ii * 1024, min(row0 + row, a.S - 1) * G::ROWB + chunk * 16);
+            }
+        }
+    };
+    auto dma_k = [&](int st, int j) { dma(krw, true, st * G::TILEB, j * 64); };
+    auto dma_v = [&](int st, int j) { dma(vrw, false, (2 + st) * G::TILEB, j * 64); };
+
     int j_cur = 0;
+    // The Q / dO loads are the only loads the compiler tracks: settle them
+    // before the first DMA on every path, so none of its waits counts tiles.
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     if (ntiles > 0) {
         j_cur = tile_of(0);
-        dma_tile<D, NW, true>(krs, kst(0), j_cur * 64, a.S, wave, lane);
-        dma_tile<D, NW, false>(vrs, vst(0), j_cur * 64, a.S, wave, lane);
+        dma_k(0, j_cur);
+        dma_v(0, j_cur);
     }
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    __syncthreads();
+    bare_barrier();
 
     for (int n = 0; n < ntiles; ++n) {
         const int st = n & 1;
         const int j_next = (n + 1 < ntiles) ? tile_of(n + 1) : 0;
         if (n + 1 < ntiles) {  // stage st ^ 1 was last read in step n - 1
-            dma_tile<D, NW, true>(krs, kst(st ^ 1), j_next * 64, a.S, wave, lane);
-            dma_tile<D, NW, false>(vrs, vst(st ^ 1), j_next * 64, a.S, wave, lane);
+            dma_k(st ^ 1, j_next);
+            dma_v(st ^ 1, j_next);
         }
         const char* kt = kst(st);
         const char* vt = vst(st);
@@ -466,12 +489,22 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_mfma_kernel(AttnBwdArgs a) 
                 dp[mb] = mfma(row_frag<D, false>(vt, 32 * mb + l32, 2 * ks + hf), dof[ks], dp[mb]);
             }
         // Lane holds query qrow and keys 32 mb + 8 (x / 4) + 4 hf + (x % 4) of the tile at [mb][x].
+        // Partial tiles (causal diagonal, ragged tail) only: keys past the
+        // lane's query row or past S get S = -inf, hence P = 0. Key offset of
+        // element x is c(x) + 4 hf: compare the constant c(x) with lim - 4 hf.
         const int key0 = j_cur * 64;
         const bool need_mask = (a.causal && key0 + 63 > qw0) || (key0 + 64 > a.S);
-        int lim = 63;
         if (need_mask) {
-            lim = min(63, a.S - 1 - key0);
+            int lim = min(63, a.S - 1 - key0);
             if (a.causal) lim = min(lim, qrow - key0);
+            const int limh = lim - 4 * hf;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    const int c = 32 * mb + 8 * (x >> 2) + (x & 3);
+                    s[mb][x] = c <= limh ? s[mb][x] : kNegInf;
+                }
         }
         bf16x8 dsf[4];
 #pragma unroll
@@ -479,20 +512,28 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_mfma_kernel(AttnBwdArgs a) 
             const int mb = kk >> 1, q4 = 8 * (kk & 1);
 #pragma unroll
             for (int x = 0; x < 8; ++x) {
-                const int off = 32 * mb + 8 * ((q4 + x) >> 2) + 4 * hf + ((q4 + x) & 3);
-                float p = fast_exp2(__builtin_fmaf(s[mb][q4 + x], a.scale_log2, -lse_l2));
-                p = off <= lim ? p : 0.f;
+                const float p = fast_exp2(__builtin_fmaf(s[mb][q4 + x], a.scale_log2, -lse_l2));
                 dsf[kk][x] = (__bf16)(p * (dp[mb][q4 + x] - delta));
             }
         }
         // dQ^T += K^T dS^T; contraction over keys 16 kk + 4 hf + (0..3), 16 kk + 8 + 4 hf + (0..3).
+        bf16x8 tf[2][DBLK];
+        auto load_t = [&](int kk, int buf) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+            for (int m = 0; m < DBLK; ++m) tf[buf][m] = tr_frag<D>(kt, 16 * kk, m, lane);
+        };
+        load_t(0, 0);
 #pragma unroll
-            for (int m = 0; m < DBLK; ++m) dq[m] = mfma(tr_frag<D>(kt, 16 * kk, m, lane), dsf[kk], dq[m]);
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk + 1 < 4) load_t(kk + 1, (kk + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < DBLK; ++m) dq[m] = mfma(tf[kk & 1][m], dsf[kk], dq[m]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         j_cur = j_next;
-        __builtin_amdgcn_s_waitcnt(kVmcnt0);
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);  // tile n + 1 has landed
+        bare_barrier();
     }
 
     if (qvalid) {

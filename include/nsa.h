@@ -189,6 +189,27 @@ int nsa_select_planned(const nsa_plan* plan, const nsa_tensor* q, const nsa_tens
  * queued on that device first (a planned selection may still be reading it). */
 void nsa_plan_destroy(nsa_plan* plan);
 
+/* ---- Plan cache of nsa_select and nsa_select_sizes ---------------------------
+ * Both calls look their plan up in a process-wide cache before building it
+ * (the plan cache of selection_plan on the selection page). The key is the
+ * whole request: q and k shapes and dtypes, every nsa_spec field, and the
+ * shape and bytes of pins and drops, so a request whose masks differ in one
+ * byte builds its own plan (the page's key leaves the masks out). Entries are
+ * host memory only (the plan is uploaded per call on the caller's stream, as
+ * without the cache); the least recently used entry is replaced when the
+ * cache is full. Thread-safe. */
+
+/* Host only. Keeps at most `capacity` plans (default 8; 0 disables caching).
+ * Lowering it drops the least recently used entries. BAD_SPEC if capacity < 0. */
+int nsa_plan_cache_config(int32_t capacity);
+
+/* Host only. Drops every cached plan and zeroes the counters. */
+void nsa_plan_cache_clear(void);
+
+/* Host only. Lookups that found a plan, lookups that built one, and the entries
+ * held now. NULL_ARG if any pointer is NULL. */
+int nsa_plan_cache_stats(int64_t* hits, int64_t* misses, int32_t* entries);
+
 /* ---- Controls (selection page: schedule, radial_blocks, BlockSelection.density) */
 
 /* Host only. Per-step budgets: out[i] = budget, raised to min(1, budget + bump)

@@ -1,7 +1,8 @@
 """GPU parity of the controls and plan reuse: the radial band (device keep and
 CSR against the oracle, then attention and its gradients over that band with one
 selection broadcast to every batch entry), planned selection against
-nsa_select, and the host-side density."""
+nsa_select, the plan cache of nsa_select keyed on the mask contents, and the
+host-side density."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +10,7 @@ import torch
 import oracle
 import top_kv_tile_amd as tkt
 from oracle.attention_bwd import attention_backward
-from parity_util import check_attention, say, to_dev
+from parity_util import check_attention, check_selection, say, to_dev
 from test_gpu_backward import _compare
 
 pytestmark = pytest.mark.gpu
@@ -66,3 +67,43 @@ def test_planned_selection_equals_select():
         assert abs(b.density() - float(b.keep.float().mean().item())) < 1e-12
     dense_plan = tkt.nsa_plan_create(to_dev(q0), to_dev(k0), tkt.SparseSpec(budget=1.0))
     assert tkt.nsa_select_planned(dense_plan, to_dev(q0), to_dev(k0)) is None
+
+
+def test_select_plan_cache_keys_on_masks():
+    """nsa_select caches its plan. A call whose drops differ from the previous
+    call's in one candidate tile (same shapes, spec and pins) gets the plan of
+    its own masks, and the first mask set still finds its own: every selection
+    matches the oracle for the masks it was given."""
+    say("plan cache keyed on masks")
+    B, Hq, Hkv, S, D, bq, bkv, budget = 1, 4, 2, 2048, 128, 128, 64, 0.25
+    nq, nk = S // bq, S // bkv
+    rng = np.random.default_rng(5)
+    pins = np.zeros((1, 1, nq, nk), np.int8)
+    pins[..., 0] = 1
+    drops = (rng.random((1, Hq, nq, nk)) < 0.05).astype(np.int8)
+    plan = oracle.selection_plan(nq, nk, bq, bkv, budget, B, Hq, pins, drops)
+    flip = None
+    for h in range(Hq):
+        for i in range(nq):
+            c = int(plan["c"][0, h, i])
+            if c > 1 and int(oracle.keep_per_row(np.array([c - 1]), budget)[0]) != int(plan["k"][0, h, i]):
+                flip = (h, i, int(np.nonzero(plan["candidates"][0, h, i])[0][0]))
+                break
+        if flip:
+            break
+    assert flip is not None
+    drops2 = drops.copy()
+    drops2[0, flip[0], flip[1], flip[2]] = 1
+    q, k, _, _ = _inputs(B, Hq, Hkv, S, D, seed=9)
+    qd, kd = to_dev(q), to_dev(k)
+    spec = tkt.SparseSpec(budget=budget, block_q=bq, block_kv=bkv)
+    tkt.nsa_plan_cache_clear()
+    nnz = []
+    for d in (drops, drops2, drops):
+        sel = tkt.nsa_select(qd, kd, spec, pins, d)
+        ref = oracle.select_blocks(q, k, budget, bq, bkv, False, False, pins, d)
+        check_selection(sel, ref, "cached plan")
+        nnz.append(int(sel.row_ptr[-1].item()))
+    assert nnz[0] != nnz[1] and nnz[0] == nnz[2]
+    hits, misses, _ = tkt.nsa_plan_cache_stats()
+    assert misses == 2 and hits == 4  # nsa_select_sizes and nsa_select look up once each per call

@@ -23,6 +23,9 @@ from .nsa import (  # noqa: F401
     nsa_decode_pool_update,
     nsa_decode_select,
     nsa_permute_tokens,
+    nsa_plan_cache_clear,
+    nsa_plan_cache_config,
+    nsa_plan_cache_stats,
     nsa_plan_create,
     nsa_pool_blocks,
     nsa_radial_blocks,

@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -784,6 +785,157 @@ int validate_bwd(const nsa_tensor* q, const nsa_tensor* k, const nsa_tensor* v, 
     if (sel && (int64_t)sel->B * sel->H * sel->NQ * sel->NK > 0 && !sel->keep) return NSA_ERR_NULL_ARG;
     return NSA_OK;
 }
+
+// ---- plan cache of nsa_select / nsa_select_sizes ---------------------------
+//
+// The selection page caches its plan (must / forbidden / candidates / keep
+// counts) under a caller key, the tile counts, the block sizes, the budget and
+// the device (selector.py, selection_plan). The pins and drops are not part of
+// that key, so a plan built for one mask set is returned for another under the
+// same caller key. Here the key is the whole request: the q and k shapes and
+// dtypes, every spec field, and the shape and bytes of both masks (a 64-bit
+// hash rejects quickly, a byte comparison confirms). Entries hold host plans
+// only, no device memory, so evicting one (least recently used) never waits
+// for device work; an entry in use by a call stays alive until that call ends.
+struct PlanCacheEntry {
+    nsa_tensor q, k;  // data pointers cleared
+    nsa_spec spec;
+    int32_t pdims[4], ddims[4];  // all -1 when the mask is absent
+    uint64_t phash = 0, dhash = 0;
+    std::vector<int8_t> pins, drops;  // copies of the mask bytes
+    std::shared_ptr<const Plan> plan;
+    uint64_t stamp = 0;
+};
+struct PlanCache {
+    std::mutex mu;
+    std::vector<PlanCacheEntry> entries;
+    size_t capacity = 8;
+    uint64_t clock = 0;
+    int64_t hits = 0, misses = 0;
+};
+PlanCache& plan_cache() {
+    static PlanCache c;
+    return c;
+}
+
+size_t mask_bytes(const nsa_mask* m) {
+    return m ? (size_t)m->b_dim * m->h_dim * m->nq * m->nk : 0;
+}
+// Four independent multiply-xor lanes over 8-byte words (a fast reject, not a
+// proof of equality).
+uint64_t mask_hash(const nsa_mask* m) {
+    if (!m) return 0;
+    const size_t n = mask_bytes(m);
+    const unsigned char* p = (const unsigned char*)m->data;
+    const uint64_t mul = 0xff51afd7ed558ccdull;
+    uint64_t h[4] = {0x9E3779B97F4A7C15ull ^ n, 0xC2B2AE3D27D4EB4Full, 0x165667B19E3779F9ull, 0x27D4EB2F165667C5ull};
+    size_t i = 0;
+    for (; i + 32 <= n; i += 32)
+        for (int l = 0; l < 4; ++l) {
+            uint64_t w;
+            std::memcpy(&w, p + i + 8 * l, 8);
+            h[l] = (h[l] ^ w) * mul;
+            h[l] ^= h[l] >> 29;
+        }
+    uint64_t r = h[0] ^ (h[1] * 3) ^ (h[2] * 5) ^ (h[3] * 7);
+    for (; i < n; ++i) {
+        r = (r ^ p[i]) * mul;
+        r ^= r >> 29;
+    }
+    return r;
+}
+void mask_dims(const nsa_mask* m, int32_t* d) {
+    if (!m) {
+        d[0] = d[1] = d[2] = d[3] = -1;
+        return;
+    }
+    d[0] = m->b_dim;
+    d[1] = m->h_dim;
+    d[2] = m->nq;
+    d[3] = m->nk;
+}
+bool same_tensor_shape(const nsa_tensor& a, const nsa_tensor& b) {
+    return a.dtype == b.dtype && a.B == b.B && a.H == b.H && a.S == b.S && a.D == b.D;
+}
+bool same_spec(const nsa_spec& a, const nsa_spec& b) {
+    uint32_t ba, bb;
+    std::memcpy(&ba, &a.budget, 4);
+    std::memcpy(&bb, &b.budget, 4);
+    return ba == bb && a.block_q == b.block_q && a.block_kv == b.block_kv && a.head_shared == b.head_shared &&
+           a.force == b.force && a.score_chunk_bytes == b.score_chunk_bytes;
+}
+bool same_mask(const int32_t* dims, const std::vector<int8_t>& bytes, uint64_t hash, const nsa_mask* m,
+               uint64_t mhash) {
+    int32_t md[4];
+    mask_dims(m, md);
+    if (std::memcmp(dims, md, sizeof md) != 0 || hash != mhash) return false;
+    const size_t n = mask_bytes(m);
+    return n == bytes.size() && (n == 0 || std::memcmp(bytes.data(), m->data, n) == 0);
+}
+
+// The plan of a validated request (g from validate_select), from the cache or
+// built (and cached) now.
+int cached_plan(const Geo& g, const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, const nsa_mask* pins,
+                const nsa_mask* drops, std::shared_ptr<const Plan>& out) {
+    PlanCache& c = plan_cache();
+    size_t cap;
+    {
+        std::lock_guard<std::mutex> lock(c.mu);
+        cap = c.capacity;
+    }
+    const uint64_t ph = cap ? mask_hash(pins) : 0, dh = cap ? mask_hash(drops) : 0;
+    auto find = [&]() -> PlanCacheEntry* {  // caller holds c.mu
+        for (PlanCacheEntry& e : c.entries) {
+            if (!same_tensor_shape(e.q, *q) || !same_tensor_shape(e.k, *k) || !same_spec(e.spec, *spec)) continue;
+            if (!same_mask(e.pdims, e.pins, e.phash, pins, ph) || !same_mask(e.ddims, e.drops, e.dhash, drops, dh))
+                continue;
+            return &e;
+        }
+        return nullptr;
+    };
+    if (cap) {
+        std::lock_guard<std::mutex> lock(c.mu);
+        if (PlanCacheEntry* e = find()) {
+            e->stamp = ++c.clock;
+            ++c.hits;
+            out = e->plan;
+            return NSA_OK;
+        }
+    }
+    auto built = std::make_shared<Plan>();
+    const int st = build_plan(g, spec, pins, drops, *built, true);
+    if (st != NSA_OK) return st;
+    out = built;
+    std::lock_guard<std::mutex> lock(c.mu);
+    ++c.misses;
+    if (c.capacity == 0 || !cap) return NSA_OK;
+    if (PlanCacheEntry* e = find()) {  // another caller built the same plan meanwhile
+        e->stamp = ++c.clock;
+        return NSA_OK;
+    }
+    PlanCacheEntry e;
+    e.q = *q;
+    e.k = *k;
+    e.q.data = nullptr;
+    e.k.data = nullptr;
+    e.spec = *spec;
+    mask_dims(pins, e.pdims);
+    mask_dims(drops, e.ddims);
+    e.phash = ph;
+    e.dhash = dh;
+    if (pins) e.pins.assign(pins->data, pins->data + mask_bytes(pins));
+    if (drops) e.drops.assign(drops->data, drops->data + mask_bytes(drops));
+    e.plan = built;
+    e.stamp = ++c.clock;
+    if (c.entries.size() >= c.capacity) {
+        auto lru = std::min_element(c.entries.begin(), c.entries.end(),
+                                    [](const PlanCacheEntry& a, const PlanCacheEntry& b) { return a.stamp < b.stamp; });
+        *lru = std::move(e);
+    } else {
+        c.entries.push_back(std::move(e));
+    }
+    return NSA_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -815,10 +967,10 @@ int nsa_select_sizes(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* s
         Geo g;
         int st = validate_select(q, k, spec, pins, drops, g);
         if (st != NSA_OK) return st;
-        Plan p;
-        st = build_plan(g, spec, pins, drops, p, row_ptr_host != nullptr);
+        std::shared_ptr<const Plan> p;
+        st = cached_plan(g, q, k, spec, pins, drops, p);
         if (st != NSA_OK) return st;
-        fill_sizes(p, spec, out, row_ptr_host);
+        fill_sizes(*p, spec, out, row_ptr_host);
         return NSA_OK;
     } catch (...) {
         return NSA_ERR_UNSUPPORTED;
@@ -833,10 +985,10 @@ int nsa_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, c
         Geo g;
         int st = validate_select(q, k, spec, pins, drops, g);
         if (st != NSA_OK) return st;
-        Plan p;
-        st = build_plan(g, spec, pins, drops, p, true);
+        std::shared_ptr<const Plan> p;
+        st = cached_plan(g, q, k, spec, pins, drops, p);
         if (st != NSA_OK) return st;
-        return run_select(q, k, spec, p, out, workspace, workspace_bytes, (hipStream_t)stream_);
+        return run_select(q, k, spec, *p, out, workspace, workspace_bytes, (hipStream_t)stream_);
     } catch (...) {
         return NSA_ERR_UNSUPPORTED;
     }
@@ -923,6 +1075,37 @@ int nsa_select_planned(const nsa_plan* plan, const nsa_tensor* q, const nsa_tens
 }
 
 void nsa_plan_destroy(nsa_plan* plan) { delete plan; }
+
+int nsa_plan_cache_config(int32_t capacity) {
+    if (capacity < 0) return NSA_ERR_BAD_SPEC;
+    PlanCache& c = plan_cache();
+    std::lock_guard<std::mutex> lock(c.mu);
+    c.capacity = (size_t)capacity;
+    if (c.entries.size() > c.capacity) {  // keep the most recently used
+        std::sort(c.entries.begin(), c.entries.end(),
+                  [](const PlanCacheEntry& a, const PlanCacheEntry& b) { return a.stamp > b.stamp; });
+        c.entries.resize(c.capacity);
+    }
+    return NSA_OK;
+}
+
+void nsa_plan_cache_clear(void) {
+    PlanCache& c = plan_cache();
+    std::lock_guard<std::mutex> lock(c.mu);
+    c.entries.clear();
+    c.hits = 0;
+    c.misses = 0;
+}
+
+int nsa_plan_cache_stats(int64_t* hits, int64_t* misses, int32_t* entries) {
+    if (!hits || !misses || !entries) return NSA_ERR_NULL_ARG;
+    PlanCache& c = plan_cache();
+    std::lock_guard<std::mutex> lock(c.mu);
+    *hits = c.hits;
+    *misses = c.misses;
+    *entries = (int32_t)c.entries.size();
+    return NSA_OK;
+}
 
 int nsa_schedule(int32_t steps, double budget, double bump, int32_t bump_steps, double* out) {
     if (steps > 0 && !out) return NSA_ERR_NULL_ARG;

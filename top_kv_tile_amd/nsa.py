@@ -24,7 +24,8 @@ __all__ = [
     "nsa_pool_blocks", "nsa_score_blocks", "nsa_status_string", "Plan", "nsa_plan_create",
     "nsa_select_planned", "nsa_schedule", "nsa_radial_blocks", "nsa_selection_density", "nsa_curve_order",
     "nsa_permute_tokens", "NSA_CURVE_MORTON", "NSA_CURVE_HILBERT", "nsa_decode_pool_update", "nsa_decode_select",
-    "nsa_decode_attn", "LIB_PATH", "EXPORTS",
+    "nsa_decode_attn", "nsa_plan_cache_config", "nsa_plan_cache_clear", "nsa_plan_cache_stats", "LIB_PATH",
+    "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnsa.so")
@@ -33,7 +34,8 @@ EXPORTS = ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_attn_
            "nsa_last_hip_error", "nsa_version", "nsa_plan_create", "nsa_plan_sizes", "nsa_select_planned",
            "nsa_plan_destroy", "nsa_schedule", "nsa_radial_sizes", "nsa_radial_blocks", "nsa_selection_density",
            "nsa_curve_order", "nsa_permute_tokens", "nsa_decode_pool_update", "nsa_decode_select_sizes",
-           "nsa_decode_select", "nsa_decode_attn", "nsa_decode_attn_workspace_size")
+           "nsa_decode_select", "nsa_decode_attn", "nsa_decode_attn_workspace_size", "nsa_plan_cache_config",
+           "nsa_plan_cache_clear", "nsa_plan_cache_stats")
 
 NSA_OK, NSA_DENSE = 0, 1
 NSA_F32, NSA_BF16 = 0, 1
@@ -107,6 +109,10 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_size_t, ctypes.c_void_p]
         L.nsa_plan_destroy.argtypes = [ctypes.c_void_p]
         L.nsa_plan_destroy.restype = None
+        L.nsa_plan_cache_config.argtypes = [ctypes.c_int32]
+        L.nsa_plan_cache_clear.argtypes = []
+        L.nsa_plan_cache_clear.restype = None
+        L.nsa_plan_cache_stats.argtypes = [P(ctypes.c_int64), P(ctypes.c_int64), P(ctypes.c_int32)]
         L.nsa_schedule.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_double, ctypes.c_int32,
                                    P(ctypes.c_double)]
         L.nsa_radial_sizes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_double, P(_Spec), P(_Sizes),
@@ -135,7 +141,7 @@ def lib() -> ctypes.CDLL:
                      "nsa_plan_create", "nsa_plan_sizes", "nsa_select_planned", "nsa_schedule", "nsa_radial_sizes",
                      "nsa_radial_blocks", "nsa_selection_density", "nsa_curve_order", "nsa_permute_tokens",
                      "nsa_decode_pool_update", "nsa_decode_select_sizes", "nsa_decode_select", "nsa_decode_attn",
-                     "nsa_decode_attn_workspace_size"):
+                     "nsa_decode_attn_workspace_size", "nsa_plan_cache_config", "nsa_plan_cache_stats"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -393,6 +399,23 @@ def nsa_select_planned(plan: Plan, q: torch.Tensor, k: torch.Tensor, stream=None
                                          ctypes.byref(csel), ctypes.c_void_p(workspace.data_ptr()),
                                          workspace.numel(), _stream(stream)), "nsa_select_planned")
     return None if st == NSA_DENSE else sel
+
+
+def nsa_plan_cache_config(capacity: int) -> None:
+    """Plans kept by the cache of nsa_select / nsa_select_sizes (0 disables it)."""
+    _check(lib().nsa_plan_cache_config(int(capacity)), "nsa_plan_cache_config")
+
+
+def nsa_plan_cache_clear() -> None:
+    """Drops every cached plan and zeroes the counters."""
+    lib().nsa_plan_cache_clear()
+
+
+def nsa_plan_cache_stats() -> tuple:
+    """(hits, misses, entries) of the plan cache."""
+    h, m, e = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    _check(lib().nsa_plan_cache_stats(ctypes.byref(h), ctypes.byref(m), ctypes.byref(e)), "nsa_plan_cache_stats")
+    return h.value, m.value, e.value
 
 
 def nsa_schedule(steps: int, budget: float, bump: float = 0.0, bump_steps: int = 0) -> tuple:

@@ -181,8 +181,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     const int kv_bytes = a.Skv * G::ROWB;          // the keys of one kv head
     const __amdgpu_buffer_rsrc_t qrs =
         make_rsrc((const uint16_t*)a.q + (((int64_t)wk.b * a.Hq + wk.h) * a.S) * D, head_bytes);
-    const u32x4 krs = rsrc_words((const uint16_t*)a.k + ((int64_t)wk.b * a.Hkv + wk.g) * a.kv_rows * D, kv_bytes);
-    const u32x4 vrs = rsrc_words((const uint16_t*)a.v + ((int64_t)wk.b * a.Hkv + wk.g) * a.kv_rows * D, kv_bytes);
+    const uint16_t* kbase = (const uint16_t*)a.k + ((int64_t)wk.b * a.Hkv + wk.g) * a.kv_rows * D;
+    const uint16_t* vbase = (const uint16_t*)a.v + ((int64_t)wk.b * a.Hkv + wk.g) * a.kv_rows * D;
 
     // Q^T operand: lane holds q[qrow][16*ks + 8*hf .. +8] for every ks (zeros past S).
     bf16x8 qf[KSTEPS];
@@ -224,33 +224,37 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     // DMA: wave w issues instructions w, w + NW, ...; lane L of instruction ii
     // fills LDS bytes ii*1024 + 16L, i.e. row ii*RPI + L/CH, physical chunk L%CH,
     // from the logical chunk given by the row's swizzle.
-    // Rows past the end of the sequence (ragged last tile) read row S - 1
-    // instead: in range, finite, and masked out (K) or weighted by p = 0 (V).
     // The DMA is issued by the instruction itself and every wait on it is
     // explicit (vmcnt(0) at the end of a step), so the tiles of step n + 1 stay
     // in flight through the whole of step n, transposed V reads included.
-    // (Row and chunk offsets are recomputed from the lane index at each issue
-    // rather than kept in registers: a spilled register's reload is a vector
-    // memory load, and waiting for it would also wait for the tiles in flight.)
     char* kst[2] = {lds, lds + G::TILEB};
     char* vst[2] = {lds + 2 * G::TILEB, lds + 3 * G::TILEB};
     const uint32_t lds0 = lds_address(lds);
-    auto dma = [&](u32x4 rs, bool is_v, char* stage_base, int j) {
-        const int key0 = j * BKV;
-        const uint32_t base = lds0 + (uint32_t)(stage_base - lds);
+    // Per-lane source offsets inside a tile of this wave's DMA instructions
+    // (they do not depend on the tile); the tile itself is selected by the
+    // base of the buffer resource, whose record count ends at the last key,
+    // so the rows of a ragged last tile past it read as zeros (their keys
+    // are masked, so P = 0 for them).
+    int kvo[IPW], vvo[IPW];
+#pragma unroll
+    for (int x = 0; x < IPW; ++x) {
+        const int ii = wave + NW * x;
+        const int row = ii * G::RPI + lane / G::CH, pc = lane % G::CH;
+        kvo[x] = row * G::ROWB + (pc ^ G::kswz(row)) * 16;
+        vvo[x] = row * G::ROWB + (pc ^ G::vswz(row)) * 16;
+    }
+    auto dma = [&](const uint16_t* base, const int (&vo)[IPW], char* stage_base, int j) {
+        const uint32_t off = (uint32_t)j * (BKV * G::ROWB);
+        const u32x4 rs = rsrc_words((const char*)base + off, (uint32_t)kv_bytes - off);
+        const uint32_t sb = lds0 + (uint32_t)(stage_base - lds);
 #pragma unroll
         for (int x = 0; x < IPW; ++x) {
             const int ii = wave + NW * x;
-            if (G::NINSTR % NW == 0 || ii < G::NINSTR) {
-                const int row = ii * G::RPI + lane / G::CH, pc = lane % G::CH;
-                const int chunk = pc ^ (is_v ? G::vswz(row) : G::kswz(row));
-                const int off = min(key0 + row, a.Skv - 1) * G::ROWB + chunk * 16;
-                dma16(rs, base + ii * 1024, off);
-            }
+            if (G::NINSTR % NW == 0 || ii < G::NINSTR) dma16(rs, sb + ii * 1024, vo[x]);
         }
     };
-    auto dma_k = [&](int j, int stage) { dma(krs, false, kst[stage], j); };
-    auto dma_v = [&](int j, int stage) { dma(vrs, true, vst[stage], j); };
+    auto dma_k = [&](int j, int stage) { dma(kbase, kvo, kst[stage], j); };
+    auto dma_v = [&](int j, int stage) { dma(vbase, vvo, vst[stage], j); };
 
     // LDS read offsets (bytes) that do not depend on the tile.
     // K: lane reads row 32*mb + l32, logical chunk 2*ks + hf.

@@ -437,22 +437,33 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_mfma_kernel(AttnBwdArgs a) 
     // Tile DMA through the instruction itself (the compiler does not track it,
     // so the transposed K reads of step n do not wait for the tiles of step
     // n + 1); every wait on it is explicit.
-    const u32x4 krw = rsrc_words((const uint16_t*)a.k + khead * D, head_bytes);
-    const u32x4 vrw = rsrc_words((const uint16_t*)a.v + khead * D, head_bytes);
+    // Per-lane source offsets inside a tile (independent of the tile); the
+    // tile is selected by the base of the buffer resource, whose record count
+    // ends at the last key, so rows of a ragged last tile past it read as
+    // zeros (their keys are masked: P = 0, dS = 0).
+    constexpr int IPW = (G::NINSTR + NW - 1) / NW;
+    const uint16_t* kbase = (const uint16_t*)a.k + khead * D;
+    const uint16_t* vbase = (const uint16_t*)a.v + khead * D;
     const uint32_t lds0 = lds_address(lds);
-    auto dma = [&](u32x4 rs, bool both, int st_off, int row0) {
+    int kvo[IPW], vvo[IPW];
 #pragma unroll
-        for (int x = 0; x < (G::NINSTR + NW - 1) / NW; ++x) {
+    for (int x = 0; x < IPW; ++x) {
+        const int ii = wave + NW * x;
+        const int row = ii * G::RPI + lane / G::CH, pc = lane % G::CH;
+        kvo[x] = row * G::ROWB + (pc ^ G::bswz(row)) * 16;
+        vvo[x] = row * G::ROWB + (pc ^ G::rswz(row)) * 16;
+    }
+    auto dma = [&](const uint16_t* base, const int (&vo)[IPW], int st_off, int j) {
+        const uint32_t off = (uint32_t)j * (64 * G::ROWB);
+        const u32x4 rs = rsrc_words((const char*)base + off, (uint32_t)head_bytes - off);
+#pragma unroll
+        for (int x = 0; x < IPW; ++x) {
             const int ii = wave + NW * x;
-            if (G::NINSTR % NW == 0 || ii < G::NINSTR) {
-                const int row = ii * G::RPI + lane / G::CH, pc = lane % G::CH;
-                const int chunk = pc ^ (both ? G::bswz(row) : G::rswz(row));
-                dma16(rs, lds0 + st_off + ii * 1024, min(row0 + row, a.S - 1) * G::ROWB + chunk * 16);
-            }
+            if (G::NINSTR % NW == 0 || ii < G::NINSTR) dma16(rs, lds0 + st_off + ii * 1024, vo[x]);
         }
     };
-    auto dma_k = [&](int st, int j) { dma(krw, true, st * G::TILEB, j * 64); };
-    auto dma_v = [&](int st, int j) { dma(vrw, false, (2 + st) * G::TILEB, j * 64); };
+    auto dma_k = [&](int st, int j) { dma(kbase, kvo, st * G::TILEB, j); };
+    auto dma_v = [&](int st, int j) { dma(vbase, vvo, (2 + st) * G::TILEB, j); };
 
     int j_cur = 0;
     // The Q / dO loads are the only loads the compiler tracks: settle them

@@ -41,10 +41,13 @@ def test_pool_blocks(dtype, S, D, block):
     assert (got - ref).abs().max().item() <= bound
 
 
-@pytest.mark.parametrize("Hq,Hkv,shared", [(4, 4, False), (8, 2, False), (6, 3, True)])
-def test_score_blocks(Hq, Hkv, shared):
-    say(f"scores Hq={Hq} Hkv={Hkv} shared={shared}")
-    S, D, bq, bkv = 2000, 128, 128, 64
+@pytest.mark.parametrize("Hq,Hkv,shared,S,D,bq,bkv", [
+    (4, 4, False, 2000, 128, 128, 64), (8, 2, False, 2000, 128, 128, 64), (6, 3, True, 2000, 128, 128, 64),
+    # more than 64 query tiles (the LDS-staged kernel), ragged in both block dimensions
+    (4, 2, False, 20000, 128, 128, 64), (2, 1, False, 9000, 64, 64, 32), (2, 2, True, 12000, 256, 128, 64),
+])
+def test_score_blocks(Hq, Hkv, shared, S, D, bq, bkv):
+    say(f"scores Hq={Hq} Hkv={Hkv} shared={shared} S={S} D={D} bq={bq} bkv={bkv}")
     q, k, _ = _qkv(1, Hq, Hkv, S, D, seed=Hq * 7 + Hkv, dtype=torch.bfloat16)
     spec = tkt.SparseSpec(block_q=bq, block_kv=bkv, head_shared=shared)
     got = tkt.nsa_score_blocks(to_dev(q), to_dev(k), spec).cpu().numpy().astype(np.float64)

@@ -231,6 +231,111 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qh
     store(c11, 32, 32);
 }
 
+// The same product for many query rows (NQ > 64), one 128 x 256 block per
+// workgroup: wave w takes query rows 64 (w / 2) .. + 63 and key columns
+// 128 (w % 2) .. + 127 (2 x 4 blocks of 32 x 32 as above). Loading each lane's
+// own rows from L2 touches a cache line per lane and every wave of a workgroup
+// reloads the rows it shares with the others, so here the operands go through
+// LDS in chunks of 32 contraction indices: the workgroup loads the chunk's 128
+// pooled-query rows and 256 pooled-key rows with 8 lanes per 128-byte row
+// segment, one chunk ahead in registers, and stores them to LDS with rows
+// padded to 36 floats (16-byte reads of 16 consecutive rows then fall in
+// distinct banks). At step (g, e) of a chunk, lane half hf supplies
+// contraction index 16*hf + 4*g + e.
+template <int D>
+__global__ __launch_bounds__(256) void score_lds_kernel(const float* __restrict__ qh, const float* __restrict__ kh,
+                                                        int Hsel, int Hk, int group, int h0, int nh, int NQ,
+                                                        int NK, int NKs, int nbi, int nbj, float* __restrict__ s) {
+    constexpr int KC = 32, PAD = 36, ROWS = 128, COLS = 256;
+    __shared__ __attribute__((aligned(16))) float As[ROWS * PAD];
+    __shared__ __attribute__((aligned(16))) float Bs[COLS * PAD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int64_t wid = blockIdx.x;
+    const int bj = (int)(wid % nbj);
+    wid /= nbj;
+    const int bi = (int)(wid % nbi);
+    wid /= nbi;
+    const int hl = (int)(wid % nh);
+    const int b = (int)(wid / nh);
+    const int h = h0 + hl;
+    const int hk = (Hk == 1) ? 0 : h / group;
+    const float* A = qh + ((int64_t)b * Hsel + h) * NQ * D;
+    const float* Bm = kh + ((int64_t)b * Hk + hk) * NKs * D;  // NKs >= NK rows per head
+    const int i0 = bi * ROWS, j0 = bj * COLS;
+
+    // Global loads: thread t takes rows t / 8 + 32 x (x < 4), floats 4 (t % 8) .. + 3
+    // of the chunk (rows past the end repeat the last row; their results are not stored).
+    const int lr = tid >> 3, lq = tid & 7;
+    const float* ag[4];
+    const float* bg[8];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) ag[x] = A + (int64_t)min(i0 + lr + 32 * x, NQ - 1) * D + 4 * lq;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) bg[x] = Bm + (int64_t)min(j0 + lr + 32 * x, NK - 1) * D + 4 * lq;
+    f32x4 ra[4], rb[8];
+    auto gload = [&](int kc) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) ra[x] = *(const f32x4*)(ag[x] + kc);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) rb[x] = *(const f32x4*)(bg[x] + kc);
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) *(f32x4*)(As + (lr + 32 * x) * PAD + 4 * lq) = ra[x];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) *(f32x4*)(Bs + (lr + 32 * x) * PAD + 4 * lq) = rb[x];
+    };
+    const int wi = wave >> 1, wj = wave & 1;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const float* a0l = As + (wi * 64 + l32) * PAD + 16 * hf;
+    const float* a1l = a0l + 32 * PAD;
+    const float* b0l = Bs + (wj * 128 + l32) * PAD + 16 * hf;
+
+    f32x16 c0[4] = {}, c1[4] = {};
+    gload(0);
+#pragma unroll
+    for (int kc = 0; kc < D; kc += KC) {
+        __syncthreads();  // the previous chunk's LDS reads are done
+        lstore();
+        __syncthreads();
+        if (kc + KC < D) gload(kc + KC);  // in flight under this chunk's products
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 x0 = *(const f32x4*)(a0l + 4 * g), x1 = *(const f32x4*)(a1l + 4 * g);
+            f32x4 y[4];
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) y[jb] = *(const f32x4*)(b0l + jb * 32 * PAD + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) {
+                    c0[jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0[e], y[jb][e], c0[jb], 0, 0, 0);
+                    c1[jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1[e], y[jb][e], c1[jb], 0, 0, 0);
+                }
+        }
+    }
+    // Accumulator layout of a 32 x 32 block: lane holds column l32 and rows
+    // 8*q + 4*hf + e at element 4*q + e.
+    float* out = s + ((int64_t)b * nh + hl) * NQ * NK;
+    const int r0 = i0 + wi * 64, cb = j0 + wj * 128;
+    auto store = [&](const f32x16& c, int ib, int jb) {
+        const int col = cb + jb + l32;
+        if (col >= NK) return;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = r0 + ib + 8 * q + 4 * hf + e;
+                if (row < NQ) out[(int64_t)row * NK + col] = c[4 * q + e];
+            }
+    };
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+        store(c0[jb], 0, 32 * jb);
+        store(c1[jb], 32, 32 * jb);
+    }
+}
+
 // Scores of a few query rows (NQ <= 8, e.g. while decoding): a 64 x 64 MFMA
 // block would be almost all padding, so one thread takes one kv tile and
 // forms its dot products with the (at most 8) pooled query rows held in LDS.
@@ -538,6 +643,19 @@ hipError_t launch_scores(const float* qh, const float* kh, int B, int Hsel, int 
         else if (D == 256) NSA_ROWS(256);
         else return hipErrorInvalidValue;
 #undef NSA_ROWS
+        return hipGetLastError();
+    }
+    if (NQ > 64) {
+        const int nbi = (NQ + 127) / 128, nbj = (NK + 255) / 256;
+        const dim3 grid((unsigned)((int64_t)B * nh * nbi * nbj));
+#define NSA_SCORE_LDS(DD)                                                                                     \
+    hipLaunchKernelGGL((score_lds_kernel<DD>), grid, dim3(256), 0, stream, qh, kh, Hsel, Hk, group, h0, nh, NQ, \
+                       NK, NKs, nbi, nbj, s)
+        if (D == 64) NSA_SCORE_LDS(64);
+        else if (D == 128) NSA_SCORE_LDS(128);
+        else if (D == 256) NSA_SCORE_LDS(256);
+        else return hipErrorInvalidValue;
+#undef NSA_SCORE_LDS
         return hipGetLastError();
     }
     const int nbi = (NQ + 63) / 64, nbj = (NK + 63) / 64;

@@ -171,6 +171,63 @@ def test_all_tied_scores_pick_lowest_index():
     say(f"  {rep}")
 
 
+def test_few_long_rows():
+    """Few selection rows (a workgroup per row) with 4096 kv tiles each, pins
+    and drops, against the oracle; attention on sampled rows."""
+    say("few long rows")
+    B, Hq, Hkv, S, D = 1, 2, 1, 65536, 64
+    q, k, v = _qkv(B, Hq, Hkv, S, D, seed=19, dtype=torch.bfloat16)
+    spec = tkt.SparseSpec(budget=0.05, block_q=1024, block_kv=16)
+    nq, nk = S // 1024, S // 16
+    rng = np.random.default_rng(19)
+    pins = (rng.random((1, 1, nq, nk)) < 0.01).astype(np.int8)
+    drops = (rng.random((1, Hq, nq, nk)) < 0.02).astype(np.int8)
+    rep = run_case(q, k, v, spec, True, pins=pins, drops=drops, rows=[(0, 0, 5), (0, 1, 63)], where="few long rows")
+    say(f"  {rep}")
+
+
+@pytest.mark.parametrize("S,bq,bkv", [(16384, 256, 16), (8192, 128, 32)])
+def test_exact_ties_take_lowest_index(S, bq, bkv):
+    """Every kv tile repeats one of three key vectors, so pooled keys are exact
+    copies and a row's scores fall into three groups of exactly equal values,
+    well apart from each other. The boundary group must be cut at the lowest
+    kv indices (score descending, index ascending): the expected keep is built
+    from float64 group scores and compared bit for bit, pins and drops
+    included."""
+    say(f"exact ties S={S} bq={bq} bkv={bkv}")
+    B, Hq, Hkv, D = 1, 2, 1, 64
+    g = torch.Generator().manual_seed(S + bq)
+    q = torch.randn(B, Hq, S, D, generator=g).to(torch.bfloat16)
+    V = torch.randn(3, D, generator=g).to(torch.bfloat16)
+    nq, nk = S // bq, S // bkv
+    tile_of = torch.arange(S) // bkv
+    k = V[tile_of % 3].reshape(1, 1, S, D).contiguous()
+    rng = np.random.default_rng(S)
+    pins = (rng.random((1, 1, nq, nk)) < 0.02).astype(np.int8)
+    drops = (rng.random((1, Hq, nq, nk)) < 0.05).astype(np.int8)
+    budget = 0.2
+    spec = tkt.SparseSpec(budget=budget, block_q=bq, block_kv=bkv)
+    sel = tkt.nsa_select(to_dev(q), to_dev(k), spec, pins, drops)
+    torch.cuda.synchronize()
+    got = sel.keep.cpu().numpy() != 0
+    pq = oracle.pool_blocks(q, bq).double().numpy()                    # (B, Hq, NQ, D)
+    gs = pq @ V.double().numpy().T                                     # (B, Hq, NQ, 3) group scores
+    gap = np.sort(gs, -1)
+    # the groups are far apart next to fp32 rounding of a pooled score (~(bq + D) 2^-24 relative)
+    assert np.all(np.diff(gap, axis=-1) > 1e-4 * np.abs(gap).max())
+    plan = oracle.selection_plan(nq, nk, bq, bkv, budget, B, Hq, pins, drops)
+    want = plan["must"] & ~plan["forbidden"]
+    grp = np.arange(nk) % 3
+    for h in range(Hq):
+        for i in range(nq):
+            cand = np.nonzero(plan["candidates"][0, h, i])[0]
+            order = sorted(cand, key=lambda j: (-gs[0, h, i, grp[j]], j))
+            want[0, h, i, order[:int(plan["k"][0, h, i])]] = True
+    assert np.array_equal(got, want)
+    r_ptr, r_col = oracle.keep_to_csr(want.astype(np.int8))
+    assert np.array_equal(sel.row_ptr.cpu().numpy(), r_ptr) and np.array_equal(sel.col_idx.cpu().numpy(), r_col)
+
+
 def test_widest_row_nk4096():
     """NK = 4096 (64 score slots per lane), per-head GQA scoring, sampled attention rows."""
     say("nk4096")

@@ -337,14 +337,20 @@ __global__ __launch_bounds__(256) void score_lds_kernel(const float* __restrict_
 }
 
 // Scores of a few query rows (NQ <= 8, e.g. while decoding): a 64 x 64 MFMA
-// block would be almost all padding, so one thread takes one kv tile and
-// forms its dot products with the (at most 8) pooled query rows held in LDS.
+// block would be almost all padding. A workgroup takes 64 kv tiles of one
+// selection head: it stages their pooled keys in LDS with coalesced 16-byte
+// loads (rows padded by 4 floats) next to the (at most 8) pooled query rows;
+// then four consecutive threads share a tile, each summing a quarter of the
+// contraction, and two DPP steps add the four partial sums.
 template <int D>
 __global__ __launch_bounds__(256) void score_rows_kernel(const float* __restrict__ qh, const float* __restrict__ kh,
                                                          int Hsel, int Hk, int group, int h0, int nh, int NQ,
                                                          int NK, int NKs, float* __restrict__ s) {
-    __shared__ float qs[8 * D];
-    const int nbj = (NK + 255) / 256;
+    constexpr int KP = D + 4, QD = D / 4;
+    __shared__ __attribute__((aligned(16))) float qs[8 * D];
+    __shared__ __attribute__((aligned(16))) float ks[64 * KP];
+    const int tid = threadIdx.x;
+    const int nbj = (NK + 63) / 64;
     int64_t wid = blockIdx.x;
     const int jb = (int)(wid % nbj);
     wid /= nbj;
@@ -353,21 +359,28 @@ __global__ __launch_bounds__(256) void score_rows_kernel(const float* __restrict
     const int h = h0 + hl;
     const int hk = (Hk == 1) ? 0 : h / group;
     const float* A = qh + ((int64_t)b * Hsel + h) * NQ * D;
-    for (int x = threadIdx.x; x < NQ * D; x += 256) qs[x] = A[x];
+    const float* Bm = kh + ((int64_t)b * Hk + hk) * NKs * D;
+    const int j0 = jb * 64;
+    for (int x = tid; x < NQ * D / 4; x += 256) *(f32x4*)(qs + 4 * x) = *(const f32x4*)(A + 4 * x);
+    for (int x = tid; x < 64 * D / 4; x += 256) {
+        const int row = x / (D / 4), c4 = x % (D / 4);
+        const int j = min(j0 + row, NK - 1);  // rows past NK repeat the last one and are not stored
+        *(f32x4*)(ks + row * KP + 4 * c4) = *(const f32x4*)(Bm + (int64_t)j * D + 4 * c4);
+    }
     __syncthreads();
-    const int j = jb * 256 + threadIdx.x;
-    if (j >= NK) return;
-    const float* krow = kh + ((int64_t)b * Hk + hk) * NKs * D + (int64_t)j * D;
+    const int t = tid >> 2, part = tid & 3;
+    const float* kr = ks + t * KP + part * QD;
+    const float* qr = qs + part * QD;
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
 #pragma unroll 4
-    for (int d = 0; d < D; d += 4) {
-        const f32x4 kv = *(const f32x4*)(krow + d);
+    for (int d = 0; d < QD; d += 4) {
+        const f32x4 kv = *(const f32x4*)(kr + d);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             if (i < NQ) {
-                const float* qv = qs + i * D + d;
+                const f32x4 qv = *(const f32x4*)(qr + i * D + d);
                 acc[i] = __builtin_fmaf(qv[0], kv[0], acc[i]);
                 acc[i] = __builtin_fmaf(qv[1], kv[1], acc[i]);
                 acc[i] = __builtin_fmaf(qv[2], kv[2], acc[i]);
@@ -375,10 +388,21 @@ __global__ __launch_bounds__(256) void score_rows_kernel(const float* __restrict
             }
         }
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (i < NQ) {
+            float v = acc[i];
+            v += __builtin_bit_cast(float, dpp<0xB1>(__builtin_bit_cast(int, v)));  // quad_perm [1, 0, 3, 2]
+            v += __builtin_bit_cast(float, dpp<0x4E>(__builtin_bit_cast(int, v)));  // quad_perm [2, 3, 0, 1]
+            acc[i] = v;
+        }
+    }
+    const int j = j0 + t;
+    if (j >= NK) return;
     float* out = s + ((int64_t)b * nh + hl) * NQ * NK;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        if (i < NQ) out[(int64_t)i * NK + j] = acc[i];
+        if (i < NQ && (i & 3) == part) out[(int64_t)i * NK + j] = acc[i];
 }
 
 // ---------------------------------------------------------------- top-k
@@ -445,14 +469,16 @@ __device__ typename MaskT<EPL>::type select_top(const float (&s)[EPL], typename 
         for (int w = 0; w < NB; ++w) bk[w] = 0;
 #pragma unroll
         for (int t = 0; t < EPL; ++t) {
+            // after the first pass few elements remain: slots with none are skipped
+            const bool on = (active >> t) & 1;
+            if (__ballot(on) == 0) continue;
             const float x = s[t];
             const float u = ((half ? 0.5f * x : x) - lo_u) * scale;
             int b = (int)u;
             b = b > 254 ? 254 : (b < 0 ? 0 : b);
             b = (x == hi) ? 255 : b;
             bk[t >> 2] |= (uint32_t)b << (8 * (t & 3));
-            // inactive elements count into this lane's spare bin (256 + lane): no branch
-            atomicAdd(&hist[((active >> t) & 1) ? b : 256 + lane], 1u);
+            if (on) atomicAdd(&hist[b], 1u);
         }
         wave_lds_sync();
         // Lane L owns buckets 4L .. 4L+3. Count what lies strictly above each.
@@ -509,11 +535,11 @@ __device__ typename MaskT<EPL>::type select_top(const float (&s)[EPL], typename 
 
 template <int EPL>
 // Up to 2048 kv tiles per row the register budget is held to four waves per
-// SIMD (a few values spill): the kernel waits on LDS atomics and loads, and
-// more resident waves hide that better than the spills cost.
+// SIMD: the kernel waits on loads and LDS atomics, and more resident waves
+// hide that.
 __global__ __launch_bounds__(256, (EPL <= 32 ? 4 : 1)) void topk_kernel(TopkArgs a) {
     typedef typename MaskT<EPL>::type M;
-    __shared__ uint32_t hist_all[4][256 + 64];  // 256 buckets + one spare bin per lane
+    __shared__ uint32_t hist_all[4][256];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar row math
     uint32_t* hist = hist_all[wave];
@@ -544,16 +570,23 @@ __global__ __launch_bounds__(256, (EPL <= 32 ? 4 : 1)) void topk_kernel(TopkArgs
     for (int t = 0; t < EPL; ++t) s[t] = srow[min(64 * t + lane, a.NK - 1)];
     // Masks: wave-uniform 64-bit words per slot (bit = lane), built one slot
     // at a time on the scalar unit.
+    // The row's mask words arrive with one vector load (lane t holds word t)
+    // and are read back per slot with readlane.
     M cand = 0, must_kept = 0;
     int c = 0;
+    const int nw = (a.NK + 63) / 64;
+    const uint64_t pin_l = (pw && lane < nw) ? pw[lane] : 0ull;
+    const uint64_t drop_l = (dw && lane < nw) ? dw[lane] : 0ull;
 #pragma unroll 1
     for (int t = 0; t < EPL; ++t) {
         const int base = 64 * t;
         const int rem = a.NK - base;
         const uint64_t valid = rem >= 64 ? ~0ull : (rem > 0 ? (1ull << rem) - 1ull : 0ull);
         const uint64_t diag = range_bits(dlo - base, dhi - base);
-        const uint64_t pin = (pw && rem > 0) ? pw[t] : 0ull;
-        const uint64_t drop = (dw && rem > 0) ? dw[t] : 0ull;
+        const uint64_t pin = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pin_l >> 32), t) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pin_l, t);
+        const uint64_t drop = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(drop_l >> 32), t) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)drop_l, t);
         const uint64_t must = (diag | pin) & valid;
         const uint64_t cw = valid & ~must & ~drop;
         const uint64_t mk = must & ~drop;
@@ -584,6 +617,209 @@ __global__ __launch_bounds__(256, (EPL <= 32 ? 4 : 1)) void topk_kernel(TopkArgs
         const int slot = pos + __builtin_popcountll(m & below);
         if (kb && slot < row_len) crow[slot] = j;  // never write past the planned row
         pos += __builtin_popcountll(m);
+    }
+}
+
+// Top-k of few rows (e.g. decoding: one row per query head): one workgroup
+// of four waves per row, so that the row's work is spread over 256 lanes
+// instead of the 64 of topk_kernel. Element j = 256 t + 64 w + lane sits in
+// slot t of lane `lane` of wave w; the ballot of slot t in wave w is word
+// 4 t + w of the row's bit masks. The selection is the bucketing of
+// select_top, with candidate counts, extremes, the bucket histogram and the
+// index-ordered tie break and compaction reduced over the workgroup in LDS.
+template <int EPT>
+__global__ __launch_bounds__(256) void topk_rows_kernel(TopkArgs a) {
+    typedef uint32_t M;
+    __shared__ uint32_t hist[256];
+    __shared__ int red_i[4];
+    __shared__ float red_lo[4], red_hi[4];
+    __shared__ int bsel[2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t lr = blockIdx.x;
+    const int i = (int)(lr % a.NQ);
+    const int64_t bh = lr / a.NQ;
+    const int hl = (int)(bh % a.nh);
+    const int b = (int)(bh / a.nh);
+    const int h = a.h0 + hl;
+    const int64_t r = ((int64_t)b * a.Hsel + h) * a.NQ + i;
+    const float* srow = a.scores + lr * a.NK;
+    const uint64_t* pw =
+        a.pin_words ? a.pin_words + (((int64_t)(b % a.pb) * a.ph + (h % a.ph)) * a.NQ + i) * a.NKW : nullptr;
+    const uint64_t* dw =
+        a.drop_words ? a.drop_words + (((int64_t)(b % a.db) * a.dh + (h % a.dh)) * a.NQ + i) * a.NKW : nullptr;
+    const int dlo = (int)((a.q_off + (int64_t)i * a.block_q) / a.block_kv);
+    const int dhi = (int)((a.q_off + (int64_t)(i + 1) * a.block_q + a.block_kv - 1) / a.block_kv) - 1;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    auto block_sum = [&](int x) -> int {  // x wave-uniform
+        if (lane == 0) red_i[wave] = x;
+        __syncthreads();
+        const int t = red_i[0] + red_i[1] + red_i[2] + red_i[3];
+        __syncthreads();
+        return t;
+    };
+
+    float sc[EPT];
+#pragma unroll
+    for (int t = 0; t < EPT; ++t) sc[t] = srow[min(256 * t + 64 * wave + lane, a.NK - 1)];
+
+    // Masks: word 4 t + w of the row (lane x < EPT holds word 4 x + w).
+    const int nw = (a.NK + 63) / 64;
+    const int wx = 4 * lane + wave;
+    const uint64_t pin_l = (pw && lane < EPT && wx < nw) ? pw[wx] : 0ull;
+    const uint64_t drop_l = (dw && lane < EPT && wx < nw) ? dw[wx] : 0ull;
+    M cand = 0, must_kept = 0;
+    int cw_count = 0;
+#pragma unroll
+    for (int t = 0; t < EPT; ++t) {
+        const int base = 64 * (4 * t + wave);
+        const int rem = a.NK - base;
+        const uint64_t valid = rem >= 64 ? ~0ull : (rem > 0 ? (1ull << rem) - 1ull : 0ull);
+        const uint64_t diag = range_bits(dlo - base, dhi - base);
+        const uint64_t pin = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pin_l >> 32), t) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pin_l, t);
+        const uint64_t drop = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(drop_l >> 32), t) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)drop_l, t);
+        const uint64_t must = (diag | pin) & valid;
+        const uint64_t cw = valid & ~must & ~drop;
+        const uint64_t mk = must & ~drop;
+        cw_count += __builtin_popcountll(cw);
+        cand |= (M)((cw >> lane) & 1ull) << t;
+        must_kept |= (M)((mk >> lane) & 1ull) << t;
+    }
+    const int c = block_sum(cw_count);
+    const float kf = ceilf(__fmul_rn((float)c, a.budget));
+    const int k = (kf >= (float)c) ? c : (int)kf;
+
+    M picked = 0;
+    if (k >= c) {
+        picked = cand;
+    } else if (k > 0) {
+        M active = cand;
+        int need = k;
+        uint32_t bk[(EPT + 3) / 4];
+        for (int iter = 0; iter < 64 && need > 0; ++iter) {
+            const int na = block_sum(wave_sum_i(__builtin_popcount(active)));
+            if (na <= need) {
+                picked |= active;
+                need = 0;
+                break;
+            }
+            float lo = FLT_MAX, hi = -FLT_MAX;
+#pragma unroll
+            for (int t = 0; t < EPT; ++t) {
+                const bool on = (active >> t) & 1;
+                lo = fminf(lo, on ? sc[t] : FLT_MAX);
+                hi = fmaxf(hi, on ? sc[t] : -FLT_MAX);
+            }
+            lo = wave_min_f(lo);
+            hi = wave_max_f(hi);
+            if (lane == 0) {
+                red_lo[wave] = lo;
+                red_hi[wave] = hi;
+            }
+            hist[tid] = 0;
+            __syncthreads();
+            lo = fminf(fminf(red_lo[0], red_lo[1]), fminf(red_lo[2], red_lo[3]));
+            hi = fmaxf(fmaxf(red_hi[0], red_hi[1]), fmaxf(red_hi[2], red_hi[3]));
+            if (!(hi > lo)) break;  // every remaining score is equal: index order below (uniform)
+            const bool half = !(hi - lo <= FLT_MAX);
+            const float lo_u = half ? 0.5f * lo : lo;
+            const float range = half ? 0.5f * hi - 0.5f * lo : hi - lo;
+            float scale = 255.0f / range;
+            if (!(scale <= FLT_MAX)) scale = FLT_MAX;
+#pragma unroll
+            for (int w = 0; w < (EPT + 3) / 4; ++w) bk[w] = 0;
+#pragma unroll
+            for (int t = 0; t < EPT; ++t) {
+                const bool on = (active >> t) & 1;
+                const float x = sc[t];
+                const float u = ((half ? 0.5f * x : x) - lo_u) * scale;
+                int bb = (int)u;
+                bb = bb > 254 ? 254 : (bb < 0 ? 0 : bb);
+                bb = (x == hi) ? 255 : bb;
+                bk[t >> 2] |= (uint32_t)bb << (8 * (t & 3));
+                if (on) atomicAdd(&hist[bb], 1u);
+            }
+            __syncthreads();
+            if (wave == 0) {  // lane L owns buckets 4L .. 4L+3; count what lies strictly above each
+                const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
+                               h3 = hist[4 * lane + 3];
+                const int own = (int)(h0 + h1 + h2 + h3);
+                const int incl = wave_prefix_sum(own);
+                int ab = __builtin_amdgcn_readlane(incl, 63) - incl;
+                int found = -1, found_above = 0;
+                const uint32_t hh[4] = {h3, h2, h1, h0};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (found < 0 && ab < need && need <= ab + (int)hh[e]) {
+                        found = 4 * lane + 3 - e;
+                        found_above = ab;
+                    }
+                    ab += (int)hh[e];
+                }
+                if (found >= 0) {  // exactly one lane
+                    bsel[0] = found;
+                    bsel[1] = found_above;
+                }
+            }
+            __syncthreads();
+            const int bstar = bsel[0], above = bsel[1];
+            M next = 0;
+#pragma unroll
+            for (int t = 0; t < EPT; ++t) {
+                const int bb = (bk[t >> 2] >> (8 * (t & 3))) & 0xff;
+                const M on = (active >> t) & 1;
+                picked |= (on & (M)(bb > bstar)) << t;
+                next |= (on & (M)(bb == bstar)) << t;
+            }
+            active = next;
+            need -= above;
+            __syncthreads();  // bsel and hist are rewritten by the next pass
+        }
+        if (need > 0) {  // equal scores: the lowest kv indices first
+            for (int t = 0; t < EPT && need > 0; ++t) {
+                const bool on = (active >> t) & 1;
+                const uint64_t m = __ballot(on);
+                if (lane == 0) red_i[wave] = __builtin_popcountll(m);
+                __syncthreads();
+                int prior = 0;
+                for (int w = 0; w < wave; ++w) prior += red_i[w];
+                const int total = red_i[0] + red_i[1] + red_i[2] + red_i[3];
+                __syncthreads();
+                if (total <= need) {
+                    if (on) picked |= (M)1 << t;
+                    need -= total;
+                } else {
+                    if (on && prior + __builtin_popcountll(m & below) < need) picked |= (M)1 << t;
+                    need = 0;
+                }
+            }
+        }
+    }
+    const M keepm = must_kept | picked;
+
+    int8_t* krow = a.keep + r * a.NK;
+    const int32_t row_begin = a.row_ptr[r];
+    const int32_t row_len = a.row_ptr[r + 1] - row_begin;  // planned on the host from the same rule
+    int32_t* crow = a.col_idx + row_begin;
+    int pos = 0;
+#pragma unroll
+    for (int t = 0; t < EPT; ++t) {
+        const int j = 256 * t + 64 * wave + lane;
+        const bool kb = (keepm >> t) & 1;
+        if (j < a.NK) krow[j] = kb ? 1 : 0;
+        const uint64_t m = __ballot(kb);
+        if (lane == 0) red_i[wave] = __builtin_popcountll(m);
+        __syncthreads();
+        int prior = 0;
+        for (int w = 0; w < wave; ++w) prior += red_i[w];
+        const int total = red_i[0] + red_i[1] + red_i[2] + red_i[3];
+        __syncthreads();
+        const int slot = pos + prior + __builtin_popcountll(m & below);
+        if (kb && slot < row_len) crow[slot] = j;  // never write past the planned row
+        pos += total;
     }
 }
 
@@ -634,7 +870,7 @@ hipError_t launch_scores(const float* qh, const float* kh, int B, int Hsel, int 
     if (NKs <= 0) NKs = NK;
     if (NQ == 0 || NK == 0 || nh == 0 || B == 0) return hipSuccess;
     if (NQ <= 8) {
-        const dim3 g((unsigned)((int64_t)B * nh * ((NK + 255) / 256)));
+        const dim3 g((unsigned)((int64_t)B * nh * ((NK + 63) / 64)));
 #define NSA_ROWS(DD)                                                                                         \
     hipLaunchKernelGGL((score_rows_kernel<DD>), g, dim3(256), 0, stream, qh, kh, Hsel, Hk, group, h0, nh, NQ, NK, \
                        NKs, s)
@@ -675,6 +911,17 @@ hipError_t launch_scores(const float* qh, const float* kh, int B, int Hsel, int 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     const int64_t rows = (int64_t)a.B * a.nh * a.NQ;
     if (rows == 0 || a.NK == 0) return hipSuccess;
+    if (rows <= 1024 && a.NK <= 4096) {  // few rows: a workgroup per row
+        const int ept = (a.NK + 255) / 256;
+#define NSA_TOPK_ROWS(E) hipLaunchKernelGGL((topk_rows_kernel<E>), dim3((unsigned)rows), dim3(256), 0, stream, a)
+        if (ept <= 1) NSA_TOPK_ROWS(1);
+        else if (ept <= 2) NSA_TOPK_ROWS(2);
+        else if (ept <= 4) NSA_TOPK_ROWS(4);
+        else if (ept <= 8) NSA_TOPK_ROWS(8);
+        else NSA_TOPK_ROWS(16);
+#undef NSA_TOPK_ROWS
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)((rows + 3) / 4));
     const int epl = (a.NK + 63) / 64;
 #define NSA_TOPK(E) hipLaunchKernelGGL((topk_kernel<E>), grid, dim3(256), 0, stream, a)

@@ -173,15 +173,37 @@ def backward_timing(q, k, v, out, lse, sel, w: synth.Workload, fwd_flops: float,
             "kernels": "delta, kv-major index (3), bwd_dq_mfma_kernel<128,4>, bwd_dkdv_mfma_kernel<128>"}
 
 
-def _event_ms(fn, calls: int, stream) -> float:
-    """Mean duration of fn() in ms, HIP events around each call on `stream`."""
+def _event_ms(fn, calls: int, stream, queued: bool = False) -> float:
+    """Mean duration of fn() in ms, HIP events around each call on `stream`.
+
+    queued=True puts a GPU spin of a few ms on the stream before each batch of
+    8 calls, so the host enqueues the batch before the device reaches it: the
+    events then time the device work of a call (its kernels and the gaps
+    between them), not the host-side argument handling of a Python caller.
+    (Batches of 8: the library's pinned upload ring has 8 slots, and a ninth
+    queued upload would wait for the first.)"""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
-    for e in ev:
-        e[0].record(stream)
-        fn()
-        e[1].record(stream)
-    torch.cuda.synchronize()
+    batch = 8 if queued else calls
+    for b0 in range(0, calls, batch):
+        if queued:
+            torch.cuda._sleep(int(5e6))
+        for e in ev[b0:b0 + batch]:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def _host_us(fn, calls: int) -> float:
+    """Mean host (wall) time of one call in us, with the device idle at the start."""
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(calls):
+        fn()
+    host = (time.perf_counter() - t) / calls * 1e6
+    torch.cuda.synchronize()
+    return host
 
 
 def decode_timing(q, k, v, w: synth.Workload, calls: int = 20):
@@ -227,7 +249,9 @@ def decode_timing(q, k, v, w: synth.Workload, calls: int = 20):
     for fn in (upd, sel, att, dense):
         fn()
     torch.cuda.synchronize()
-    up_ms, sel_ms, att_ms, dense_ms = (_event_ms(fn, calls, stream) for fn in (upd, sel, att, dense))
+    up_ms, sel_ms, att_ms, dense_ms = (_event_ms(fn, calls, stream, queued=True) for fn in (upd, sel, att, dense))
+    host_us = {name: round(_host_us(fn, calls), 1) for name, fn in (("pool_update", upd), ("select", sel),
+                                                                    ("attn", att))}
     nnz = int(box["sel"].nnz)
     heads_per_row = w.Hq if w.head_shared else 1
     tile_bytes = 2 * w.block_kv * w.D * q.element_size()
@@ -241,7 +265,10 @@ def decode_timing(q, k, v, w: synth.Workload, calls: int = 20):
             "dense_attn_us": round(dense_ms * 1e3, 1), "dense_bytes": dense_bytes,
             "dense_GBps": round(dense_bytes / (dense_ms * 1e-3) / 1e9, 1),
             "dense_frac_hbm": round(dense_bytes / (dense_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "kernels": "pool_kernel (tile range), score_kernel, topk_kernel, attn_decode_kernel<128> + "
+            "timing": "device time per call (calls queued behind a GPU spin); host_us: wall time per "
+                      "call of the Python binding",
+            "host_us": host_us,
+            "kernels": "pool_kernel (tile range), score_rows_kernel, topk_rows_kernel, attn_decode_kernel<128> + "
                        "attn_combine_kernel"}
 
 

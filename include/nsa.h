@@ -179,8 +179,8 @@ int nsa_plan_sizes(const nsa_plan* plan, nsa_sizes* out, int32_t* row_ptr_host);
  * errors as nsa_select with the plan's spec, pins and drops. The first call
  * on a device allocates device memory for the plan's row_ptr and mask words
  * and copies them there synchronously (held until nsa_plan_destroy); later
- * calls on that device copy nothing from the host (row_ptr is copied device to
- * device on `stream`). Calls on another device upload per call, as
+ * calls on that device copy nothing (the selection kernels write out->row_ptr
+ * from the device copy). Calls on another device upload per call, as
  * nsa_select does. */
 int nsa_select_planned(const nsa_plan* plan, const nsa_tensor* q, const nsa_tensor* k,
                        nsa_selection* out, void* workspace, size_t workspace_bytes, void* stream);

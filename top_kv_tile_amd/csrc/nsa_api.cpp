@@ -208,7 +208,7 @@ int build_plan(const Geo& g, const nsa_spec* spec, const nsa_mask* pins, const n
 }
 
 struct WsLayout {
-    size_t pq = 0, pk = 0, mq = 0, mk = 0, scores = 0, pinw = 0, dropw = 0, total = 0;
+    size_t pq = 0, pk = 0, mq = 0, mk = 0, scores = 0, rowp = 0, pinw = 0, dropw = 0, total = 0;
     int chunk = 1;
 };
 
@@ -232,6 +232,9 @@ WsLayout ws_layout(const Geo& g, const nsa_spec* spec, bool has_pins, int pin_sl
     const int64_t per_head = std::max<int64_t>((int64_t)g.NQ * g.NK * 4, 1);
     w.chunk = (int)std::max<int64_t>(1, std::min<int64_t>(g.Hsel, spec->score_chunk_bytes / per_head));
     w.scores = take((size_t)g.B * w.chunk * g.NQ * g.NK * 4);
+    // Row offsets, then the mask words: uploaded together with one copy (the
+    // top-k kernels write the caller's row_ptr from here).
+    w.rowp = take((size_t)(g.rows + 1) * 4);
     if (has_pins) w.pinw = take((size_t)pin_slabs * g.NQ * g.NKW * 8);
     if (has_drops) w.dropw = take((size_t)drop_slabs * g.NQ * g.NKW * 8);
     w.total = off;
@@ -287,14 +290,28 @@ hipError_t upload(int n, void* const* dst, const void* const* src, const size_t*
         if ((e = hipHostMalloc(&s.host, cap, hipHostMallocDefault)) != hipSuccess) return e;
         s.cap = cap;
     }
-    size_t off = 0;
+    // Buffers are staged 256-byte aligned; consecutive ones whose device
+    // destinations lie at the same distances go up with one copy.
+    size_t off = 0, run_off = 0, run_end = 0;
+    char* run_dst = nullptr;
     for (int x = 0; x < n; ++x) {
         if (bytes[x] == 0) continue;
-        char* h = (char*)s.host + off;
-        std::memcpy(h, src[x], bytes[x]);
-        if ((e = hipMemcpyAsync(dst[x], h, bytes[x], hipMemcpyHostToDevice, stream)) != hipSuccess) return e;
+        std::memcpy((char*)s.host + off, src[x], bytes[x]);
+        if (run_dst && (char*)dst[x] == run_dst + (off - run_off)) {
+            run_end = off + bytes[x];
+        } else {
+            if (run_dst && (e = hipMemcpyAsync(run_dst, (char*)s.host + run_off, run_end - run_off,
+                                               hipMemcpyHostToDevice, stream)) != hipSuccess)
+                return e;
+            run_dst = (char*)dst[x];
+            run_off = off;
+            run_end = off + bytes[x];
+        }
         off += align256(bytes[x]);
     }
+    if (run_dst && (e = hipMemcpyAsync(run_dst, (char*)s.host + run_off, run_end - run_off, hipMemcpyHostToDevice,
+                                       stream)) != hipSuccess)
+        return e;
     if ((e = hipEventRecord(s.done, stream)) != hipSuccess) return e;
     s.pending = true;
     return hipSuccess;
@@ -347,7 +364,7 @@ void fill_sizes(const Plan& p, const nsa_spec* spec, nsa_sizes* out, int32_t* ro
 
 int score_and_topk(const Plan& p, const nsa_spec* spec, const float* qh, const float* kh, int Hk, int NKs,
                    const WsLayout& w, char* ws, nsa_selection* out, hipStream_t stream, const uint64_t* pin_words,
-                   const uint64_t* drop_words);
+                   const uint64_t* drop_words, const int32_t* row_src);
 
 // Enqueues the selection of a built plan (row_ptr present) for tensors q, k
 // whose geometry the plan was built from.
@@ -387,35 +404,40 @@ int run_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, c
     char* ws = (char*)workspace;
     const uint64_t* pin_words = p.has_pins ? (const uint64_t*)(ws + w.pinw) : nullptr;
     const uint64_t* drop_words = p.has_drops ? (const uint64_t*)(ws + w.dropw) : nullptr;
-    if (pd) {  // the plan is on the device already: only row_ptr is copied, device to device
-        const hipError_t e = hipMemcpyAsync(out->row_ptr, pd->row_ptr, p.row_ptr.size() * sizeof(int32_t),
-                                            hipMemcpyDeviceToDevice, stream);
-        if (e != hipSuccess) return hip_fail(e);
+    if (g.rows == 0 || g.NK == 0) {  // no top-k launch: the row offsets go straight to the caller
+        void* dst[1] = {out->row_ptr};
+        const void* src[1] = {p.row_ptr.data()};
+        size_t bytes[1] = {p.row_ptr.size() * sizeof(int32_t)};
+        const hipError_t e = upload(1, dst, src, bytes, stream);
+        return e == hipSuccess ? NSA_OK : hip_fail(e);
+    }
+    const int32_t* row_src = (const int32_t*)(ws + w.rowp);
+    if (pd) {  // the plan is on the device already: nothing is copied
+        row_src = pd->row_ptr;
         pin_words = pd->pin_words;
         drop_words = pd->drop_words;
-    } else {
-        void* dst[3] = {out->row_ptr, ws + w.pinw, ws + w.dropw};
+    } else {  // row offsets and mask words, one copy into the workspace
+        void* dst[3] = {ws + w.rowp, ws + w.pinw, ws + w.dropw};
         const void* src[3] = {p.row_ptr.data(), p.pin_words.data(), p.drop_words.data()};
         size_t bytes[3] = {p.row_ptr.size() * sizeof(int32_t), p.has_pins ? p.pin_words.size() * 8 : 0,
                            p.has_drops ? p.drop_words.size() * 8 : 0};
         hipError_t e = upload(3, dst, src, bytes, stream);
         if (e != hipSuccess) return hip_fail(e);
     }
-    if (g.rows == 0 || g.NK == 0) return NSA_OK;
 
     const float* qh;
     const float* kh;
     int Hk;
     int st;
     if ((st = run_pool(q, k, spec, g, w, ws, stream, &qh, &kh, &Hk)) != NSA_OK) return st;
-    return score_and_topk(p, spec, qh, kh, Hk, g.NK, w, ws, out, stream, pin_words, drop_words);
+    return score_and_topk(p, spec, qh, kh, Hk, g.NK, w, ws, out, stream, pin_words, drop_words, row_src);
 }
 
 // Scores chunk by chunk of selection heads, each followed by its top-k and CSR.
 // pin_words / drop_words: the plan's bit-packed masks on the device (or null).
 int score_and_topk(const Plan& p, const nsa_spec* spec, const float* qh, const float* kh, int Hk, int NKs,
                    const WsLayout& w, char* ws, nsa_selection* out, hipStream_t stream, const uint64_t* pin_words,
-                   const uint64_t* drop_words) {
+                   const uint64_t* drop_words, const int32_t* row_src) {
     const Geo& g = p.g;
     float* scores = (float*)(ws + w.scores);
     for (int h0 = 0; h0 < g.Hsel; h0 += w.chunk) {
@@ -442,6 +464,7 @@ int score_and_topk(const Plan& p, const nsa_spec* spec, const float* qh, const f
         ta.drop_words = drop_words;
         ta.db = p.db;
         ta.dh = p.dh;
+        ta.row_src = row_src;
         ta.row_ptr = out->row_ptr;
         ta.keep = out->keep;
         ta.col_idx = out->col_idx;
@@ -1295,15 +1318,21 @@ int nsa_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t l
         out->seq_kv = g.Skv;
         out->budget = spec->budget;
         char* ws = (char*)workspace;
-        {
-            void* dst[3] = {out->row_ptr, ws + w.pinw, ws + w.dropw};
+        if (g.rows == 0 || g.NK == 0) {  // no top-k launch: the row offsets go straight to the caller
+            void* dst[1] = {out->row_ptr};
+            const void* src[1] = {p.row_ptr.data()};
+            size_t bytes[1] = {p.row_ptr.size() * sizeof(int32_t)};
+            const hipError_t e = upload(1, dst, src, bytes, stream);
+            return e == hipSuccess ? NSA_OK : hip_fail(e);
+        }
+        {  // row offsets and mask words, one copy into the workspace
+            void* dst[3] = {ws + w.rowp, ws + w.pinw, ws + w.dropw};
             const void* src[3] = {p.row_ptr.data(), p.pin_words.data(), p.drop_words.data()};
             size_t bytes[3] = {p.row_ptr.size() * sizeof(int32_t), p.has_pins ? p.pin_words.size() * 8 : 0,
                                p.has_drops ? p.drop_words.size() * 8 : 0};
             const hipError_t e = upload(3, dst, src, bytes, stream);
             if (e != hipSuccess) return hip_fail(e);
         }
-        if (g.rows == 0 || g.NK == 0) return NSA_OK;
         // Pooled queries; the pooled keys are the caller's cache (capacity pooled_k->S tiles per head).
         float* pq = (float*)(ws + w.pq);
         hipError_t e = nsa::launch_pool(q->data, g.bf16, (int64_t)g.B * g.Hq, g.Sq, g.D, spec->block_q, pq, stream);
@@ -1324,7 +1353,8 @@ int nsa_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t l
         }
         return score_and_topk(p, spec, qh, kh, Hk, NKs, w, ws, out, stream,
                               p.has_pins ? (const uint64_t*)(ws + w.pinw) : nullptr,
-                              p.has_drops ? (const uint64_t*)(ws + w.dropw) : nullptr);
+                              p.has_drops ? (const uint64_t*)(ws + w.dropw) : nullptr,
+                              (const int32_t*)(ws + w.rowp));
     } catch (...) {
         return NSA_ERR_UNSUPPORTED;
     }

@@ -603,8 +603,13 @@ __global__ __launch_bounds__(256, (EPL <= 32 ? 4 : 1)) void topk_kernel(TopkArgs
     const M keepm = must_kept | picked;
 
     int8_t* krow = a.keep + r * a.NK;
-    const int32_t row_begin = a.row_ptr[r];
-    const int32_t row_len = a.row_ptr[r + 1] - row_begin;  // planned on the host from the same rule
+    const int32_t row_begin = a.row_src[r];
+    const int32_t row_end = a.row_src[r + 1];
+    const int32_t row_len = row_end - row_begin;  // planned on the host from the same rule
+    if (lane == 0) {  // the caller's row offsets (the last row also writes the end)
+        a.row_ptr[r] = row_begin;
+        if (r + 1 == (int64_t)a.B * a.Hsel * a.NQ) a.row_ptr[r + 1] = row_end;
+    }
     int32_t* crow = a.col_idx + row_begin;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int pos = 0;
@@ -801,8 +806,13 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(TopkArgs a) {
     const M keepm = must_kept | picked;
 
     int8_t* krow = a.keep + r * a.NK;
-    const int32_t row_begin = a.row_ptr[r];
-    const int32_t row_len = a.row_ptr[r + 1] - row_begin;  // planned on the host from the same rule
+    const int32_t row_begin = a.row_src[r];
+    const int32_t row_end = a.row_src[r + 1];
+    const int32_t row_len = row_end - row_begin;  // planned on the host from the same rule
+    if (tid == 0) {  // the caller's row offsets (the last row also writes the end)
+        a.row_ptr[r] = row_begin;
+        if (r + 1 == (int64_t)a.B * a.Hsel * a.NQ) a.row_ptr[r + 1] = row_end;
+    }
     int32_t* crow = a.col_idx + row_begin;
     int pos = 0;
 #pragma unroll

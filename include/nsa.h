@@ -197,7 +197,9 @@ void nsa_plan_destroy(nsa_plan* plan);
  * byte builds its own plan (the page's key leaves the masks out). Entries are
  * host memory only (the plan is uploaded per call on the caller's stream, as
  * without the cache); the least recently used entry is replaced when the
- * cache is full. Thread-safe. */
+ * cache is full. Each entry keeps a copy of its masks, so requests whose pins
+ * and drops hold more than 64 MiB together are built per call and not cached.
+ * Thread-safe. */
 
 /* Host only. Keeps at most `capacity` plans (default 8; 0 disables caching).
  * Lowering it drops the least recently used entries. BAD_SPEC if capacity < 0. */

@@ -175,3 +175,17 @@ def test_concurrent_callers():
     assert not errors
     hits, misses, entries = tkt.nsa_plan_cache_stats()
     assert hits + misses == 8 * 40 and entries == 3 and misses >= 3
+
+
+def test_large_masks_are_not_cached():
+    """Each entry copies its masks: past 64 MiB of mask bytes a request is built
+    per call (still correct) and not kept."""
+    B2, Hq2, Hkv2, S2, bq2, bkv2 = 1, 72, 8, 65536, 128, 32
+    nq2, nk2 = S2 // bq2, S2 // bkv2
+    spec = tkt.SparseSpec(budget=0.1, block_q=bq2, block_kv=bkv2)
+    drops = np.zeros((1, Hq2, nq2, nk2), np.int8)  # 72 MiB
+    drops[:, :, :, 7] = 1
+    for _ in range(2):
+        out, r = _sizes(_t(B2, Hq2, S2), _t(B2, Hkv2, S2), spec, None, drops)
+    assert tkt.nsa_plan_cache_stats() == (0, 2, 0)
+    assert np.array_equal(r, _oracle_row_ptr(B2, Hq2, nq2, nk2, spec, None, drops))

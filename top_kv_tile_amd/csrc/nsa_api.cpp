@@ -829,6 +829,9 @@ struct PlanCacheEntry {
     std::shared_ptr<const Plan> plan;
     uint64_t stamp = 0;
 };
+// Requests whose masks hold more bytes than this are built per call and not
+// cached (each entry keeps a copy of its masks).
+constexpr size_t kMaxCachedMaskBytes = (size_t)64 << 20;
 struct PlanCache {
     std::mutex mu;
     std::vector<PlanCacheEntry> entries;
@@ -906,6 +909,7 @@ int cached_plan(const Geo& g, const nsa_tensor* q, const nsa_tensor* k, const ns
         std::lock_guard<std::mutex> lock(c.mu);
         cap = c.capacity;
     }
+    if (mask_bytes(pins) + mask_bytes(drops) > kMaxCachedMaskBytes) cap = 0;
     const uint64_t ph = cap ? mask_hash(pins) : 0, dh = cap ? mask_hash(drops) : 0;
     auto find = [&]() -> PlanCacheEntry* {  // caller holds c.mu
         for (PlanCacheEntry& e : c.entries) {

@@ -129,9 +129,15 @@ def cpu_baseline(inp, w: synth.Workload, budget_s: float = 20.0):
     per_row_s = t_sel / sel_rows + t_att / n_rows
     per_row_flops = fl / n_rows
     value = per_row_flops / per_row_s / 1e12
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "host_cpus": os.cpu_count(),
+        "host_cpus": os.cpu_count(), "cpu_model": cpu_model,
         "sample": (f"oracle.select_blocks on one GQA group ({G} query heads x {w.nq} query tiles, "
                    f"{t_sel:.1f} s) + oracle.attention (fp64) on {n_rows} seeded (head, query-tile) rows "
                    f"({t_att:.1f} s); per-row select + attention time, kept-tile FLOPs of the sampled rows"),
@@ -193,6 +199,31 @@ def _event_ms(fn, calls: int, stream, queued: bool = False) -> float:
             e[1].record(stream)
         torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def measured_peaks(reps: int = 10) -> dict:
+    """Rates this box reaches on two plain references, timed with events:
+    a contiguous 8192^3 bf16 GEMM through torch (the vendor GEMM library) and
+    a 2 GiB device-to-device copy (2 GiB read + 2 GiB written per call)."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(0)
+    n = 8192
+    a = torch.randn(n, n, generator=g, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, generator=g, device=dev).to(torch.bfloat16)
+    c = torch.empty(n, n, dtype=torch.bfloat16, device=dev)
+    x = torch.empty(1 << 29, dtype=torch.float32, device=dev)  # 2 GiB
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        torch.matmul(a, b, out=c)
+        y.copy_(x)
+    gemm_ms = _event_ms(lambda: torch.matmul(a, b, out=c), reps, stream)
+    copy_ms = _event_ms(lambda: y.copy_(x), reps, stream)
+    del a, b, c, x, y
+    return {"bf16_gemm_TFLOPs": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+            "copy_GBps": round(2 * (1 << 31) / (copy_ms * 1e-3) / 1e9, 1),
+            "how": "8192^3 bf16 torch.matmul and a 2 GiB tensor copy on the same GPU, events, "
+                   f"mean of {reps} calls"}
 
 
 def _host_us(fn, calls: int) -> float:
@@ -310,6 +341,8 @@ def main():
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--no-decode", action="store_true", help="skip the decoding-step timing")
     ap.add_argument("--no-reorder", action="store_true", help="skip the token-reordering timing")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured reference rates (a large bf16 GEMM and a device copy)")
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel 3 times "
@@ -377,6 +410,9 @@ def main():
     ms_step = wall * 1e3 / args.steps
     sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    pct = lambda xs: {f"p{p}": round(float(np.percentile(xs, p)), 4) for p in (10, 50, 90)}  # noqa: E731
+    step_pct = pct([e[0].elapsed_time(e[2]) for e in events])
+    attn_pct = pct([e[1].elapsed_time(e[2]) for e in events])
 
     value = full_flops / (ms_step * 1e-3) / 1e12
     kv_bytes = float(tiles * 2 * w.block_kv * w.D * 2 + 2 * q.numel() * q.element_size())
@@ -411,16 +447,20 @@ def main():
                      "avg_launch_ms": round(attn_ms, 4),
                      # K/V supply: every kept, live tile visit reads one 64-key K tile and
                      # one V tile (32 KiB at D = 128) unless L2 still holds it; plus Q read
-                     # and O written once. On this workload the visits are scattered and
-                     # this stream, not the matrix cores, bounds the kernel.
+                     # and O written once.
                      "kv_visit_bytes_per_launch": kv_bytes,
                      "kv_visit_GBps": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1),
                      "kv_visit_frac_hbm": round(kv_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "stages": {"select_ms": round(sel_ms, 4), "select_GBps": round(select_gbs, 1),
                    "select_frac_hbm": round(select_gbs / PEAK_HBM_GBS, 4),
                    "select_algorithmic_bytes": select_bytes, "attn_ms": round(attn_ms, 4),
-                   "attn_TFLOPs": round(attn_tflops, 2)},
+                   "attn_TFLOPs": round(attn_tflops, 2),
+                   "step_ms_events": step_pct, "attn_ms_events": attn_pct},
     }
+    if not args.no_peaks:
+        peaks = measured_peaks()
+        res["measured_peaks"] = peaks
+        res["roofline"]["frac_of_measured_gemm"] = round(attn_tflops / peaks["bf16_gemm_TFLOPs"], 4)
     if not args.no_backward:
         res["backward"] = backward_timing(q, k, v, out, lse, sel, w, full_flops, args.backward_steps)
     if not args.no_decode:

@@ -42,7 +42,7 @@ enum nsa_status {
     NSA_ERR_NULL_ARG = -1,        /* a required pointer is NULL */
     NSA_ERR_BAD_SHAPE = -2,       /* inconsistent sizes, Hq % Hkv != 0, mask not broadcastable */
     NSA_ERR_BAD_DTYPE = -3,       /* dtype not F32/BF16, or q/k/v/out dtypes differ */
-    NSA_ERR_UNSUPPORTED = -4,     /* valid request this build does not run (see each call) */
+    NSA_ERR_UNSUPPORTED = -4,     /* valid request this library does not run (see each call) */
     NSA_ERR_WORKSPACE = -5,       /* workspace missing or smaller than nsa_sizes.workspace_bytes */
     NSA_ERR_BAD_SPEC = -6,        /* block size <= 0, budget < 0 or NaN, chunk bytes < 0 */
     NSA_ERR_HIP = -7,             /* a HIP runtime call failed: see nsa_last_hip_error() */

@@ -5,7 +5,7 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 No page prints the attention consumer; what it computes is the plain reading of
 the selection page ("automatic/modules/attention/sparse/selector.py",
 ``BlockSelection``: the keep flags are the geometry every consumer reads) plus
-the usual attention conventions, each a reading listed in the design doc:
+the usual attention conventions, each a reading where the page shows no attention call:
 
 * query head h reads kv head g = h // (Hq / Hkv) and selection head h' = h, or
   0 when the selection is shared by all heads;

@@ -20,7 +20,7 @@ Everything here follows the page "automatic/modules/attention/sparse/selector.py
                           ``k_r`` candidates in (score descending, kv index
                           ascending) order, joined with must, minus forbidden.
 
-Readings where the page is silent (each listed in the design doc):
+Readings where the page is silent (the plainest reading the rest of the page supports):
 * The per-row budget multiplies an integer count by a Python float, which
   torch promotes to float32: k_r = ceil(fl32(fl32(c_r) * fl32(budget))).
 * Drops win over must (the forbidden set is removed last).

@@ -978,7 +978,7 @@ const char* nsa_status_string(int status) {
         case NSA_ERR_NULL_ARG: return "a required pointer is NULL";
         case NSA_ERR_BAD_SHAPE: return "inconsistent shapes (or Hq % Hkv != 0, or a mask that does not broadcast)";
         case NSA_ERR_BAD_DTYPE: return "unsupported or mismatched dtype";
-        case NSA_ERR_UNSUPPORTED: return "valid request not supported by this build";
+        case NSA_ERR_UNSUPPORTED: return "valid request this library does not run";
         case NSA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case NSA_ERR_BAD_SPEC: return "invalid spec (block size <= 0, budget < 0 or NaN, chunk bytes < 0)";
         case NSA_ERR_HIP: return "HIP runtime error (see nsa_last_hip_error)";

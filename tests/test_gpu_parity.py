@@ -186,7 +186,7 @@ def test_few_long_rows():
     say(f"  {rep}")
 
 
-@pytest.mark.parametrize("S,bq,bkv", [(16384, 256, 16), (8192, 128, 32)])
+@pytest.mark.parametrize("S,bq,bkv", [(16384, 256, 16), (8192, 128, 32), (8192, 256, 16)])
 def test_exact_ties_take_lowest_index(S, bq, bkv):
     """Every kv tile repeats one of three key vectors, so pooled keys are exact
     copies and a row's scores fall into three groups of exactly equal values,

@@ -8,6 +8,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -16,21 +17,25 @@ LIB = os.path.join(HERE, "libnsa.so")
 SOURCES = ["nsa_api.cpp", "select_kernels.hip", "attn_kernels.hip", "attn_bwd_kernels.hip", "reorder_kernels.hip"]
 
 # Packed fp32 instructions are kept out of the device code: hipcc -O3 would
-# otherwise form them from plain float code. Matrix-core accumulators are
-# allocated as ordinary VGPRs (gfx950 MFMAs take them there): with the default
-# AGPR form the register allocator shuttled live dK/dV accumulators between
-# AGPRs and VGPRs on every iteration of the gradient kernel.
+# otherwise form them from plain float code.
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-ffp-contract=fast",
     "-Wno-unused-command-line-argument",
 ]
+# Matrix-core accumulators: the selection kernels are compiled with them in
+# ordinary VGPRs (-amdgpu-mfma-vgpr-form). The gradient kernels keep the
+# default AGPR form: their dK/dV kernel holds S and dP of the next 64-query
+# chunk in AGPRs while it works on the current one, and in VGPR form the
+# register allocator moved the K and V fragments out to AGPRs and back in
+# front of every product instead. The forward and reordering kernels compile
+# to the same code either way.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+PER_SOURCE = {"attn_bwd_kernels.hip": []}
 
 
 def hipcc() -> str:
@@ -40,21 +45,41 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libnsa.so)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into top_kv_tile_amd/libnsa.so; returns the path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *srcs]
+# hipcc's host pass does not know the packed-fp32 feature and says so; that is expected.
+_NOISE = "'-packed-fp32-ops' is not a recognized feature for this target"
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass does not know the packed-fp32 feature and says so; that is expected.
-    noise = "'-packed-fp32-ops' is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+
+
+def _finish(proc, what, verbose):
+    _, stderr = proc.communicate()
+    err = "\n".join(l for l in stderr.splitlines() if _NOISE not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {what} ({proc.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (in parallel) and link top_kv_tile_amd/libnsa.so; returns the path."""
+    include = ["-I", os.path.join(ROOT, "include")]
+    with tempfile.TemporaryDirectory(prefix="_build_", dir=HERE) as tmpdir:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src + ".o")
+            flags = PER_SOURCE.get(src, VGPR_FORM)
+            procs.append((src, _run([hipcc(), *FLAGS, *flags, *include, "-c", "-o", obj,
+                                     os.path.join(CSRC, src)], verbose)))
+            objs.append(obj)
+        for src, proc in procs:
+            _finish(proc, src, verbose)
+        tmp = LIB + ".tmp"
+        _finish(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose),
+                "the link", verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -582,11 +582,11 @@ struct Unit {
 template <int D>
 struct DkdvLds {
     static constexpr int TILEB = 64 * D * 2;
-    static constexpr int NST = 4;  // stages (at most 5: the waits below count up to 3 units in flight)
-    static constexpr int SIDE = 4 * 2 * 64 * 4;        // per stage: 4 waves x (LSE, Delta) x 64 floats
-    static constexpr int BYTES = NST * 2 * TILEB + NST * SIDE;
-    static_assert(NST >= 3 && NST <= 5, "pipeline depth");
-    static_assert(2 * 2 * (D / 32) * 16 * 64 * 4 <= NST * 2 * TILEB, "reduction buffer fits the stages");
+    static constexpr int NST = 4;  // stages: the unit in work, the next one, two in flight
+    static constexpr int SIDE = 4 * 2 * 64 * 4;       // per stage: 4 waves x (LSE, Delta) x 64 floats
+    static constexpr int STAGEB = 2 * TILEB + SIDE;  // a stage: Q chunk, dO chunk, side values
+    static constexpr int BYTES = NST * STAGEB;
+    static_assert(2 * 2 * (D / 32) * 16 * 64 * 4 <= BYTES, "reduction buffer fits the stages");
 };
 
 template <int D>
@@ -598,13 +598,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
     using L = DkdvLds<D>;
     constexpr int PER_UNIT = 2 * (G::NINSTR / NW) + 2;  // vector memory instructions per wave per unit
     extern __shared__ __attribute__((aligned(1024))) char lds[];
-    auto qst = [&](int st) -> char* { return lds + st * G::TILEB; };
-    auto dost = [&](int st) -> char* { return lds + (L::NST + st) * G::TILEB; };
-    auto side = [&](int st, int w, int which) -> float* {
-        return (float*)(lds + 2 * L::NST * G::TILEB + st * L::SIDE) + (w * 2 + which) * 64;
-    };
     const uint32_t lds0 = lds_address(lds);
-    auto lds_off = [&](const void* p) -> uint32_t { return lds0 + (uint32_t)((const char*)p - lds); };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -668,20 +662,43 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
         return u;
     };
 
-    // Loads of unit u into stage st: Q and dO chunks (rows clamped to S - 1),
-    // and for this wave's 32 queries the raw LSE and Delta (zeros past S).
-    // Every lane of every wave takes part, so each wave issues PER_UNIT loads.
+    // Loads of unit u into stage st: Q and dO chunks and, for this wave's 32
+    // queries, the raw LSE and Delta. Per-lane offsets inside a chunk are the
+    // same for every unit (bswz layout); a chunk is selected by the base of
+    // its buffer resource, whose record count ends at query S - 1, so rows
+    // past it read as zeros (those queries are masked: P = 0, dS = 0). Every
+    // lane of every wave takes part, so each wave issues PER_UNIT loads.
+    static_assert(G::NINSTR % NW == 0, "every wave issues the same number of DMA instructions");
+    constexpr int IPW = G::NINSTR / NW;
+    int tvo[IPW];
+#pragma unroll
+    for (int x = 0; x < IPW; ++x) {
+        const int ii = wave + NW * x;
+        const int row = ii * G::RPI + lane / G::CH, pc = lane % G::CH;
+        tvo[x] = row * G::ROWB + (pc ^ G::bswz(row)) * 16;
+    }
+    // Query rows are counted from the first row of the group's first head.
+    const int64_t grow0 = ((int64_t)b * a.Hq + g * GRP) * a.S;
+    const char* qgrp = (const char*)a.q + grow0 * G::ROWB;
+    const char* dgrp = (const char*)a.dout + grow0 * G::ROWB;
+    const float* lgrp = a.lse + grow0;
+    const float* egrp = a.delta + grow0;
     auto issue = [&](const Unit& u, int st) {
-        const int h = g * GRP + u.hh;
-        const int64_t qhead = ((int64_t)b * a.Hq + h) * a.S;
         const int row0 = u.i * bq + 64 * u.c;
-        dma_tile_asm<D, NW>(rsrc_words((const uint16_t*)a.q + qhead * D, head_bytes), lds_off(qst(st)), row0, a.S,
-                            wave, lane);
-        dma_tile_asm<D, NW>(rsrc_words((const uint16_t*)a.dout + qhead * D, head_bytes), lds_off(dost(st)), row0,
-                            a.S, wave, lane);
-        const int toff = (row0 + 32 * qs + lane) * 4;  // lanes 32..63 fetch values no one reads
-        dma4(rsrc_words(a.lse + qhead, a.S * 4), lds_off(side(st, wave, 0)), toff);
-        dma4(rsrc_words(a.delta + qhead, a.S * 4), lds_off(side(st, wave, 1)), toff);
+        const int64_t trow = (int64_t)u.hh * a.S + row0;
+        const uint32_t tbytes = (uint32_t)(a.S - row0) * G::ROWB;
+        const u32x4 rq = rsrc_words(qgrp + trow * G::ROWB, tbytes);
+        const u32x4 rd = rsrc_words(dgrp + trow * G::ROWB, tbytes);
+        const uint32_t lq = lds0 + st * L::STAGEB;
+#pragma unroll
+        for (int x = 0; x < IPW; ++x) dma16(rq, lq + (wave + NW * x) * 1024, tvo[x]);
+#pragma unroll
+        for (int x = 0; x < IPW; ++x) dma16(rd, lq + G::TILEB + (wave + NW * x) * 1024, tvo[x]);
+        const int srow = 32 * qs;  // lanes 32..63 fetch values no one reads
+        const uint32_t sbytes = (uint32_t)max(a.S - row0 - srow, 0) * 4;
+        const uint32_t ls = lq + 2 * G::TILEB + wave * 512;
+        dma4(rsrc_words(lgrp + trow + srow, sbytes), ls, lane * 4);
+        dma4(rsrc_words(egrp + trow + srow, sbytes), ls + 256, lane * 4);
     };
 
     f32x16 dk[DBLK], dv[DBLK];
@@ -691,11 +708,44 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
         dv[m] = (f32x16){};
     }
 
-    // Pipeline: unit `cur` in stage st, the next units nx[0], nx[1], ... in
-    // the following stages (valid while hv[]). NST - 2 of them are in flight
-    // when an iteration starts, and it issues one more into the stage the
-    // previous unit used.
+    // Per-lane LDS offsets within a stage, the same for every unit: row
+    // fragments of this wave's queries (chunk 2 ks + hf of row qr), and the
+    // two halves of the transposed fragments (rows 32 qs + 4 hf + (0..3) and
+    // + 8, column block m; the second k-step is 16 rows further on).
+    const int qr = 32 * qs + l32;
+    int roff[KSTEPS], tlo[DBLK], thi[DBLK];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) roff[ks] = qr * G::ROWB + ((2 * ks + hf) ^ G::bswz(qr)) * 16;
+    {
+        const int vg = lane >> 4, vs = lane & 15;
+        const int r0 = 32 * qs + 4 * hf + (vs >> 2), r1 = r0 + 8;
+#pragma unroll
+        for (int m = 0; m < DBLK; ++m) {
+            const int d = 32 * m + 16 * (vg & 1) + 4 * (vs & 3);
+            const int c = d >> 3, bo = (d & 7) * 2;
+            tlo[m] = r0 * G::ROWB + (c ^ G::bswz(r0)) * 16 + bo;
+            thi[m] = r1 * G::ROWB + (c ^ G::bswz(r1)) * 16 + bo;
+        }
+    }
+    const int soff = 2 * G::TILEB + wave * 512 + 16 * hf;  // this wave's LSE (Delta 256 bytes on)
+    auto rowf = [&](const char* p, int ks) -> bf16x8 {
+        return __builtin_bit_cast(bf16x8, *(const u32x4*)(p + roff[ks]));
+    };
+    auto trf = [&](const char* p, int m, int s3) -> bf16x8 {
+        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p + tlo[m] + s3 * 16 * G::ROWB));
+        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p + thi[m] + s3 * 16 * G::ROWB));
+        const short8_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, w);
+    };
+    // Software pipeline over units, one unit deep: an iteration finishes unit
+    // `cur` (its P / dS and the dV / dK products) while it computes S and dP of
+    // the next unit, so the vector arithmetic of one unit runs beside the
+    // matrix products of the next. Unit cur sits in stage st, the next units
+    // nx[0], nx[1], ... in the following stages (valid while hv[]). When an
+    // iteration starts, cur and nx[0] are resident and nx[1] is in flight; it
+    // issues one more unit into the stage of the unit before cur.
     constexpr int NST = L::NST;
+    static_assert(NST == 4, "the waits below assume four stages");
     Unit cur;
     cur.hh = -1;
     cur.e = cur.e_end = 0;
@@ -725,48 +775,60 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
             }
         }
     }
+    // S = Q K^T and dP = dO V^T of the first unit (stage 0), for this wave's 32 queries x 32 keys.
+    f32x16 s = (f32x16){}, dp = (f32x16){};
+    if (have) {
+        // unit cur has landed once at most the units issued after it are outstanding
+        if (hv[1]) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER_UNIT));
+        else if (hv[0]) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_UNIT));
+        else __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        bare_barrier();
+        bf16x8 qa[KSTEPS], da[KSTEPS];
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            qa[ks] = rowf(lds, ks);
+            da[ks] = rowf(lds + G::TILEB, ks);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            s = mfma(qa[ks], kf[ks], s);
+            dp = mfma(da[ks], vf[ks], dp);
+        }
+    }
     int st = 0;
     while (have) {
-        // Unit `cur` (stage st) has landed once at most the loads of the units
-        // issued after it are outstanding (PER_UNIT per unit, in issue order).
-        int pending = 0;
-#pragma unroll
-        for (int x = 0; x < NST - 2; ++x) pending += hv[x] ? 1 : 0;
-        if (pending == 0) __builtin_amdgcn_s_waitcnt(kVmcnt0);
-        else if (pending == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_UNIT));
-        else if (pending == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER_UNIT));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * PER_UNIT));
-        bare_barrier();  // all waves: unit cur visible, and the previous unit's stage no longer read
-        if (hv[NST - 3]) {
+        // Unit nx[0] (if any) has landed once at most the unit issued after it
+        // is outstanding; the barrier also ends every wave's reads of the stage
+        // of the unit before cur.
+        if (hv[1]) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_UNIT));
+        else __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        bare_barrier();
+        if (hv[1]) {
             bool ok = false;
-            const Unit u = advance(nx[NST - 3], ok);
+            const Unit u = advance(nx[1], ok);
             if (ok) {
-                nx[NST - 2] = u;
-                hv[NST - 2] = true;
-                issue(u, (st + NST - 1) % NST);
+                nx[2] = u;
+                hv[2] = true;
+                issue(u, (st + 3) & 3);
             }
         }
-        const char* qt = qst(st);
-        const char* dt = dost(st);
-        // S = Q K^T and dP = dO V^T for this wave's 32 queries x 32 keys.
-        f32x16 s = (f32x16){}, dp = (f32x16){};
-        const int qr = 32 * qs + l32;
-        {
-            // All sixteen row fragments are read before the first product: the
-            // scheduling fence keeps the compiler from placing each read right
-            // before its product, which exposed the LDS latency sixteen times.
-            bf16x8 qa[KSTEPS], da[KSTEPS];
+        const int st1 = (st + 1) & 3;
+        const char* sp = lds + st * L::STAGEB;
+        const char* sp1 = lds + st1 * L::STAGEB;
+        // Side values of unit cur, then the row fragments of the next unit (stale
+        // but harmless when there is none: its products are then discarded).
+        f32x4 lo[4], de[4];
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                qa[ks] = row_frag<D, true>(qt, qr, 2 * ks + hf);
-                da[ks] = row_frag<D, true>(dt, qr, 2 * ks + hf);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < 4; ++q) {
+            lo[q] = *(const f32x4*)(sp + soff + 32 * q);
+            de[q] = *(const f32x4*)(sp + soff + 256 + 32 * q);
+        }
+        bf16x8 qa[KSTEPS], da[KSTEPS];
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                s = mfma(qa[ks], kf[ks], s);
-                dp = mfma(da[ks], vf[ks], dp);
-            }
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            qa[ks] = rowf(sp1, ks);
+            da[ks] = rowf(sp1 + G::TILEB, ks);
         }
         // Lane holds key mykey (column) and queries 32 qs + 8 q + 4 hf + e (chunk rows) at [4 q + e].
         // Element masks only where this wave's block is partial: under causal
@@ -777,48 +839,59 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
         const int t_lim = min(a.S, cur.i * bq + bq);  // queries of this unit are below t_lim
         const bool need_mask = (a.causal && key0 + 32 * kb + 31 > tq0) || (tq0 + 31 >= t_lim);
         const int key_lim = a.causal ? mykey : -1;
-        const float* lsp = side(st, wave, 0) + 4 * hf;
-        const float* dlp = side(st, wave, 1) + 4 * hf;
         bf16x8 pf[2], dsf[2];
-        auto p_ds = [&](auto masked) {
+        f32x16 s2 = (f32x16){}, dp2 = (f32x16){};
+        auto step = [&](auto masked) {
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 lo = *(const f32x4*)(lsp + 8 * q);
-                const f32x4 de = *(const f32x4*)(dlp + 8 * q);
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int x = 4 * q + e;
-                    float p = fast_exp2(__builtin_fmaf(s[x], a.scale_log2, -kLog2e * lo[e]));
+                    float p = fast_exp2(__builtin_fmaf(s[x], a.scale_log2, -kLog2e * lo[q][e]));
                     if (decltype(masked)::value) {
                         const int t = tq0 + 8 * q + 4 * hf + e;
                         p = (t < t_lim && key_lim <= t) ? p : 0.f;
                     }
-                    const float ds = p * (dp[x] - de[e]);
+                    const float ds = p * (dp[x] - de[q][e]);
                     pf[x >> 3][x & 7] = (__bf16)p;
                     dsf[x >> 3][x & 7] = (__bf16)ds;
                 }
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                s2 = mfma(qa[ks], kf[ks], s2);
+                dp2 = mfma(da[ks], vf[ks], dp2);
             }
+            // One product, then a share of the vector work, sixteen times over.
+#pragma unroll
+            for (int x = 0; x < 2 * KSTEPS; ++x) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, decltype(masked)::value ? 10 : 7, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         };
         // Two copies, so that full blocks (the common case) carry no mask arithmetic.
-        if (need_mask) p_ds(std::true_type{});
-        else p_ds(std::false_type{});
+        if (need_mask) step(std::true_type{});
+        else step(std::false_type{});
         // dV^T += dO^T P and dK^T += Q^T dS; contraction over this wave's queries,
         // k-step s covering rows 32 qs + 16 s + 4 hf + (0..3) and + 8.
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            bf16x8 ta[DBLK], tb[DBLK];  // read ahead of the products, as above
+        for (int s3 = 0; s3 < 2; ++s3) {
+            bf16x8 ta[DBLK], tb[DBLK];  // read ahead of the products
 #pragma unroll
             for (int m = 0; m < DBLK; ++m) {
-                ta[m] = tr_frag<D>(dt, 32 * qs + 16 * s2, m, lane);
-                tb[m] = tr_frag<D>(qt, 32 * qs + 16 * s2, m, lane);
+                ta[m] = trf(sp + G::TILEB, m, s3);
+                tb[m] = trf(sp, m, s3);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int m = 0; m < DBLK; ++m) {
-                dv[m] = mfma(ta[m], pf[s2], dv[m]);
-                dk[m] = mfma(tb[m], dsf[s2], dk[m]);
+                dv[m] = mfma(ta[m], pf[s3], dv[m]);
+                dk[m] = mfma(tb[m], dsf[s3], dk[m]);
             }
         }
+        s = s2;
+        dp = dp2;
         cur = nx[0];
         have = hv[0];
 #pragma unroll
@@ -827,7 +900,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
             hv[x] = hv[x + 1];
         }
         hv[NST - 2] = false;
-        st = (st == NST - 1) ? 0 : st + 1;
+        st = st1;
     }
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();  // every wave is done with the stages (nothing is in flight any more)

@@ -364,7 +364,7 @@ void fill_sizes(const Plan& p, const nsa_spec* spec, nsa_sizes* out, int32_t* ro
 
 int score_and_topk(const Plan& p, const nsa_spec* spec, const float* qh, const float* kh, int Hk, int NKs,
                    const WsLayout& w, char* ws, nsa_selection* out, hipStream_t stream, const uint64_t* pin_words,
-                   const uint64_t* drop_words, const int32_t* row_src);
+                   const uint64_t* drop_words, const int32_t* row_src, int32_t row_step = 0);
 
 // Enqueues the selection of a built plan (row_ptr present) for tensors q, k
 // whose geometry the plan was built from.
@@ -437,7 +437,7 @@ int run_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, c
 // pin_words / drop_words: the plan's bit-packed masks on the device (or null).
 int score_and_topk(const Plan& p, const nsa_spec* spec, const float* qh, const float* kh, int Hk, int NKs,
                    const WsLayout& w, char* ws, nsa_selection* out, hipStream_t stream, const uint64_t* pin_words,
-                   const uint64_t* drop_words, const int32_t* row_src) {
+                   const uint64_t* drop_words, const int32_t* row_src, int32_t row_step) {
     const Geo& g = p.g;
     float* scores = (float*)(ws + w.scores);
     for (int h0 = 0; h0 < g.Hsel; h0 += w.chunk) {
@@ -465,6 +465,7 @@ int score_and_topk(const Plan& p, const nsa_spec* spec, const float* qh, const f
         ta.db = p.db;
         ta.dh = p.dh;
         ta.row_src = row_src;
+        ta.row_step = row_step;
         ta.row_ptr = out->row_ptr;
         ta.keep = out->keep;
         ta.col_idx = out->col_idx;
@@ -1329,7 +1330,13 @@ int nsa_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t l
             const hipError_t e = upload(1, dst, src, bytes, stream);
             return e == hipSuccess ? NSA_OK : hip_fail(e);
         }
-        {  // row offsets and mask words, one copy into the workspace
+        // Without masks every row sees the same keys and keeps the same number
+        // of tiles: the top-k kernel then computes the row offsets itself and
+        // nothing is copied to the device.
+        const int32_t step = p.row_ptr[1] - p.row_ptr[0];
+        bool uniform = !p.has_pins && !p.has_drops;
+        for (size_t r = 1; uniform && r < p.row_ptr.size(); ++r) uniform = p.row_ptr[r] == (int64_t)r * step;
+        if (!uniform) {  // row offsets and mask words, one copy into the workspace
             void* dst[3] = {ws + w.rowp, ws + w.pinw, ws + w.dropw};
             const void* src[3] = {p.row_ptr.data(), p.pin_words.data(), p.drop_words.data()};
             size_t bytes[3] = {p.row_ptr.size() * sizeof(int32_t), p.has_pins ? p.pin_words.size() * 8 : 0,
@@ -1358,7 +1365,7 @@ int nsa_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t l
         return score_and_topk(p, spec, qh, kh, Hk, NKs, w, ws, out, stream,
                               p.has_pins ? (const uint64_t*)(ws + w.pinw) : nullptr,
                               p.has_drops ? (const uint64_t*)(ws + w.dropw) : nullptr,
-                              (const int32_t*)(ws + w.rowp));
+                              uniform ? nullptr : (const int32_t*)(ws + w.rowp), uniform ? step : 0);
     } catch (...) {
         return NSA_ERR_UNSUPPORTED;
     }

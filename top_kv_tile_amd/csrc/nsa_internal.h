@@ -40,7 +40,8 @@ struct TopkArgs {
     int pb, ph;
     const uint64_t* drop_words;
     int db, dh;
-    const int32_t* row_src;    // (B*Hsel*NQ + 1) row offsets (planned on the host), read
+    const int32_t* row_src;    // (B*Hsel*NQ + 1) row offsets (planned on the host), read; or null:
+    int32_t row_step;          //   then row r starts at r * row_step (every row keeps row_step tiles)
     int32_t* row_ptr;          // (B*Hsel*NQ + 1) the caller's row offsets, written from row_src
     int8_t* keep;              // (B, Hsel, NQ, NK)
     int32_t* col_idx;

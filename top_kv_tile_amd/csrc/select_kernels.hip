@@ -603,8 +603,8 @@ __global__ __launch_bounds__(256, (EPL <= 32 ? 4 : 1)) void topk_kernel(TopkArgs
     const M keepm = must_kept | picked;
 
     int8_t* krow = a.keep + r * a.NK;
-    const int32_t row_begin = a.row_src[r];
-    const int32_t row_end = a.row_src[r + 1];
+    const int32_t row_begin = a.row_src ? a.row_src[r] : (int32_t)(r * a.row_step);
+    const int32_t row_end = a.row_src ? a.row_src[r + 1] : (int32_t)((r + 1) * a.row_step);
     const int32_t row_len = row_end - row_begin;  // planned on the host from the same rule
     if (lane == 0) {  // the caller's row offsets (the last row also writes the end)
         a.row_ptr[r] = row_begin;
@@ -806,8 +806,8 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(TopkArgs a) {
     const M keepm = must_kept | picked;
 
     int8_t* krow = a.keep + r * a.NK;
-    const int32_t row_begin = a.row_src[r];
-    const int32_t row_end = a.row_src[r + 1];
+    const int32_t row_begin = a.row_src ? a.row_src[r] : (int32_t)(r * a.row_step);
+    const int32_t row_end = a.row_src ? a.row_src[r + 1] : (int32_t)((r + 1) * a.row_step);
     const int32_t row_len = row_end - row_begin;  // planned on the host from the same rule
     if (tid == 0) {  // the caller's row offsets (the last row also writes the end)
         a.row_ptr[r] = row_begin;

@@ -362,9 +362,9 @@ void fill_sizes(const Plan& p, const nsa_spec* spec, nsa_sizes* out, int32_t* ro
     if (row_ptr_host) std::memcpy(row_ptr_host, p.row_ptr.data(), p.row_ptr.size() * sizeof(int32_t));
 }
 
-int score_and_topk(const Plan& p, const nsa_spec* spec, const float* qh, const float* kh, int Hk, int NKs,
+int score_and_topk(const Plan& p, const nsa_spec* spec, const void* qh, const float* kh, int Hk, int NKs,
                    const WsLayout& w, char* ws, nsa_selection* out, hipStream_t stream, const uint64_t* pin_words,
-                   const uint64_t* drop_words, const int32_t* row_src, int32_t row_step = 0);
+                   const uint64_t* drop_words, const int32_t* row_src, int32_t row_step = 0, int q_rows = 0);
 
 // Enqueues the selection of a built plan (row_ptr present) for tensors q, k
 // whose geometry the plan was built from.
@@ -435,15 +435,15 @@ int run_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, c
 
 // Scores chunk by chunk of selection heads, each followed by its top-k and CSR.
 // pin_words / drop_words: the plan's bit-packed masks on the device (or null).
-int score_and_topk(const Plan& p, const nsa_spec* spec, const float* qh, const float* kh, int Hk, int NKs,
+int score_and_topk(const Plan& p, const nsa_spec* spec, const void* qh, const float* kh, int Hk, int NKs,
                    const WsLayout& w, char* ws, nsa_selection* out, hipStream_t stream, const uint64_t* pin_words,
-                   const uint64_t* drop_words, const int32_t* row_src, int32_t row_step) {
+                   const uint64_t* drop_words, const int32_t* row_src, int32_t row_step, int q_rows) {
     const Geo& g = p.g;
     float* scores = (float*)(ws + w.scores);
     for (int h0 = 0; h0 < g.Hsel; h0 += w.chunk) {
         const int nh = std::min(w.chunk, g.Hsel - h0);
         hipError_t e = nsa::launch_scores(qh, kh, g.B, g.Hsel, Hk, g.group, h0, nh, g.NQ, g.NK, g.D, scores,
-                                          stream, NKs);
+                                          stream, NKs, q_rows);
         if (e != hipSuccess) return hip_fail(e);
         nsa::TopkArgs ta;
         ta.scores = scores;
@@ -1345,10 +1345,16 @@ int nsa_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t l
             if (e != hipSuccess) return hip_fail(e);
         }
         // Pooled queries; the pooled keys are the caller's cache (capacity pooled_k->S tiles per head).
+        // One new token per head (per-head selection): the score kernel pools
+        // its single-row tile itself and nothing is launched for it here.
         float* pq = (float*)(ws + w.pq);
-        hipError_t e = nsa::launch_pool(q->data, g.bf16, (int64_t)g.B * g.Hq, g.Sq, g.D, spec->block_q, pq, stream);
-        if (e != hipSuccess) return hip_fail(e);
-        const float* qh = pq;
+        const int q_rows = (g.Sq == 1 && !spec->head_shared) ? (g.bf16 ? 1 : 2) : 0;
+        hipError_t e = hipSuccess;
+        if (!q_rows) {
+            e = nsa::launch_pool(q->data, g.bf16, (int64_t)g.B * g.Hq, g.Sq, g.D, spec->block_q, pq, stream);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        const void* qh = q_rows ? q->data : (const void*)pq;
         const float* kh = (const float*)pooled_k->data;
         int Hk = g.Hkv, NKs = pooled_k->S;
         if (spec->head_shared) {
@@ -1365,7 +1371,7 @@ int nsa_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t l
         return score_and_topk(p, spec, qh, kh, Hk, NKs, w, ws, out, stream,
                               p.has_pins ? (const uint64_t*)(ws + w.pinw) : nullptr,
                               p.has_drops ? (const uint64_t*)(ws + w.dropw) : nullptr,
-                              uniform ? nullptr : (const int32_t*)(ws + w.rowp), uniform ? step : 0);
+                              uniform ? nullptr : (const int32_t*)(ws + w.rowp), uniform ? step : 0, q_rows);
     } catch (...) {
         return NSA_ERR_UNSUPPORTED;
     }

@@ -26,8 +26,11 @@ hipError_t launch_head_mean(const float* in, int B, int H, int N, int D, float* 
 // Scores for selection heads [h0, h0 + nh): s[b, h - h0, i, j] = qh[b, h, i] . kh[b, h / group, j]
 // qh: (B, Hsel, NQ, D) fp32, kh: (B, Hk, NK, D) fp32, s: (B, nh, NQ, NK) fp32.
 // kh rows of one head are NKs apart (NKs = 0 means NK).
-hipError_t launch_scores(const float* qh, const float* kh, int B, int Hsel, int Hk, int group,
-                         int h0, int nh, int NQ, int NK, int D, float* s, hipStream_t stream, int NKs = 0);
+// q_rows = 1 or 2: qh holds query rows (bf16 or fp32) of single-token tiles,
+// pooled on the fly (NQ <= 8 only).
+hipError_t launch_scores(const void* qh, const float* kh, int B, int Hsel, int Hk, int group,
+                         int h0, int nh, int NQ, int NK, int D, float* s, hipStream_t stream, int NKs = 0,
+                         int q_rows = 0);
 
 // Per-row top-k over the score chunk of heads [h0, h0 + nh) and CSR emission.
 struct TopkArgs {

@@ -342,8 +342,11 @@ __global__ __launch_bounds__(256) void score_lds_kernel(const float* __restrict_
 // loads (rows padded by 4 floats) next to the (at most 8) pooled query rows;
 // then four consecutive threads share a tile, each summing a quarter of the
 // contraction, and two DPP steps add the four partial sums.
-template <int D>
-__global__ __launch_bounds__(256) void score_rows_kernel(const float* __restrict__ qh, const float* __restrict__ kh,
+// QIN says what qh holds: 0 the pooled queries (fp32); 1 or 2 the query rows
+// themselves (bf16 or fp32), when every query tile is a single token. Such a
+// tile's pooled query is 0 + row / 1 in fp32, which is what is staged.
+template <int D, int QIN>
+__global__ __launch_bounds__(256) void score_rows_kernel(const void* __restrict__ qh, const float* __restrict__ kh,
                                                          int Hsel, int Hk, int group, int h0, int nh, int NQ,
                                                          int NK, int NKs, float* __restrict__ s) {
     constexpr int KP = D + 4, QD = D / 4;
@@ -358,10 +361,19 @@ __global__ __launch_bounds__(256) void score_rows_kernel(const float* __restrict
     const int b = (int)(wid / nh);
     const int h = h0 + hl;
     const int hk = (Hk == 1) ? 0 : h / group;
-    const float* A = qh + ((int64_t)b * Hsel + h) * NQ * D;
+    const int64_t qoff = ((int64_t)b * Hsel + h) * NQ * D;
     const float* Bm = kh + ((int64_t)b * Hk + hk) * NKs * D;
     const int j0 = jb * 64;
-    for (int x = tid; x < NQ * D / 4; x += 256) *(f32x4*)(qs + 4 * x) = *(const f32x4*)(A + 4 * x);
+    if constexpr (QIN == 0) {
+        const float* A = (const float*)qh + qoff;
+        for (int x = tid; x < NQ * D / 4; x += 256) *(f32x4*)(qs + 4 * x) = *(const f32x4*)(A + 4 * x);
+    } else if constexpr (QIN == 1) {
+        const uint16_t* A = (const uint16_t*)qh + qoff;
+        for (int x = tid; x < NQ * D; x += 256) qs[x] = 0.f + __uint_as_float((uint32_t)A[x] << 16);
+    } else {
+        const float* A = (const float*)qh + qoff;
+        for (int x = tid; x < NQ * D; x += 256) qs[x] = 0.f + A[x];
+    }
     for (int x = tid; x < 64 * D / 4; x += 256) {
         const int row = x / (D / 4), c4 = x % (D / 4);
         const int j = min(j0 + row, NK - 1);  // rows past NK repeat the last one and are not stored
@@ -875,27 +887,34 @@ hipError_t launch_head_mean(const float* in, int B, int H, int N, int D, float* 
     return hipGetLastError();
 }
 
-hipError_t launch_scores(const float* qh, const float* kh, int B, int Hsel, int Hk, int group, int h0, int nh,
-                         int NQ, int NK, int D, float* s, hipStream_t stream, int NKs) {
+hipError_t launch_scores(const void* qh, const float* kh, int B, int Hsel, int Hk, int group, int h0, int nh,
+                         int NQ, int NK, int D, float* s, hipStream_t stream, int NKs, int q_rows) {
     if (NKs <= 0) NKs = NK;
     if (NQ == 0 || NK == 0 || nh == 0 || B == 0) return hipSuccess;
+    if (q_rows != 0 && NQ > 8) return hipErrorInvalidValue;
     if (NQ <= 8) {
         const dim3 g((unsigned)((int64_t)B * nh * ((NK + 63) / 64)));
-#define NSA_ROWS(DD)                                                                                         \
-    hipLaunchKernelGGL((score_rows_kernel<DD>), g, dim3(256), 0, stream, qh, kh, Hsel, Hk, group, h0, nh, NQ, NK, \
-                       NKs, s)
-        if (D == 64) NSA_ROWS(64);
-        else if (D == 128) NSA_ROWS(128);
-        else if (D == 256) NSA_ROWS(256);
-        else return hipErrorInvalidValue;
+#define NSA_ROWS(DD, QI)                                                                                          \
+    hipLaunchKernelGGL((score_rows_kernel<DD, QI>), g, dim3(256), 0, stream, qh, kh, Hsel, Hk, group, h0, nh, NQ, \
+                       NK, NKs, s)
+#define NSA_ROWS_D(QI)                      \
+    if (D == 64) NSA_ROWS(64, QI);          \
+    else if (D == 128) NSA_ROWS(128, QI);   \
+    else if (D == 256) NSA_ROWS(256, QI);   \
+    else return hipErrorInvalidValue;
+        if (q_rows == 0) NSA_ROWS_D(0)
+        else if (q_rows == 1) NSA_ROWS_D(1)
+        else NSA_ROWS_D(2)
+#undef NSA_ROWS_D
 #undef NSA_ROWS
         return hipGetLastError();
     }
+    const float* qf = (const float*)qh;
     if (NQ > 64) {
         const int nbi = (NQ + 127) / 128, nbj = (NK + 255) / 256;
         const dim3 grid((unsigned)((int64_t)B * nh * nbi * nbj));
 #define NSA_SCORE_LDS(DD)                                                                                     \
-    hipLaunchKernelGGL((score_lds_kernel<DD>), grid, dim3(256), 0, stream, qh, kh, Hsel, Hk, group, h0, nh, NQ, \
+    hipLaunchKernelGGL((score_lds_kernel<DD>), grid, dim3(256), 0, stream, qf, kh, Hsel, Hk, group, h0, nh, NQ, \
                        NK, NKs, nbi, nbj, s)
         if (D == 64) NSA_SCORE_LDS(64);
         else if (D == 128) NSA_SCORE_LDS(128);
@@ -908,7 +927,7 @@ hipError_t launch_scores(const float* qh, const float* kh, int B, int Hsel, int 
     const int64_t blocks = (int64_t)B * nh * nbi * ((nbj + 3) / 4);
     const dim3 grid((unsigned)blocks);
 #define NSA_SCORE(DD)                                                                                 \
-    hipLaunchKernelGGL((score_kernel<DD>), grid, dim3(256), 0, stream, qh, kh, Hsel, Hk, group, h0, nh, NQ, \
+    hipLaunchKernelGGL((score_kernel<DD>), grid, dim3(256), 0, stream, qf, kh, Hsel, Hk, group, h0, nh, NQ, \
                        NK, NKs, nbi, nbj, s)
     if (D == 64) NSA_SCORE(64);
     else if (D == 128) NSA_SCORE(128);

@@ -364,7 +364,8 @@ void fill_sizes(const Plan& p, const nsa_spec* spec, nsa_sizes* out, int32_t* ro
 
 int score_and_topk(const Plan& p, const nsa_spec* spec, const void* qh, const float* kh, int Hk, int NKs,
                    const WsLayout& w, char* ws, nsa_selection* out, hipStream_t stream, const uint64_t* pin_words,
-                   const uint64_t* drop_words, const int32_t* row_src, int32_t row_step = 0, int q_rows = 0);
+                   const uint64_t* drop_words, const int32_t* row_src, int32_t row_step = 0, int q_rows = 0,
+                   bool inline_masks = false);
 
 // Enqueues the selection of a built plan (row_ptr present) for tensors q, k
 // whose geometry the plan was built from.
@@ -437,7 +438,8 @@ int run_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, c
 // pin_words / drop_words: the plan's bit-packed masks on the device (or null).
 int score_and_topk(const Plan& p, const nsa_spec* spec, const void* qh, const float* kh, int Hk, int NKs,
                    const WsLayout& w, char* ws, nsa_selection* out, hipStream_t stream, const uint64_t* pin_words,
-                   const uint64_t* drop_words, const int32_t* row_src, int32_t row_step, int q_rows) {
+                   const uint64_t* drop_words, const int32_t* row_src, int32_t row_step, int q_rows,
+                   bool inline_masks) {
     const Geo& g = p.g;
     float* scores = (float*)(ws + w.scores);
     for (int h0 = 0; h0 < g.Hsel; h0 += w.chunk) {
@@ -466,6 +468,20 @@ int score_and_topk(const Plan& p, const nsa_spec* spec, const void* qh, const fl
         ta.dh = p.dh;
         ta.row_src = row_src;
         ta.row_step = row_step;
+        if (inline_masks) {  // the plan's mask words ride in the launch arguments
+            int n = 0;
+            if (p.has_pins) {
+                std::memcpy(ta.words, p.pin_words.data(), p.pin_words.size() * 8);
+                ta.pin_at = 0;
+                ta.pin_words = nullptr;
+                n = (int)p.pin_words.size();
+            }
+            if (p.has_drops) {
+                std::memcpy(ta.words + n, p.drop_words.data(), p.drop_words.size() * 8);
+                ta.drop_at = n;
+                ta.drop_words = nullptr;
+            }
+        }
         ta.row_ptr = out->row_ptr;
         ta.keep = out->keep;
         ta.col_idx = out->col_idx;
@@ -1330,12 +1346,18 @@ int nsa_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t l
             const hipError_t e = upload(1, dst, src, bytes, stream);
             return e == hipSuccess ? NSA_OK : hip_fail(e);
         }
-        // Without masks every row sees the same keys and keeps the same number
-        // of tiles: the top-k kernel then computes the row offsets itself and
-        // nothing is copied to the device.
+        // When every row keeps the same number of tiles (always so without
+        // masks: every row sees the same keys) the top-k kernel computes the
+        // row offsets itself, and small masks ride in its launch arguments:
+        // then nothing is copied to the device.
         const int32_t step = p.row_ptr[1] - p.row_ptr[0];
-        bool uniform = !p.has_pins && !p.has_drops;
+        bool uniform = true;
         for (size_t r = 1; uniform && r < p.row_ptr.size(); ++r) uniform = p.row_ptr[r] == (int64_t)r * step;
+        // A mask rides in the launch arguments only as one row of words that every row shares.
+        const size_t mask_words = (p.has_pins ? p.pin_words.size() : 0) + (p.has_drops ? p.drop_words.size() : 0);
+        const bool one_row = (!p.has_pins || p.pin_words.size() == (size_t)g.NKW) &&
+                             (!p.has_drops || p.drop_words.size() == (size_t)g.NKW);
+        uniform = uniform && one_row && mask_words <= (size_t)nsa::kInlineMaskWords;
         if (!uniform) {  // row offsets and mask words, one copy into the workspace
             void* dst[3] = {ws + w.rowp, ws + w.pinw, ws + w.dropw};
             const void* src[3] = {p.row_ptr.data(), p.pin_words.data(), p.drop_words.data()};
@@ -1371,7 +1393,8 @@ int nsa_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t l
         return score_and_topk(p, spec, qh, kh, Hk, NKs, w, ws, out, stream,
                               p.has_pins ? (const uint64_t*)(ws + w.pinw) : nullptr,
                               p.has_drops ? (const uint64_t*)(ws + w.dropw) : nullptr,
-                              uniform ? nullptr : (const int32_t*)(ws + w.rowp), uniform ? step : 0, q_rows);
+                              uniform ? nullptr : (const int32_t*)(ws + w.rowp), uniform ? step : 0, q_rows,
+                              uniform);
     } catch (...) {
         return NSA_ERR_UNSUPPORTED;
     }

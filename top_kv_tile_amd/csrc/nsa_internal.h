@@ -33,6 +33,7 @@ hipError_t launch_scores(const void* qh, const float* kh, int B, int Hsel, int H
                          int q_rows = 0);
 
 // Per-row top-k over the score chunk of heads [h0, h0 + nh) and CSR emission.
+constexpr int kInlineMaskWords = 64;  // mask words a top-k launch can carry in its arguments
 struct TopkArgs {
     const float* scores;       // (B, nh, NQ, NK)
     int B, Hsel, h0, nh, NQ, NK, NKW;
@@ -43,6 +44,9 @@ struct TopkArgs {
     int pb, ph;
     const uint64_t* drop_words;
     int db, dh;
+    int pin_at = -1, drop_at = -1;  // with pin_words / drop_words null: the words start at
+                                    // words[pin_at] / words[drop_at] (-1: no such mask)
+    uint64_t words[kInlineMaskWords];
     const int32_t* row_src;    // (B*Hsel*NQ + 1) row offsets (planned on the host), read; or null:
     int32_t row_step;          //   then row r starts at r * row_step (every row keeps row_step tiles)
     int32_t* row_ptr;          // (B*Hsel*NQ + 1) the caller's row offsets, written from row_src

@@ -587,8 +587,14 @@ __global__ __launch_bounds__(256, (EPL <= 32 ? 4 : 1)) void topk_kernel(TopkArgs
     M cand = 0, must_kept = 0;
     int c = 0;
     const int nw = (a.NK + 63) / 64;
-    const uint64_t pin_l = (pw && lane < nw) ? pw[lane] : 0ull;
-    const uint64_t drop_l = (dw && lane < nw) ? dw[lane] : 0ull;
+    // Mask words from device memory, or (masks shared by every row) from the launch arguments.
+    uint64_t pin_l = 0ull, drop_l = 0ull;
+    if (lane < nw) {
+        if (pw) pin_l = pw[lane];
+        else if (a.pin_at >= 0) pin_l = a.words[a.pin_at + lane];
+        if (dw) drop_l = dw[lane];
+        else if (a.drop_at >= 0) drop_l = a.words[a.drop_at + lane];
+    }
 #pragma unroll 1
     for (int t = 0; t < EPL; ++t) {
         const int base = 64 * t;
@@ -684,8 +690,14 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(TopkArgs a) {
     // Masks: word 4 t + w of the row (lane x < EPT holds word 4 x + w).
     const int nw = (a.NK + 63) / 64;
     const int wx = 4 * lane + wave;
-    const uint64_t pin_l = (pw && lane < EPT && wx < nw) ? pw[wx] : 0ull;
-    const uint64_t drop_l = (dw && lane < EPT && wx < nw) ? dw[wx] : 0ull;
+    // Mask words from device memory, or (masks shared by every row) from the launch arguments.
+    uint64_t pin_l = 0ull, drop_l = 0ull;
+    if (lane < EPT && wx < nw) {
+        if (pw) pin_l = pw[wx];
+        else if (a.pin_at >= 0) pin_l = a.words[a.pin_at + wx];
+        if (dw) drop_l = dw[wx];
+        else if (a.drop_at >= 0) drop_l = a.words[a.drop_at + wx];
+    }
     M cand = 0, must_kept = 0;
     int cw_count = 0;
 #pragma unroll

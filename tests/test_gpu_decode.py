@@ -153,3 +153,34 @@ def test_decode_128k_cache(shared):
     out, lse = tkt.nsa_decode_attn(qd, kd, vd, L, L - 1, None)
     ref_o, ref_l = oracle.decode_attention(q, kc, vc, L, L - 1, np.ones((1, 1, 1, nk), np.int8), 32, bkv)
     check_attention(out, lse, ref_o, ref_l, "bf16", where="128k dense decode")
+
+
+@pytest.mark.parametrize("n,pin_rows,drop_rows", [(1, 1, 1), (3, 1, 1), (1, 0, 1), (1, 2, 1), (2, 1, 16)])
+def test_decode_mask_rows(n, pin_rows, drop_rows):
+    """Decode selection with pin and drop masks of one row shared by every row
+    (carried in the top-k launch: nothing is uploaded), of several rows (copied
+    to the device), or absent, for one and for a few new tokens."""
+    say(f"decode masks n={n} pin_rows={pin_rows} drop_rows={drop_rows}")
+    B, Hq, Hkv, L, D, bkv, bq = 2, 16, 4, 8192, 128, 64, 32
+    g = torch.Generator().manual_seed(1000 + 10 * n + pin_rows + drop_rows)
+    kc, vc = (torch.randn(B, Hkv, L, D, generator=g).to(torch.bfloat16) for _ in range(2))
+    q = torch.randn(B, Hq, n, D, generator=g).to(torch.bfloat16)
+    nk = L // bkv
+    rng = np.random.default_rng(n + pin_rows + drop_rows)
+    pins = None
+    if pin_rows:
+        pins = (rng.random((pin_rows, 1, 1, nk)) < 0.03).astype(np.int8)
+        pins[..., 0] = 1
+        pins[..., nk // 2] = 1
+    drops = (rng.random((1, drop_rows, 1, nk)) < 0.1).astype(np.int8)
+    drops[..., nk // 2] = 1  # pinned and dropped: the drop wins
+    kd, vd, qd = to_dev(kc), to_dev(vc), to_dev(q)
+    pooled = torch.zeros(B, Hkv, nk, D, dtype=torch.float32, device="cuda:0")
+    tkt.nsa_decode_pool_update(kd, 0, L, bkv, pooled)
+    spec = tkt.SparseSpec(budget=0.1, block_q=bq, block_kv=bkv, head_shared=False)
+    sel = tkt.nsa_decode_select(qd, pooled, L, L - n, spec, pins=pins, drops=drops)
+    ref = oracle.decode_select(q, kc, L, L - n, spec.budget, bq, bkv, False, False, pins=pins, drops=drops)
+    keep, _ = check_selection(sel, ref, "mask rows select")
+    out, lse = tkt.nsa_decode_attn(qd, kd, vd, L, L - n, sel)
+    ref_o, ref_l = oracle.decode_attention(q, kc, vc, L, L - n, keep, bq, bkv)
+    check_attention(out, lse, ref_o, ref_l, "bf16", where="mask rows decode")

@@ -98,37 +98,63 @@ def read_traffic():
         return None
 
 
-def cpu_baseline(inp, w: synth.Workload, budget_s: float = 20.0):
-    """The oracle, untuned, on a bounded sample of the same workload (host cores)."""
+def _oracle_attention_threaded(inp, w: synth.Workload, keep, rows, threads: int) -> float:
+    """Wall time of oracle.attention over `rows` (b, h, i), one query head's slice
+    per call (q[b, h], its kv head, its selection plane), `threads` calls at a
+    time with BLAS held to one thread each, so the per-row work occupies the
+    cores the way one large BLAS call would."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    group = w.Hq // w.Hkv
+    by_head = {}
+    for b, h, i in rows:
+        by_head.setdefault((b, h), []).append(i)
+    jobs = [(b, h, t) for (b, h), t in sorted(by_head.items())]
+
+    def run(job):
+        b, h, tiles = job
+        g = h // group
+        kb = b if keep.shape[0] == w.B else 0
+        hs = h if keep.shape[1] == w.Hq else 0
+        oracle.attention(inp.q[b:b + 1, h:h + 1], inp.k[b:b + 1, g:g + 1], inp.v[b:b + 1, g:g + 1],
+                         keep[kb:kb + 1, hs:hs + 1], w.block_q, w.block_kv, w.causal,
+                         rows=[(0, 0, i) for i in tiles])
+
+    nthr = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        with threadpool_limits(1), ThreadPoolExecutor(threads) as ex:
+            list(ex.map(run, jobs))
+        return time.perf_counter() - t0
+    finally:
+        torch.set_num_threads(nthr)
+
+
+def cpu_baseline(inp, w: synth.Workload, full_flops: float, heads_per_index: int = 4):
+    """The oracle, untuned, on the host cores: oracle.select_blocks on the whole
+    workload, and oracle.attention (fp64) on a seeded 1/16 of the (b, h, q-tile)
+    rows (heads_per_index heads for every query-tile index), extrapolated
+    linearly to all rows. value = the step's kept-tile FLOPs / that time."""
     import oracle
 
-    threads = torch.get_num_threads()
-    g0 = 0  # one GQA group: query heads 0..7 with kv head 0
-    G = w.Hq // w.Hkv
-    q = inp.q[:, g0 * G:(g0 + 1) * G]
-    k = inp.k[:, g0:g0 + 1]
-    v = inp.v[:, g0:g0 + 1]
+    threads = max(1, min(16, os.cpu_count() or 1))
     t0 = time.perf_counter()
-    ref = oracle.select_blocks(q, k, w.budget, w.block_q, w.block_kv, w.head_shared, False, inp.pins, inp.drops)
+    ref = oracle.select_blocks(inp.q, inp.k, w.budget, w.block_q, w.block_kv, w.head_shared, False,
+                               inp.pins, inp.drops)
     t_sel = time.perf_counter() - t0
-    sel_rows = G * w.nq
     rng = np.random.default_rng(11)
-    t_att, n_rows, fl = 0.0, 0, 0.0
-    keep = ref["keep"]
-    while t_att < budget_s * 0.6 and n_rows < 256:
-        h = int(rng.integers(G))
-        i = int(rng.integers(w.nq))
-        t0 = time.perf_counter()
-        oracle.attention(q, k, v, keep, w.block_q, w.block_kv, w.causal, rows=[(0, h, i)])
-        t_att += time.perf_counter() - t0
-        n_rows += 1
-        cols = np.nonzero(keep[0, h, i])[0]
-        qhi = min((i + 1) * w.block_q, w.S)
-        live = cols[cols * w.block_kv <= qhi - 1]
-        fl += 4.0 * w.D * w.block_q * w.block_kv * live.size
-    per_row_s = t_sel / sel_rows + t_att / n_rows
-    per_row_flops = fl / n_rows
-    value = per_row_flops / per_row_s / 1e12
+    rows = []
+    for i in range(w.nq):
+        for p in rng.choice(w.B * w.Hq, size=min(heads_per_index, w.B * w.Hq), replace=False):
+            rows.append((int(p) // w.Hq, int(p) % w.Hq, i))
+    total_rows = w.B * w.Hq * w.nq
+    t_att = _oracle_attention_threaded(inp, w, ref["keep"], rows, threads)
+    frac = len(rows) / total_rows
+    t_step = t_sel + t_att / frac
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -136,11 +162,16 @@ def cpu_baseline(inp, w: synth.Workload, budget_s: float = 20.0):
     except OSError:
         pass
     return {
-        "value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "value": full_flops / t_step / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "host_cpus": os.cpu_count(), "cpu_model": cpu_model,
-        "sample": (f"oracle.select_blocks on one GQA group ({G} query heads x {w.nq} query tiles, "
-                   f"{t_sel:.1f} s) + oracle.attention (fp64) on {n_rows} seeded (head, query-tile) rows "
-                   f"({t_att:.1f} s); per-row select + attention time, kept-tile FLOPs of the sampled rows"),
+        "select_s": round(t_sel, 2), "attn_sample_s": round(t_att, 2), "attn_sample_rows": len(rows),
+        "attn_sample_frac": frac, "step_s_extrapolated": round(t_step, 2),
+        "sample": (f"oracle.select_blocks on the whole workload ({w.B * (1 if w.head_shared else w.Hq) * w.nq} "
+                   f"rows, {t_sel:.1f} s, torch/numpy on {torch.get_num_threads()} threads) + oracle.attention "
+                   f"(fp64) on a seeded 1/{round(1 / frac)} of the query rows ({len(rows)} rows: "
+                   f"{heads_per_index} heads per query-tile index, {t_att:.1f} s on {threads} threads, one "
+                   f"head slice per call), extrapolated linearly to all rows; value = the step's kept-tile "
+                   f"FLOPs over select + extrapolated attention time"),
     }
 
 
@@ -225,6 +256,76 @@ def measured_peaks(reps: int = 10) -> dict:
             "how": "8192^3 bf16 torch.matmul and a 2 GiB torch tensor copy on the same GPU, events, "
                    f"mean of {reps} calls; torch's copy streams slower than this library's own "
                    "pooling and permutation kernels, so HBM fractions use the published 8 TB/s"}
+
+
+PEAK_FP32_TFLOPS = 157.3     # MI355X dense fp32 (matrix and vector)
+
+
+def stage_timing(plan, q, k, ws, sel: tkt.Selection, w: synth.Workload, spec: tkt.SparseSpec,
+                 calls: int = 20) -> dict:
+    """Device time of every selection stage, from the library's stage events,
+    over `calls` planned selections (run after the timed steps, same inputs),
+    with each stage's algorithmic bytes (and FLOPs for the score product):
+      pool_q / pool_k: read q / k once, write the pooled fp32 means;
+      scores_c (head chunk c): 2 * B * nh * NQ * NK * D FLOP, writes the chunk's fp32 scores;
+      topk_c: reads the chunk's scores, writes its keep bytes, CSR entries and row offsets.
+    Reports p10 / p50 / p90 in ms, GB/s and fractions at the published peaks."""
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        tkt.nsa_select_planned(plan, q, k, workspace=ws)
+    torch.cuda.synchronize()
+    tkt.nsa_stage_timing_begin()
+    for _ in range(calls):
+        tkt.nsa_select_planned(plan, q, k, workspace=ws)
+    recs = tkt.nsa_stage_timing_end()
+    per_call = len(recs) // calls
+    if per_call * calls != len(recs):
+        raise RuntimeError(f"stage timing: {len(recs)} records for {calls} calls")
+    names, seen = [], {}
+    for name, _ in recs[:per_call]:
+        n = seen.get(name, 0)
+        seen[name] = n + 1
+        names.append(f"{name}_{n}" if name in ("scores", "topk") else name)
+    times = {nm: [recs[c * per_call + x][1] for c in range(calls)] for x, nm in enumerate(names)}
+
+    H = sel.keep.shape[1]
+    NQ, NK, D, B = w.nq, w.nk, w.D, w.B
+    esz = q.element_size()
+    chunk = max(1, min(H, spec.score_chunk_bytes // (NQ * NK * 4)))
+    row_ptr = sel.row_ptr.cpu().numpy().astype(np.int64)
+    out = {}
+    for nm, xs in times.items():
+        ms = float(np.median(xs))
+        d = {"p10_ms": round(float(np.percentile(xs, 10)), 4), "p50_ms": round(ms, 4),
+             "p90_ms": round(float(np.percentile(xs, 90)), 4)}
+        flops = None
+        if nm == "pool_q":
+            nbytes = B * w.Hq * w.S * D * esz + B * w.Hq * NQ * D * 4
+        elif nm == "pool_k":
+            nbytes = B * w.Hkv * w.S * D * esz + B * w.Hkv * NK * D * 4
+        elif nm == "head_mean":
+            nbytes = B * (w.Hq * NQ + w.Hkv * NK + NQ + NK) * D * 4
+        else:
+            c = int(nm.rsplit("_", 1)[1])
+            h0 = c * chunk
+            nh = min(chunk, H - h0)
+            cells = B * nh * NQ * NK
+            if nm.startswith("scores"):
+                flops = 2.0 * cells * D
+                nbytes = cells * 4
+            else:
+                nnz = sum(int(row_ptr[(b * H + h0 + nh) * NQ] - row_ptr[(b * H + h0) * NQ]) for b in range(B))
+                nbytes = cells * 4 + cells + 4 * nnz + 4 * B * nh * NQ
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        d.update({"bytes": float(nbytes), "GBps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+        if flops is not None:
+            tf = flops / (ms * 1e-3) / 1e12
+            d.update({"flops": flops, "TFLOPs": round(tf, 2), "frac_fp32_peak": round(tf / PEAK_FP32_TFLOPS, 4)})
+        out[nm] = d
+    out["how"] = (f"HIP events the library records on the selection stream between its launches "
+                  f"(nsa_stage_timing_begin/_end), {calls} planned selections after the timed steps; "
+                  f"fractions against 8 TB/s HBM and 157.3 TFLOP/s fp32")
+    return out
 
 
 def _host_us(fn, calls: int) -> float:
@@ -458,6 +559,8 @@ def main():
                    "attn_TFLOPs": round(attn_tflops, 2),
                    "step_ms_events": step_pct, "attn_ms_events": attn_pct},
     }
+    log("[bench] per-stage selection timing")
+    res["stages"]["select_stages"] = stage_timing(plan, q, k, ws, sel, w, spec)
     if not args.no_peaks:
         peaks = measured_peaks()
         res["measured_peaks"] = peaks
@@ -471,7 +574,7 @@ def main():
         res["reorder"] = reorder_timing(q, w)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample)")
-        res["cpu_baseline"] = cpu_baseline(inp, w)
+        res["cpu_baseline"] = cpu_baseline(inp, w, full_flops)
     print(json.dumps(res), flush=True)
 
 

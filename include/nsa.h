@@ -358,6 +358,27 @@ int nsa_pool_blocks(const nsa_tensor* x, int32_t block, float* out, void* stream
 int nsa_score_blocks(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec,
                      float* scores, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Stage timing (measurement) ----------------------------------------------
+ * Between nsa_stage_timing_begin and nsa_stage_timing_end, the selection calls
+ * (nsa_select, nsa_select_planned, nsa_decode_select) made on the calling
+ * thread record a HIP event on their stream at their start and after each
+ * stage: "pool_q", "pool_k", "head_mean" (head_shared), then "scores" and
+ * "topk" once per head chunk. Host only; the events are created by the library
+ * and destroyed by _end. */
+typedef struct nsa_stage_time {
+    const char* name;   /* static string: the stage that ended at this mark */
+    float ms;           /* device time since the previous mark of the same call */
+} nsa_stage_time;
+
+/* Starts recording on this thread (drops any marks of an unfinished run). */
+int nsa_stage_timing_begin(void);
+
+/* Stops recording, waits for the last recorded event, and writes up to
+ * `capacity` stages in the order they were enqueued; *count receives the
+ * number recorded (which may exceed capacity). NULL_ARG if count is NULL, or
+ * out is NULL with capacity > 0; HIP if an event query fails. */
+int nsa_stage_timing_end(nsa_stage_time* out, int32_t capacity, int32_t* count);
+
 /* Static description of a status code. Never NULL. */
 const char* nsa_status_string(int status);
 

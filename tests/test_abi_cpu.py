@@ -91,6 +91,13 @@ def test_dense_decision_and_force(L):
     assert st == 0 and out.dense == 0 and out.nnz == 2 * 8 * 16  # every tile of both heads
     st, out = _sizes(_t(1, 2, 0, 64), _t(1, 2, 0, 64, data=None), tkt.SparseSpec())
     assert st == 0 and out.dense == 1 and out.rows == 0
+    # a finite budget far above 1 keeps every candidate, like budget 1
+    # (k_r is clamped to c_r before its integer conversion)
+    for budget in (1.5, 1e30, 3.0e38):
+        st, out = _sizes(q, k, tkt.SparseSpec(budget=budget, block_q=64, block_kv=32, force=True))
+        assert st == 0 and out.dense == 0 and out.nnz == 2 * 8 * 16, budget
+        st, out = _sizes(q, k, tkt.SparseSpec(budget=budget, block_q=64, block_kv=32))
+        assert st == 0 and out.dense == 1, budget
 
 
 @pytest.mark.parametrize("mutate,code", [
@@ -102,6 +109,8 @@ def test_dense_decision_and_force(L):
     (lambda q, k, s: (N._Tensor(1, N.NSA_BF16, 1, 4, 256, 96), N._Tensor(1, N.NSA_BF16, 1, 2, 256, 96), s), -4),
     (lambda q, k, s: (q, k, tkt.SparseSpec(budget=-0.1)), -6),
     (lambda q, k, s: (q, k, tkt.SparseSpec(budget=float("nan"))), -6),
+    (lambda q, k, s: (q, k, tkt.SparseSpec(budget=float("inf"))), -6),
+    (lambda q, k, s: (q, k, tkt.SparseSpec(budget=1e39)), -6),         # inf once rounded to fp32
     (lambda q, k, s: (q, k, tkt.SparseSpec(block_q=0)), -6),
     (lambda q, k, s: (q, k, tkt.SparseSpec(score_chunk_bytes=-1)), -6),
     (lambda q, k, s: (N._Tensor(None, N.NSA_BF16, 1, 4, 256, 128), k, s), -1),
@@ -225,3 +234,4 @@ def test_backward_rejects_before_launch(L):
     sel_badnnz = N._Selection(keep=1, row_ptr=1, col_idx=1, nnz=-3, B=1, H=4, NQ=2, NK=4, block_q=128,
                               block_kv=64, seq_q=256, seq_kv=256)
     assert call(sel=sel_badnnz) == -2
+

@@ -4,12 +4,16 @@ the fp64 gradient oracle, on the GPU's own selection.
 Tolerances (derived from the arithmetic; each error is taken relative to the
 largest magnitude of the reference tensor it belongs to):
   * fp32 inputs: max 1e-4 and mean 1e-4 (fp32 accumulation, fp32 P and dS);
-  * bf16 inputs: max 2e-2 and mean 1e-2 of the mean magnitude. The kernels
+  * bf16 inputs: max 2e-2 and mean 5e-3 of the mean magnitude. The kernels
     round P and dS to bf16 for the matrix cores (2^-9 relative each), take
-    Delta from the bf16 forward output, and round the results to bf16
-    (2^-9); sums of such terms with random signs stay well inside 2^-6.
+    Delta from the bf16 forward output, and round the results to bf16. The
+    final rounding alone gives a mean relative error near 2^-9 * 0.7 ~ 1.4e-3
+    (round-to-nearest on an 8-bit significand); the bound leaves about 3.5x
+    that for the P and dS roundings, whose sums have random signs.
 Outputs are prefilled with NaN, so every element must be written.
 """
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -21,7 +25,7 @@ from parity_util import check_selection, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
-GRAD_TOL = {"f32": dict(max_rel=1e-4, mean_rel=1e-4), "bf16": dict(max_rel=2e-2, mean_rel=1e-2)}
+GRAD_TOL = {"f32": dict(max_rel=1e-4, mean_rel=1e-4), "bf16": dict(max_rel=2e-2, mean_rel=5e-3)}
 
 
 def _inputs(B, Hq, Hkv, S, D, seed, dtype):
@@ -37,6 +41,11 @@ def _compare(name, got, ref, dtype, mask=None, where=""):
     g = got.float().cpu().numpy().astype(np.float64)
     if mask is not None:
         g, ref = g[mask], ref[mask]
+    return compare_arrays(name, g, ref, dtype, where)
+
+
+def compare_arrays(name, g, ref, dtype, where=""):
+    """Gradient bounds of this file on fp64 numpy arrays (GPU values, oracle values)."""
     assert np.all(np.isfinite(g)), f"{where}: {name} has non-finite values (unwritten?)"
     assert np.all(np.isfinite(ref))
     tol = GRAD_TOL[dtype]
@@ -101,7 +110,7 @@ CASES = [
 def test_backward_matches_oracle(case):
     name, B, Hq, Hkv, S, D, bq, bkv, budget, shared, causal, dtype = case
     say(f"bwd case {name}")
-    q, k, v, do = _inputs(B, Hq, Hkv, S, D, seed=abs(hash(name)) % 10000, dtype=dtype)
+    q, k, v, do = _inputs(B, Hq, Hkv, S, D, seed=zlib.crc32(name.encode()) % 10000, dtype=dtype)
     spec = tkt.SparseSpec(budget=budget, block_q=bq, block_kv=bkv, head_shared=shared)
     rep = run_bwd_case(q, k, v, do, spec, causal, where=name)
     say(f"  {rep}")

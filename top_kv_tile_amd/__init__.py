@@ -35,6 +35,8 @@ from .nsa import (  # noqa: F401
     nsa_select_planned,
     nsa_select_sizes,
     nsa_selection_density,
+    nsa_stage_timing_begin,
+    nsa_stage_timing_end,
     nsa_status_string,
 )
 

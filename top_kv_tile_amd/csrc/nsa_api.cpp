@@ -51,7 +51,8 @@ struct Geo {
 int check_spec(const nsa_spec* s) {
     if (!s) return NSA_ERR_NULL_ARG;
     if (s->block_q <= 0 || s->block_kv <= 0) return NSA_ERR_BAD_SPEC;
-    if (!(s->budget >= 0.0f)) return NSA_ERR_BAD_SPEC;  // rejects NaN and negatives
+    // rejects NaN, infinities and negatives
+    if (!std::isfinite(s->budget) || s->budget < 0.0f) return NSA_ERR_BAD_SPEC;
     if (s->score_chunk_bytes < 0) return NSA_ERR_BAD_SPEC;
     return NSA_OK;
 }
@@ -132,9 +133,12 @@ struct Plan {
 
 // k_r = ceil(fl32(c_r) * fl32(budget)): an integer count times the budget,
 // evaluated in float32 (the type torch promotes that product to).
+// A product at or above c (a budget above 1) keeps every candidate, so it is
+// clamped to c before the integer conversion.
 inline int64_t keep_per_row(int64_t c, float budget) {
     volatile float prod = (float)c * budget;  // one IEEE fp32 rounding, no contraction
-    return (int64_t)std::ceil((float)prod);
+    const float kf = std::ceil((float)prod);
+    return kf >= (float)c ? c : (int64_t)kf;
 }
 
 int build_plan(const Geo& g, const nsa_spec* spec, const nsa_mask* pins, const nsa_mask* drops, Plan& p,
@@ -317,23 +321,48 @@ hipError_t upload(int n, void* const* dst, const void* const* src, const size_t*
     return hipSuccess;
 }
 
+// Stage timing (nsa_stage_timing_begin / _end): while it is on, the
+// selection calls of this thread record an event on their stream at the start
+// and after every stage launch. Off, a mark costs one thread-local test.
+struct StageTiming {
+    bool on = false;
+    std::vector<const char*> names;
+    std::vector<hipEvent_t> marks;
+};
+thread_local StageTiming t_stages;
+
+hipError_t stage_mark(const char* name, hipStream_t stream) {
+    StageTiming& t = t_stages;
+    if (!t.on) return hipSuccess;
+    hipEvent_t ev = nullptr;
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) return e;
+    t.names.push_back(name);
+    t.marks.push_back(ev);
+    return hipEventRecord(ev, stream);
+}
+
 // Enqueues pooling (+ head means) of q and k into the workspace.
 int run_pool(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, const Geo& g, const WsLayout& w,
              char* ws, hipStream_t stream, const float** qh, const float** kh, int* Hk) {
     hipError_t e;
     float* pq = (float*)(ws + w.pq);
     float* pk = (float*)(ws + w.pk);
+    if ((e = stage_mark("start", stream)) != hipSuccess) return hip_fail(e);
     if ((e = nsa::launch_pool(q->data, g.bf16, (int64_t)g.B * g.Hq, g.Sq, g.D, spec->block_q, pq, stream)) !=
         hipSuccess)
         return hip_fail(e);
+    if ((e = stage_mark("pool_q", stream)) != hipSuccess) return hip_fail(e);
     if ((e = nsa::launch_pool(k->data, g.bf16, (int64_t)g.B * g.Hkv, g.Skv, g.D, spec->block_kv, pk,
                               stream)) != hipSuccess)
         return hip_fail(e);
+    if ((e = stage_mark("pool_k", stream)) != hipSuccess) return hip_fail(e);
     if (spec->head_shared) {
         float* mq = (float*)(ws + w.mq);
         float* mk = (float*)(ws + w.mk);
         if ((e = nsa::launch_head_mean(pq, g.B, g.Hq, g.NQ, g.D, mq, stream)) != hipSuccess) return hip_fail(e);
         if ((e = nsa::launch_head_mean(pk, g.B, g.Hkv, g.NK, g.D, mk, stream)) != hipSuccess) return hip_fail(e);
+        if ((e = stage_mark("head_mean", stream)) != hipSuccess) return hip_fail(e);
         *qh = mq;
         *kh = mk;
         *Hk = 1;
@@ -447,6 +476,7 @@ int score_and_topk(const Plan& p, const nsa_spec* spec, const void* qh, const fl
         hipError_t e = nsa::launch_scores(qh, kh, g.B, g.Hsel, Hk, g.group, h0, nh, g.NQ, g.NK, g.D, scores,
                                           stream, NKs, q_rows);
         if (e != hipSuccess) return hip_fail(e);
+        if ((e = stage_mark("scores", stream)) != hipSuccess) return hip_fail(e);
         nsa::TopkArgs ta;
         ta.scores = scores;
         ta.B = g.B;
@@ -486,6 +516,7 @@ int score_and_topk(const Plan& p, const nsa_spec* spec, const void* qh, const fl
         ta.keep = out->keep;
         ta.col_idx = out->col_idx;
         if ((e = nsa::launch_topk(ta, stream)) != hipSuccess) return hip_fail(e);
+        if ((e = stage_mark("topk", stream)) != hipSuccess) return hip_fail(e);
     }
     return NSA_OK;
 }
@@ -1371,10 +1402,12 @@ int nsa_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t l
         // its single-row tile itself and nothing is launched for it here.
         float* pq = (float*)(ws + w.pq);
         const int q_rows = (g.Sq == 1 && !spec->head_shared) ? (g.bf16 ? 1 : 2) : 0;
-        hipError_t e = hipSuccess;
+        hipError_t e = stage_mark("start", stream);
+        if (e != hipSuccess) return hip_fail(e);
         if (!q_rows) {
             e = nsa::launch_pool(q->data, g.bf16, (int64_t)g.B * g.Hq, g.Sq, g.D, spec->block_q, pq, stream);
             if (e != hipSuccess) return hip_fail(e);
+            if ((e = stage_mark("pool_q", stream)) != hipSuccess) return hip_fail(e);
         }
         const void* qh = q_rows ? q->data : (const void*)pq;
         const float* kh = (const float*)pooled_k->data;
@@ -1439,6 +1472,43 @@ int nsa_decode_attn(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa_te
                                               : nsa::launch_attn_simt(a, bf16, stream);
     }
     return e == hipSuccess ? NSA_OK : hip_fail(e);
+}
+
+int nsa_stage_timing_begin(void) {
+    StageTiming& t = t_stages;
+    for (hipEvent_t ev : t.marks) (void)hipEventDestroy(ev);
+    t.names.clear();
+    t.marks.clear();
+    t.on = true;
+    return NSA_OK;
+}
+
+int nsa_stage_timing_end(nsa_stage_time* out, int32_t capacity, int32_t* count) {
+    StageTiming& t = t_stages;
+    t.on = false;
+    if (!count || (capacity > 0 && !out)) return NSA_ERR_NULL_ARG;
+    int32_t n = 0;
+    int st = NSA_OK;
+    hipError_t e = t.marks.empty() ? hipSuccess : hipEventSynchronize(t.marks.back());
+    if (e != hipSuccess) st = hip_fail(e);
+    for (size_t x = 1; st == NSA_OK && x < t.marks.size(); ++x) {
+        if (std::strcmp(t.names[x], "start") == 0) continue;  // a new call: no stage ends here
+        float ms = 0.f;
+        if ((e = hipEventElapsedTime(&ms, t.marks[x - 1], t.marks[x])) != hipSuccess) {
+            st = hip_fail(e);
+            break;
+        }
+        if (n < capacity) {
+            out[n].name = t.names[x];
+            out[n].ms = ms;
+        }
+        ++n;
+    }
+    for (hipEvent_t ev : t.marks) (void)hipEventDestroy(ev);
+    t.names.clear();
+    t.marks.clear();
+    *count = n;
+    return st;
 }
 
 int nsa_selection_density(const nsa_selection* sel, double* out) {

@@ -24,8 +24,8 @@ __all__ = [
     "nsa_pool_blocks", "nsa_score_blocks", "nsa_status_string", "Plan", "nsa_plan_create",
     "nsa_select_planned", "nsa_schedule", "nsa_radial_blocks", "nsa_selection_density", "nsa_curve_order",
     "nsa_permute_tokens", "NSA_CURVE_MORTON", "NSA_CURVE_HILBERT", "nsa_decode_pool_update", "nsa_decode_select",
-    "nsa_decode_attn", "nsa_plan_cache_config", "nsa_plan_cache_clear", "nsa_plan_cache_stats", "LIB_PATH",
-    "EXPORTS",
+    "nsa_decode_attn", "nsa_plan_cache_config", "nsa_plan_cache_clear",
+    "nsa_plan_cache_stats", "nsa_stage_timing_begin", "nsa_stage_timing_end", "LIB_PATH", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnsa.so")
@@ -35,7 +35,8 @@ EXPORTS = ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_attn_
            "nsa_plan_destroy", "nsa_schedule", "nsa_radial_sizes", "nsa_radial_blocks", "nsa_selection_density",
            "nsa_curve_order", "nsa_permute_tokens", "nsa_decode_pool_update", "nsa_decode_select_sizes",
            "nsa_decode_select", "nsa_decode_attn", "nsa_decode_attn_workspace_size", "nsa_plan_cache_config",
-           "nsa_plan_cache_clear", "nsa_plan_cache_stats")
+           "nsa_plan_cache_clear", "nsa_plan_cache_stats", "nsa_stage_timing_begin",
+           "nsa_stage_timing_end")
 
 NSA_OK, NSA_DENSE = 0, 1
 NSA_F32, NSA_BF16 = 0, 1
@@ -133,6 +134,8 @@ def lib() -> ctypes.CDLL:
                                       ctypes.c_void_p]
         L.nsa_decode_attn_workspace_size.argtypes = [P(_Tensor), P(_Tensor), ctypes.c_int32, ctypes.c_int32,
                                                      P(_Selection), P(ctypes.c_int64)]
+        L.nsa_stage_timing_begin.argtypes = []
+        L.nsa_stage_timing_end.argtypes = [ctypes.c_void_p, ctypes.c_int32, P(ctypes.c_int32)]
         L.nsa_status_string.argtypes = [ctypes.c_int]
         L.nsa_status_string.restype = ctypes.c_char_p
         L.nsa_version.restype = ctypes.c_char_p
@@ -141,7 +144,8 @@ def lib() -> ctypes.CDLL:
                      "nsa_plan_create", "nsa_plan_sizes", "nsa_select_planned", "nsa_schedule", "nsa_radial_sizes",
                      "nsa_radial_blocks", "nsa_selection_density", "nsa_curve_order", "nsa_permute_tokens",
                      "nsa_decode_pool_update", "nsa_decode_select_sizes", "nsa_decode_select", "nsa_decode_attn",
-                     "nsa_decode_attn_workspace_size", "nsa_plan_cache_config", "nsa_plan_cache_stats"):
+                     "nsa_decode_attn_workspace_size", "nsa_plan_cache_config", "nsa_plan_cache_stats",
+                     "nsa_stage_timing_begin", "nsa_stage_timing_end"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -533,3 +537,23 @@ def nsa_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
            "nsa_decode_attn")
     return out, lse
+
+
+class _StageTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("ms", ctypes.c_float)]
+
+
+def nsa_stage_timing_begin():
+    """Start recording stage events for the selection calls of this thread."""
+    _check(lib().nsa_stage_timing_begin(), "nsa_stage_timing_begin")
+
+
+def nsa_stage_timing_end(capacity: int = 1 << 14):
+    """Stop recording; returns [(stage name, device ms)] in launch order."""
+    buf = (_StageTime * capacity)()
+    n = ctypes.c_int32(0)
+    _check(lib().nsa_stage_timing_end(ctypes.cast(buf, ctypes.c_void_p), capacity, ctypes.byref(n)),
+           "nsa_stage_timing_end")
+    if n.value > capacity:
+        raise NsaError(f"nsa_stage_timing_end: {n.value} stages recorded, capacity {capacity}")
+    return [(buf[x].name.decode(), float(buf[x].ms)) for x in range(n.value)]

@@ -320,6 +320,23 @@ int nsa_decode_attn(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa_te
                     int32_t q_pos0, const nsa_selection* sel, nsa_tensor* out, float* lse, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* nsa_decode_attn without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. The split partials go
+ * to a static device buffer of the library, NSA_DECODE_SCRATCH_BYTES (16 MiB)
+ * per GPU, held until the process ends; its address on the current device is
+ * looked up on the first call there. Every call on one GPU shares that buffer
+ * (each call writes every partial it reads, so nothing carries over), so calls
+ * that overlap on one GPU -- from several threads or streams -- race and must be
+ * serialised by the caller. Arguments, result and errors as nsa_decode_attn
+ * with no workspace; NSA_ERR_WORKSPACE when nsa_decode_attn_workspace_size
+ * for the request exceeds NSA_DECODE_SCRATCH_BYTES. The tensors must live on
+ * the current device. */
+#define NSA_DECODE_SCRATCH_BYTES (16u << 20)
+int nsa_decode_attn_static(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa_tensor* v_cache,
+                           int32_t length, int32_t q_pos0, const nsa_selection* sel, nsa_tensor* out, float* lse,
+                           void* stream);
+
 /* Device workspace, in bytes, that nsa_block_sparse_attn_bwd needs for these
  * shapes and this selection (sel may be NULL for dense). Host only. */
 int nsa_attn_bwd_workspace_size(const nsa_tensor* q, const nsa_tensor* k, const nsa_selection* sel,

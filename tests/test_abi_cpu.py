@@ -235,3 +235,29 @@ def test_backward_rejects_before_launch(L):
                               block_kv=64, seq_q=256, seq_kv=256)
     assert call(sel=sel_badnnz) == -2
 
+
+def test_decode_attn_static_rejects_before_launch(L):
+    """The allocation-free decode call checks its request against the static
+    buffer before any HIP call: a split-partial need above
+    NSA_DECODE_SCRATCH_BYTES is NSA_ERR_WORKSPACE, bad shapes as nsa_decode_attn."""
+    limit = 16 << 20
+    hdr = open(os.path.join(ROOT, "include", "nsa.h")).read()
+    assert re.search(r"#define NSA_DECODE_SCRATCH_BYTES \(16u << 20\)", hdr)
+    S = L.nsa_decode_attn_static
+    lse = ctypes.c_void_p(1)
+    # 32 query heads x 32 new tokens over a 128k cache, dense: 64 splits of fp32 partials
+    q = _t(1, 32, 32, 128)
+    kc = _t(1, 32, 131072, 128)
+    need = ctypes.c_int64(0)
+    assert L.nsa_decode_attn_workspace_size(ctypes.byref(q), ctypes.byref(kc), 131072, 131072 - 32, None,
+                                            ctypes.byref(need)) == 0
+    assert need.value > limit
+    assert S(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(kc), 131072, 131072 - 32, None,
+             ctypes.byref(_t(1, 32, 32, 128)), lse, None) == -5
+    # shape and argument errors come first, as in nsa_decode_attn
+    assert S(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(kc), 131073, 0, None,
+             ctypes.byref(_t(1, 32, 32, 128)), lse, None) == -2
+    assert S(ctypes.byref(q), ctypes.byref(kc), ctypes.byref(kc), 131072, 131072 - 32, None,
+             ctypes.byref(_t(1, 32, 32, 128)), None, None) == -1
+    assert S(ctypes.byref(q), ctypes.byref(_t(1, 32, 131072, 128, N.NSA_F32)), ctypes.byref(kc), 131072, 0,
+             None, ctypes.byref(_t(1, 32, 32, 128)), lse, None) == -3

@@ -20,6 +20,8 @@ from .nsa import (  # noqa: F401
     nsa_block_sparse_attn_bwd,
     nsa_curve_order,
     nsa_decode_attn,
+    nsa_decode_attn_static,
+    nsa_decode_attn_workspace_size,
     nsa_decode_pool_update,
     nsa_decode_select,
     nsa_permute_tokens,

@@ -25,8 +25,33 @@
 #include <algorithm>
 #include <float.h>
 #include <math.h>
+#include <mutex>
+#include <vector>
 
 namespace nsa {
+
+// Split partials of the allocation-free decode call (nsa_decode_attn_static):
+// one copy per GPU, held while the process runs. Host code must never pass
+// this name to a kernel (on the host it is only a stand-in); it uses the
+// device address that decode_scratch() looks up.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+    static std::mutex mu;
+    static std::vector<void*> addr;  // per device ordinal
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((size_t)dev >= addr.size()) addr.resize((size_t)dev + 1, nullptr);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 namespace {
 

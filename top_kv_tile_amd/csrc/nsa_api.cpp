@@ -1474,6 +1474,24 @@ int nsa_decode_attn(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa_te
     return e == hipSuccess ? NSA_OK : hip_fail(e);
 }
 
+int nsa_decode_attn_static(const nsa_tensor* q, const nsa_tensor* k_cache, const nsa_tensor* v_cache,
+                           int32_t length, int32_t q_pos0, const nsa_selection* sel, nsa_tensor* out, float* lse,
+                           void* stream) {
+    nsa::AttnArgs a;
+    int st = decode_attn_config(q, k_cache, v_cache, out, length, q_pos0, sel, a);
+    if (st != NSA_OK) return st;
+    if (numel(q) > 0 && !lse) return NSA_ERR_NULL_ARG;
+    if ((int64_t)a.B * a.Hq * a.NQ == 0) return NSA_OK;
+    const size_t need = decode_attn_workspace(a);
+    if (need > nsa::kDecodeScratchBytes) return NSA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0) {
+        const hipError_t e = nsa::decode_scratch(&ws);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return nsa_decode_attn(q, k_cache, v_cache, length, q_pos0, sel, out, lse, ws, need, stream);
+}
+
 int nsa_stage_timing_begin(void) {
     StageTiming& t = t_stages;
     for (hipEvent_t ev : t.marks) (void)hipEventDestroy(ev);

@@ -93,6 +93,10 @@ hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_combine(const AttnArgs& a, int bf16, hipStream_t stream);
 // General path (fp32 or bf16 inputs, any block sizes, D in {64, 128}).
 hipError_t launch_attn_simt(const AttnArgs& a, int bf16, hipStream_t stream);
+// Device address of the library's static split-partial buffer on the current
+// device (kDecodeScratchBytes bytes, 256-byte aligned), looked up once per device.
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+hipError_t decode_scratch(void** ptr);
 
 // ---- attention gradients ---------------------------------------------------
 

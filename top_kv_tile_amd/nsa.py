@@ -24,7 +24,7 @@ __all__ = [
     "nsa_pool_blocks", "nsa_score_blocks", "nsa_status_string", "Plan", "nsa_plan_create",
     "nsa_select_planned", "nsa_schedule", "nsa_radial_blocks", "nsa_selection_density", "nsa_curve_order",
     "nsa_permute_tokens", "NSA_CURVE_MORTON", "NSA_CURVE_HILBERT", "nsa_decode_pool_update", "nsa_decode_select",
-    "nsa_decode_attn", "nsa_plan_cache_config", "nsa_plan_cache_clear",
+    "nsa_decode_attn", "nsa_decode_attn_static", "nsa_decode_attn_workspace_size", "nsa_plan_cache_config", "nsa_plan_cache_clear",
     "nsa_plan_cache_stats", "nsa_stage_timing_begin", "nsa_stage_timing_end", "LIB_PATH", "EXPORTS",
 ]
 
@@ -35,7 +35,7 @@ EXPORTS = ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_attn_
            "nsa_plan_destroy", "nsa_schedule", "nsa_radial_sizes", "nsa_radial_blocks", "nsa_selection_density",
            "nsa_curve_order", "nsa_permute_tokens", "nsa_decode_pool_update", "nsa_decode_select_sizes",
            "nsa_decode_select", "nsa_decode_attn", "nsa_decode_attn_workspace_size", "nsa_plan_cache_config",
-           "nsa_plan_cache_clear", "nsa_plan_cache_stats", "nsa_stage_timing_begin",
+           "nsa_plan_cache_clear", "nsa_plan_cache_stats", "nsa_decode_attn_static", "nsa_stage_timing_begin",
            "nsa_stage_timing_end")
 
 NSA_OK, NSA_DENSE = 0, 1
@@ -134,6 +134,8 @@ def lib() -> ctypes.CDLL:
                                       ctypes.c_void_p]
         L.nsa_decode_attn_workspace_size.argtypes = [P(_Tensor), P(_Tensor), ctypes.c_int32, ctypes.c_int32,
                                                      P(_Selection), P(ctypes.c_int64)]
+        L.nsa_decode_attn_static.argtypes = [P(_Tensor), P(_Tensor), P(_Tensor), ctypes.c_int32, ctypes.c_int32,
+                                             P(_Selection), P(_Tensor), ctypes.c_void_p, ctypes.c_void_p]
         L.nsa_stage_timing_begin.argtypes = []
         L.nsa_stage_timing_end.argtypes = [ctypes.c_void_p, ctypes.c_int32, P(ctypes.c_int32)]
         L.nsa_status_string.argtypes = [ctypes.c_int]
@@ -145,7 +147,7 @@ def lib() -> ctypes.CDLL:
                      "nsa_radial_blocks", "nsa_selection_density", "nsa_curve_order", "nsa_permute_tokens",
                      "nsa_decode_pool_update", "nsa_decode_select_sizes", "nsa_decode_select", "nsa_decode_attn",
                      "nsa_decode_attn_workspace_size", "nsa_plan_cache_config", "nsa_plan_cache_stats",
-                     "nsa_stage_timing_begin", "nsa_stage_timing_end"):
+                     "nsa_decode_attn_static", "nsa_stage_timing_begin", "nsa_stage_timing_end"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -536,6 +538,32 @@ def nsa_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
                                  ctypes.c_void_p(workspace.data_ptr()),
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
            "nsa_decode_attn")
+    return out, lse
+
+
+def nsa_decode_attn_workspace_size(q: torch.Tensor, k_cache: torch.Tensor, length: int, q_pos0: int,
+                                   selection: Selection | None) -> int:
+    """Bytes of split-partial workspace nsa_decode_attn needs for this request."""
+    csel = ctypes.byref(selection._c()) if selection is not None else None
+    need = ctypes.c_int64(0)
+    _check(lib().nsa_decode_attn_workspace_size(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k_cache)),
+                                                int(length), int(q_pos0), csel, ctypes.byref(need)),
+           "nsa_decode_attn_workspace_size")
+    return need.value
+
+
+def nsa_decode_attn_static(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, length: int,
+                           q_pos0: int, selection: Selection | None, out: torch.Tensor, lse: torch.Tensor,
+                           stream=None):
+    """nsa_decode_attn with the library's static scratch instead of a workspace.
+
+    Allocates nothing: the caller passes ``out`` and ``lse``; returns them."""
+    csel = ctypes.byref(selection._c()) if selection is not None else None
+    _check(lib().nsa_decode_attn_static(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k_cache)),
+                                        ctypes.byref(_tensor(v_cache)), int(length), int(q_pos0), csel,
+                                        ctypes.byref(_tensor(out)), ctypes.c_void_p(lse.data_ptr()),
+                                        _stream(stream)),
+           "nsa_decode_attn_static")
     return out, lse
 
 

@@ -261,7 +261,7 @@ def measured_peaks(reps: int = 10) -> dict:
 PEAK_FP32_TFLOPS = 157.3     # MI355X dense fp32 (matrix and vector)
 
 
-def stage_timing(plan, q, k, ws, sel: tkt.Selection, w: synth.Workload, spec: tkt.SparseSpec,
+def stage_timing(plan, plan_dev, q, k, ws, sel: tkt.Selection, w: synth.Workload, spec: tkt.SparseSpec,
                  calls: int = 20) -> dict:
     """Device time of every selection stage, from the library's stage events,
     over `calls` planned selections (run after the timed steps, same inputs),
@@ -272,11 +272,11 @@ def stage_timing(plan, q, k, ws, sel: tkt.Selection, w: synth.Workload, spec: tk
     Reports p10 / p50 / p90 in ms, GB/s and fractions at the published peaks."""
     stream = torch.cuda.current_stream()
     for _ in range(2):
-        tkt.nsa_select_planned(plan, q, k, workspace=ws)
+        tkt.nsa_select_planned(plan, q, k, workspace=ws, plan_dev=plan_dev)
     torch.cuda.synchronize()
     tkt.nsa_stage_timing_begin()
     for _ in range(calls):
-        tkt.nsa_select_planned(plan, q, k, workspace=ws)
+        tkt.nsa_select_planned(plan, q, k, workspace=ws, plan_dev=plan_dev)
     recs = tkt.nsa_stage_timing_end()
     per_call = len(recs) // calls
     if per_call * calls != len(recs):
@@ -478,6 +478,7 @@ def main():
     # The plan depends on geometry, spec and masks only: built once and kept on
     # the device, as the selection page caches it across the steps of a run.
     plan = tkt.nsa_plan_create(q, k, spec, inp.pins, inp.drops)
+    plan_dev = plan.upload(dev)
     sizes = plan.sizes()
     ws = torch.empty(sizes.workspace_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
@@ -487,7 +488,7 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        sel = tkt.nsa_select_planned(plan, q, k, workspace=ws)
+        sel = tkt.nsa_select_planned(plan, q, k, workspace=ws, plan_dev=plan_dev)
         if ev is not None:
             ev[1].record(stream)
         tkt.nsa_block_sparse_attn(q, k, v, sel, w.causal, out=out, lse=lse)
@@ -560,7 +561,7 @@ def main():
                    "step_ms_events": step_pct, "attn_ms_events": attn_pct},
     }
     log("[bench] per-stage selection timing")
-    res["stages"]["select_stages"] = stage_timing(plan, q, k, ws, sel, w, spec)
+    res["stages"]["select_stages"] = stage_timing(plan, plan_dev, q, k, ws, sel, w, spec)
     if not args.no_peaks:
         peaks = measured_peaks()
         res["measured_peaks"] = peaks

@@ -174,19 +174,31 @@ int nsa_plan_create(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* sp
 /* Host only. The sizes of the planned selection (as nsa_select_sizes). */
 int nsa_plan_sizes(const nsa_plan* plan, nsa_sizes* out, int32_t* row_ptr_host);
 
+/* Host only. Bytes of the plan's device image (its row offsets and bit-packed
+ * pin / drop words): the size of the buffer nsa_plan_upload fills. */
+int nsa_plan_device_bytes(const nsa_plan* plan, int64_t* bytes);
+
+/* Copies the plan's device image into plan_dev, a caller-owned device buffer
+ * of at least nsa_plan_device_bytes bytes, 256-byte aligned, enqueued on
+ * `stream` through a pinned host staging slot of the library (no device
+ * allocation, no synchronisation). The image stays valid while the caller
+ * keeps the buffer; it does not depend on tensor data. Errors: NULL_ARG,
+ * WORKSPACE (plan_dev NULL, misaligned or too small), HIP. */
+int nsa_plan_upload(const nsa_plan* plan, void* plan_dev, size_t bytes, void* stream);
+
 /* nsa_select with a prebuilt plan: q and k must have the plan's shapes and
  * dtype (BAD_SHAPE / BAD_DTYPE otherwise). Result, outputs, workspace and
- * errors as nsa_select with the plan's spec, pins and drops. The first call
- * on a device allocates device memory for the plan's row_ptr and mask words
- * and copies them there synchronously (held until nsa_plan_destroy); later
- * calls on that device copy nothing (the selection kernels write out->row_ptr
- * from the device copy). Calls on another device upload per call, as
- * nsa_select does. */
-int nsa_select_planned(const nsa_plan* plan, const nsa_tensor* q, const nsa_tensor* k,
+ * errors as nsa_select with the plan's spec, pins and drops. plan_dev: the
+ * plan's device image written by nsa_plan_upload (on this or an earlier
+ * point of the same stream), read by the selection kernels, which copy its
+ * row offsets into out->row_ptr; nothing is then copied from the host. NULL:
+ * the image is uploaded into the workspace by this call, as nsa_select does.
+ * WORKSPACE also when plan_dev is not 256-byte aligned. */
+int nsa_select_planned(const nsa_plan* plan, const void* plan_dev, const nsa_tensor* q, const nsa_tensor* k,
                        nsa_selection* out, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Frees a plan (NULL is allowed). If it has a device copy, waits for the work
- * queued on that device first (a planned selection may still be reading it). */
+/* Frees a plan (NULL is allowed). Host memory only: device buffers holding
+ * its image are the caller's. */
 void nsa_plan_destroy(nsa_plan* plan);
 
 /* ---- Plan cache of nsa_select and nsa_select_sizes ---------------------------

@@ -85,10 +85,26 @@ def test_plan_sizes_equal_select_sizes(L, B, Hq, Hkv, S, bq, bkv, budget, shared
     assert np.array_equal(rp_a, rp_b)
     # shape mismatch is rejected before anything is enqueued
     sel = N._Selection(keep=1, row_ptr=1, col_idx=1, col_capacity=1 << 40)
-    assert L.nsa_select_planned(h, ctypes.byref(_t(B, Hq, S + 1, 128)), ctypes.byref(k), ctypes.byref(sel), None,
-                                0, None) == -2
-    assert L.nsa_select_planned(h, ctypes.byref(_t(B, Hq, S, 128, N.NSA_F32)), ctypes.byref(k), ctypes.byref(sel),
-                                None, 0, None) == -3
+    assert L.nsa_select_planned(h, None, ctypes.byref(_t(B, Hq, S + 1, 128)), ctypes.byref(k), ctypes.byref(sel),
+                                None, 0, None) == -2
+    assert L.nsa_select_planned(h, None, ctypes.byref(_t(B, Hq, S, 128, N.NSA_F32)), ctypes.byref(k),
+                                ctypes.byref(sel), None, 0, None) == -3
+    # the device image: size from the plan (row offsets + bit-packed masks, 256-byte sections),
+    # a missing, misaligned or short buffer is rejected before anything is enqueued
+    n = ctypes.c_int64(-1)
+    assert L.nsa_plan_device_bytes(h, ctypes.byref(n)) == 0
+    sec = lambda x: -(-x // 256) * 256  # noqa: E731
+    nkw = -(-nk // 64)
+    want = (sec(4 * (B * H * nq + 1)) + sec(8 * int(np.prod(pshape)) * nq * nkw)
+            + sec(8 * int(np.prod(dshape)) * nq * nkw))
+    assert n.value == want
+    assert L.nsa_plan_upload(h, None, n.value, None) == -5
+    assert L.nsa_plan_upload(h, ctypes.c_void_p(4096 + 16), n.value, None) == -5
+    assert L.nsa_plan_upload(h, ctypes.c_void_p(4096), n.value - 1, None) == -5
+    assert L.nsa_plan_upload(None, ctypes.c_void_p(4096), n.value, None) == -1
+    assert L.nsa_plan_device_bytes(h, None) == -1
+    assert L.nsa_select_planned(h, ctypes.c_void_p(4096 + 8), ctypes.byref(_t(B, Hq, S, 128)), ctypes.byref(k),
+                                ctypes.byref(sel), None, 0, None) == -5
     L.nsa_plan_destroy(h)
     L.nsa_plan_destroy(None)
 

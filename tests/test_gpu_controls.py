@@ -56,14 +56,17 @@ def test_planned_selection_equals_select():
     spec = tkt.SparseSpec(budget=0.3)
     q0, k0, _, _ = _inputs(B, Hq, Hkv, S, D, seed=1)
     plan = tkt.nsa_plan_create(to_dev(q0), to_dev(k0), spec, pins, drops)
+    img = plan.upload(torch.device("cuda:0"))  # the plan's device image, uploaded once
     for seed in (2, 3, 4):  # same shapes, new values: the plan is reused
         q, k, _, _ = _inputs(B, Hq, Hkv, S, D, seed=seed)
         qd, kd = to_dev(q), to_dev(k)
         a = tkt.nsa_select(qd, kd, spec, pins, drops)
-        b = tkt.nsa_select_planned(plan, qd, kd)
+        b = tkt.nsa_select_planned(plan, qd, kd)               # image uploaded by the call
+        c = tkt.nsa_select_planned(plan, qd, kd, plan_dev=img)  # image from the caller's buffer
         torch.cuda.synchronize()
-        assert torch.equal(a.keep, b.keep) and torch.equal(a.row_ptr, b.row_ptr)
-        assert torch.equal(a.col_idx, b.col_idx)
+        for x in (b, c):
+            assert torch.equal(a.keep, x.keep) and torch.equal(a.row_ptr, x.row_ptr)
+            assert torch.equal(a.col_idx, x.col_idx)
         assert abs(b.density() - float(b.keep.float().mean().item())) < 1e-12
     dense_plan = tkt.nsa_plan_create(to_dev(q0), to_dev(k0), tkt.SparseSpec(budget=1.0))
     assert tkt.nsa_select_planned(dense_plan, to_dev(q0), to_dev(k0)) is None

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import top_kv_tile_amd as tkt
-from parity_util import check_attention, run_case, say, to_dev
+from parity_util import check_attention, check_selection, run_case, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -188,20 +188,23 @@ def test_few_long_rows():
     say(f"  {rep}")
 
 
-@pytest.mark.parametrize("S,bq,bkv", [(16384, 256, 16), (8192, 128, 32), (8192, 256, 16)])
-def test_exact_ties_take_lowest_index(S, bq, bkv):
+@pytest.mark.parametrize("S,bq,bkv,Hq", [(16384, 256, 16, 2), (8192, 128, 32, 2), (8192, 256, 16, 2),
+                                         # more than 1024 rows: one wavefront per row
+                                         (8192, 64, 16, 16), (32768, 256, 16, 16), (4096, 32, 64, 24),
+                                         (6000, 64, 24, 12)])
+def test_exact_ties_take_lowest_index(S, bq, bkv, Hq):
     """Every kv tile repeats one of three key vectors, so pooled keys are exact
     copies and a row's scores fall into three groups of exactly equal values,
     well apart from each other. The boundary group must be cut at the lowest
     kv indices (score descending, index ascending): the expected keep is built
     from float64 group scores and compared bit for bit, pins and drops
     included."""
-    say(f"exact ties S={S} bq={bq} bkv={bkv}")
-    B, Hq, Hkv, D = 1, 2, 1, 64
+    say(f"exact ties S={S} bq={bq} bkv={bkv} Hq={Hq}")
+    B, Hkv, D = 1, 1, 64
     g = torch.Generator().manual_seed(S + bq)
     q = torch.randn(B, Hq, S, D, generator=g).to(torch.bfloat16)
     V = torch.randn(3, D, generator=g).to(torch.bfloat16)
-    nq, nk = S // bq, S // bkv
+    nq, nk = -(-S // bq), -(-S // bkv)
     tile_of = torch.arange(S) // bkv
     k = V[tile_of % 3].reshape(1, 1, S, D).contiguous()
     rng = np.random.default_rng(S)
@@ -213,10 +216,14 @@ def test_exact_ties_take_lowest_index(S, bq, bkv):
     torch.cuda.synchronize()
     got = sel.keep.cpu().numpy() != 0
     pq = oracle.pool_blocks(q, bq).double().numpy()                    # (B, Hq, NQ, D)
+    # the last kv tile may be ragged: its pooled key is still one of the three vectors
     gs = pq @ V.double().numpy().T                                     # (B, Hq, NQ, 3) group scores
     gap = np.sort(gs, -1)
-    # the groups are far apart next to fp32 rounding of a pooled score (~(bq + D) 2^-24 relative)
-    assert np.all(np.diff(gap, axis=-1) > 1e-4 * np.abs(gap).max())
+    # Rows whose three group scores are far apart next to fp32 rounding of a
+    # pooled score (~(bq + D) 2^-24 relative) have one exact answer; the rare
+    # rows with two close groups are held to the selection rules only.
+    exact = np.all(np.diff(gap, axis=-1) > 1e-4 * np.abs(gap).max(axis=-1, keepdims=True), axis=-1)
+    assert exact.mean() > 0.9
     plan = oracle.selection_plan(nq, nk, bq, bkv, budget, B, Hq, pins, drops)
     want = plan["must"] & ~plan["forbidden"]
     grp = np.arange(nk) % 3
@@ -225,9 +232,38 @@ def test_exact_ties_take_lowest_index(S, bq, bkv):
             cand = np.nonzero(plan["candidates"][0, h, i])[0]
             order = sorted(cand, key=lambda j: (-gs[0, h, i, grp[j]], j))
             want[0, h, i, order[:int(plan["k"][0, h, i])]] = True
-    assert np.array_equal(got, want)
-    r_ptr, r_col = oracle.keep_to_csr(want.astype(np.int8))
+    assert np.array_equal(got[exact], want[exact])
+    must = plan["must"] & ~plan["forbidden"]
+    assert np.all(got[must]) and not np.any(got & plan["forbidden"])
+    assert np.array_equal(got.sum(-1), want.sum(-1))
+    r_ptr, r_col = oracle.keep_to_csr(got.astype(np.int8))
     assert np.array_equal(sel.row_ptr.cpu().numpy(), r_ptr) and np.array_equal(sel.col_idx.cpu().numpy(), r_col)
+    assert np.array_equal(r_ptr, oracle.keep_to_csr(want.astype(np.int8))[0])
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,bq,bkv,budget", [
+    (2, 16, 4, 8192, 128, 64, 0.25),     # 128 kv tiles
+    (1, 24, 8, 16384, 128, 16, 0.05),    # 1024 kv tiles
+    (1, 16, 4, 32768, 256, 16, 0.05),    # 2048 kv tiles
+    (1, 16, 16, 8000, 64, 64, 0.30),     # 125 kv tiles (not a multiple of 4)
+    (1, 12, 3, 6100, 64, 16, 0.10),      # 382 kv tiles, ragged tail
+])
+def test_many_rows_pins_drops(B, Hq, Hkv, S, bq, bkv, budget):
+    """More than 1024 selection rows (one wavefront per row) against the oracle,
+    with per-batch pins and per-head drops covering diagonal tiles too."""
+    say(f"many rows B={B} Hq={Hq} S={S} bq={bq} bkv={bkv}")
+    D = 64
+    q, k, _ = _qkv(B, Hq, Hkv, S, D, seed=S + Hq, dtype=torch.bfloat16)
+    nq, nk = -(-S // bq), -(-S // bkv)
+    rng = np.random.default_rng(S)
+    pins = (rng.random((B, 1, nq, nk)) < 0.02).astype(np.int8)
+    drops = (rng.random((1, Hq, nq, nk)) < 0.03).astype(np.int8)
+    spec = tkt.SparseSpec(budget=budget, block_q=bq, block_kv=bkv)
+    ref = oracle.select_blocks(q, k, budget, bq, bkv, False, False, pins, drops)
+    sel = tkt.nsa_select(to_dev(q), to_dev(k), spec, pins, drops)
+    torch.cuda.synchronize()
+    _, nflag = check_selection(sel, ref, "many rows")
+    say(f"  rows {B * Hq * nq}, near-tie rows {nflag}, nnz {sel.nnz}")
 
 
 def test_widest_row_nk4096():

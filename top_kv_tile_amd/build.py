@@ -64,25 +64,36 @@ def _finish(proc, what, verbose):
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source (in parallel) and link top_kv_tile_amd/libnsa.so; returns the path."""
+# Host-side AddressSanitizer build of the C ABI layer (nsa_api.cpp): the
+# host pass only (-Xarch_host), the device code unchanged. Load it into a
+# process with the compiler's ASan runtime preloaded.
+ASAN_LIB = os.path.join(HERE, "libnsa_asan.so")
+ASAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(verbose: bool = False, asan: bool = False) -> str:
+    """Compile every source (in parallel) and link top_kv_tile_amd/libnsa.so
+    (libnsa_asan.so with asan=True); returns the path."""
     include = ["-I", os.path.join(ROOT, "include")]
+    lib = ASAN_LIB if asan else LIB
     with tempfile.TemporaryDirectory(prefix="_build_", dir=HERE) as tmpdir:
         objs, procs = [], []
         for src in SOURCES:
             obj = os.path.join(tmpdir, src + ".o")
             flags = PER_SOURCE.get(src, VGPR_FORM)
-            procs.append((src, _run([hipcc(), *FLAGS, *flags, *include, "-c", "-o", obj,
+            extra = ASAN_HOST if (asan and src.endswith(".cpp")) else []
+            procs.append((src, _run([hipcc(), *FLAGS, *flags, *extra, *include, "-c", "-o", obj,
                                      os.path.join(CSRC, src)], verbose)))
             objs.append(obj)
         for src, proc in procs:
             _finish(proc, src, verbose)
-        tmp = LIB + ".tmp"
-        _finish(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose),
+        tmp = lib + ".tmp"
+        link_extra = ["-Xarch_host", "-fsanitize=address"] if asan else []
+        _finish(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *link_extra, "-o", tmp, *objs], verbose),
                 "the link", verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, asan="--asan" in sys.argv[1:]))

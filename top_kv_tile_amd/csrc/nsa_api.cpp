@@ -396,18 +396,17 @@ int score_and_topk(const Plan& p, const nsa_spec* spec, const void* qh, const fl
                    const uint64_t* drop_words, const int32_t* row_src, int32_t row_step = 0, int q_rows = 0,
                    bool inline_masks = false);
 
-// Enqueues the selection of a built plan (row_ptr present) for tensors q, k
-// whose geometry the plan was built from.
-// Device-resident copy of a plan's row_ptr and mask words (a plan handle keeps
-// one on the device of its first planned selection).
+// A plan's row offsets and mask words already in device memory (the image
+// nsa_plan_upload writes into a caller buffer).
 struct PlanDevice {
-    int dev = -1;
-    void* buf = nullptr;
     int32_t* row_ptr = nullptr;
     uint64_t* pin_words = nullptr;
     uint64_t* drop_words = nullptr;
 };
 
+// Enqueues the selection of a built plan (row_ptr present) for tensors q, k
+// whose geometry the plan was built from; pd: the plan's device image, or null
+// (then it is uploaded into the workspace).
 int run_select(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, const Plan& p, nsa_selection* out,
                void* workspace, size_t workspace_bytes, hipStream_t stream, const PlanDevice* pd = nullptr) {
     const Geo& g = p.g;
@@ -758,24 +757,12 @@ uint64_t hilbert_key(const int64_t* c, int n, int p) {
 }  // namespace
 
 // Opaque host-side selection plan: the geometry, the packed pin / drop masks
-// and the row offsets, built once and reused by nsa_select_planned.
+// and the row offsets, built once and reused by nsa_select_planned. It holds
+// host memory only; its device image lives in a buffer of the caller.
 struct nsa_plan {
     nsa_spec spec;
     nsa_tensor qshape, kshape;  // shapes and dtype only
     Plan p;
-    // row_ptr and mask words on the device of the first planned selection,
-    // uploaded once (later selections on that device copy nothing from the host)
-    mutable std::mutex mu;
-    mutable PlanDevice d;
-    ~nsa_plan() {
-        if (!d.buf) return;
-        int cur = 0;
-        const bool restore = hipGetDevice(&cur) == hipSuccess && cur != d.dev;
-        if (restore) (void)hipSetDevice(d.dev);
-        (void)hipDeviceSynchronize();  // a planned selection may still read the copy
-        (void)hipFree(d.buf);
-        if (restore) (void)hipSetDevice(cur);
-    }
 };
 
 namespace {
@@ -1101,8 +1088,45 @@ int nsa_plan_sizes(const nsa_plan* plan, nsa_sizes* out, int32_t* row_ptr_host) 
     return NSA_OK;
 }
 
-int nsa_select_planned(const nsa_plan* plan, const nsa_tensor* q, const nsa_tensor* k, nsa_selection* out,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// Device image of a plan: row offsets, then pin words, then drop words, each
+// section 256-byte aligned.
+struct PlanImage {
+    size_t rb, pb, db;
+    size_t total() const { return rb + pb + db; }
+};
+PlanImage plan_image(const Plan& p) {
+    return {align256(p.row_ptr.size() * sizeof(int32_t)), align256(p.has_pins ? p.pin_words.size() * 8 : 0),
+            align256(p.has_drops ? p.drop_words.size() * 8 : 0)};
+}
+}  // namespace
+
+int nsa_plan_device_bytes(const nsa_plan* plan, int64_t* bytes) {
+    if (!plan || !bytes) return NSA_ERR_NULL_ARG;
+    *bytes = (int64_t)plan_image(plan->p).total();
+    return NSA_OK;
+}
+
+int nsa_plan_upload(const nsa_plan* plan, void* plan_dev, size_t bytes, void* stream) {
+    try {
+        if (!plan) return NSA_ERR_NULL_ARG;
+        const Plan& p = plan->p;
+        const PlanImage im = plan_image(p);
+        if (!plan_dev || ((uintptr_t)plan_dev & 255) || bytes < im.total()) return NSA_ERR_WORKSPACE;
+        char* c = (char*)plan_dev;
+        void* dst[3] = {c, c + im.rb, c + im.rb + im.pb};
+        const void* src[3] = {p.row_ptr.data(), p.pin_words.data(), p.drop_words.data()};
+        size_t n[3] = {p.row_ptr.size() * sizeof(int32_t), p.has_pins ? p.pin_words.size() * 8 : 0,
+                       p.has_drops ? p.drop_words.size() * 8 : 0};
+        const hipError_t e = upload(3, dst, src, n, (hipStream_t)stream);
+        return e == hipSuccess ? NSA_OK : hip_fail(e);
+    } catch (...) {
+        return NSA_ERR_UNSUPPORTED;
+    }
+}
+
+int nsa_select_planned(const nsa_plan* plan, const void* plan_dev, const nsa_tensor* q, const nsa_tensor* k,
+                       nsa_selection* out, void* workspace, size_t workspace_bytes, void* stream) {
     try {
         if (!plan || !out) return NSA_ERR_NULL_ARG;
         int st;
@@ -1112,38 +1136,18 @@ int nsa_select_planned(const nsa_plan* plan, const nsa_tensor* q, const nsa_tens
         if (q->dtype != pq.dtype || k->dtype != pk.dtype) return NSA_ERR_BAD_DTYPE;
         if (q->B != pq.B || q->H != pq.H || q->S != pq.S || q->D != pq.D) return NSA_ERR_BAD_SHAPE;
         if (k->B != pk.B || k->H != pk.H || k->S != pk.S || k->D != pk.D) return NSA_ERR_BAD_SHAPE;
+        if (plan_dev && ((uintptr_t)plan_dev & 255)) return NSA_ERR_WORKSPACE;
         const Plan& p = plan->p;
-        const PlanDevice* pd = nullptr;
-        if (!(p.dense && !plan->spec.force) && p.g.rows > 0) {
-            int dev = 0;
-            hipError_t e = hipGetDevice(&dev);
-            if (e != hipSuccess) return hip_fail(e);
-            std::lock_guard<std::mutex> lock(plan->mu);
-            if (plan->d.dev < 0) {  // first planned selection: upload the plan to this device
-                const size_t rb = align256(p.row_ptr.size() * sizeof(int32_t));
-                const size_t pb = align256(p.has_pins ? p.pin_words.size() * 8 : 0);
-                const size_t db = align256(p.has_drops ? p.drop_words.size() * 8 : 0);
-                void* buf = nullptr;
-                if ((e = hipMalloc(&buf, rb + pb + db)) != hipSuccess) return hip_fail(e);
-                char* c = (char*)buf;
-                e = hipMemcpy(c, p.row_ptr.data(), p.row_ptr.size() * sizeof(int32_t), hipMemcpyHostToDevice);
-                if (e == hipSuccess && pb)
-                    e = hipMemcpy(c + rb, p.pin_words.data(), p.pin_words.size() * 8, hipMemcpyHostToDevice);
-                if (e == hipSuccess && db)
-                    e = hipMemcpy(c + rb + pb, p.drop_words.data(), p.drop_words.size() * 8, hipMemcpyHostToDevice);
-                if (e != hipSuccess) {
-                    (void)hipFree(buf);
-                    return hip_fail(e);
-                }
-                plan->d.dev = dev;
-                plan->d.buf = buf;
-                plan->d.row_ptr = (int32_t*)c;
-                plan->d.pin_words = pb ? (uint64_t*)(c + rb) : nullptr;
-                plan->d.drop_words = db ? (uint64_t*)(c + rb + pb) : nullptr;
-            }
-            if (plan->d.dev == dev) pd = &plan->d;  // on another device: the host upload path
+        PlanDevice pd;
+        if (plan_dev) {  // the plan's image, uploaded by nsa_plan_upload: nothing is copied here
+            const PlanImage im = plan_image(p);
+            const char* c = (const char*)plan_dev;
+            pd.row_ptr = (int32_t*)c;
+            pd.pin_words = im.pb ? (uint64_t*)(c + im.rb) : nullptr;
+            pd.drop_words = im.db ? (uint64_t*)(c + im.rb + im.pb) : nullptr;
         }
-        return run_select(q, k, &plan->spec, p, out, workspace, workspace_bytes, (hipStream_t)stream, pd);
+        return run_select(q, k, &plan->spec, p, out, workspace, workspace_bytes, (hipStream_t)stream,
+                          plan_dev ? &pd : nullptr);
     } catch (...) {
         return NSA_ERR_UNSUPPORTED;
     }

@@ -36,7 +36,7 @@ EXPORTS = ("nsa_select_sizes", "nsa_select", "nsa_block_sparse_attn", "nsa_attn_
            "nsa_curve_order", "nsa_permute_tokens", "nsa_decode_pool_update", "nsa_decode_select_sizes",
            "nsa_decode_select", "nsa_decode_attn", "nsa_decode_attn_workspace_size", "nsa_plan_cache_config",
            "nsa_plan_cache_clear", "nsa_plan_cache_stats", "nsa_decode_attn_static", "nsa_stage_timing_begin",
-           "nsa_stage_timing_end")
+           "nsa_stage_timing_end", "nsa_plan_device_bytes", "nsa_plan_upload")
 
 NSA_OK, NSA_DENSE = 0, 1
 NSA_F32, NSA_BF16 = 0, 1
@@ -106,8 +106,10 @@ def lib() -> ctypes.CDLL:
         L.nsa_plan_create.argtypes = [P(_Tensor), P(_Tensor), P(_Spec), P(_Mask), P(_Mask),
                                       P(ctypes.c_void_p)]
         L.nsa_plan_sizes.argtypes = [ctypes.c_void_p, P(_Sizes), ctypes.c_void_p]
-        L.nsa_select_planned.argtypes = [ctypes.c_void_p, P(_Tensor), P(_Tensor), P(_Selection), ctypes.c_void_p,
-                                         ctypes.c_size_t, ctypes.c_void_p]
+        L.nsa_select_planned.argtypes = [ctypes.c_void_p, ctypes.c_void_p, P(_Tensor), P(_Tensor), P(_Selection),
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.nsa_plan_device_bytes.argtypes = [ctypes.c_void_p, P(ctypes.c_int64)]
+        L.nsa_plan_upload.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.nsa_plan_destroy.argtypes = [ctypes.c_void_p]
         L.nsa_plan_destroy.restype = None
         L.nsa_plan_cache_config.argtypes = [ctypes.c_int32]
@@ -147,7 +149,8 @@ def lib() -> ctypes.CDLL:
                      "nsa_radial_blocks", "nsa_selection_density", "nsa_curve_order", "nsa_permute_tokens",
                      "nsa_decode_pool_update", "nsa_decode_select_sizes", "nsa_decode_select", "nsa_decode_attn",
                      "nsa_decode_attn_workspace_size", "nsa_plan_cache_config", "nsa_plan_cache_stats",
-                     "nsa_decode_attn_static", "nsa_stage_timing_begin", "nsa_stage_timing_end"):
+                     "nsa_decode_attn_static", "nsa_stage_timing_begin", "nsa_stage_timing_end",
+                     "nsa_plan_device_bytes", "nsa_plan_upload"):
             getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -370,6 +373,18 @@ class Plan:
         _check(lib().nsa_plan_sizes(self._h, ctypes.byref(out), None), "nsa_plan_sizes")
         return Sizes(out.NQ, out.NK, out.sel_heads, bool(out.dense), out.rows, out.nnz, out.workspace_bytes)
 
+    def device_bytes(self) -> int:
+        n = ctypes.c_int64(0)
+        _check(lib().nsa_plan_device_bytes(self._h, ctypes.byref(n)), "nsa_plan_device_bytes")
+        return n.value
+
+    def upload(self, device, stream=None) -> torch.Tensor:
+        """The plan's device image in a new uint8 tensor on `device` (nsa_plan_upload)."""
+        img = torch.empty(max(self.device_bytes(), 1), dtype=torch.uint8, device=device)
+        _check(lib().nsa_plan_upload(self._h, ctypes.c_void_p(img.data_ptr()), img.numel(), _stream(stream)),
+               "nsa_plan_upload")
+        return img
+
     def __del__(self):
         h, self._h = getattr(self, "_h", None), None
         if h is not None and h.value and _LIB is not None:
@@ -387,8 +402,10 @@ def nsa_plan_create(q: torch.Tensor, k: torch.Tensor, spec: SparseSpec = SparseS
 
 
 def nsa_select_planned(plan: Plan, q: torch.Tensor, k: torch.Tensor, stream=None,
-                       workspace: torch.Tensor | None = None):
-    """nsa_select with a prebuilt plan; returns a Selection, or None when the plan is dense."""
+                       workspace: torch.Tensor | None = None, plan_dev: torch.Tensor | None = None):
+    """nsa_select with a prebuilt plan; returns a Selection, or None when the plan is dense.
+
+    plan_dev: the plan's device image from Plan.upload (None: uploaded by this call)."""
     sizes = plan.sizes()
     if sizes.dense:
         return None
@@ -401,7 +418,8 @@ def nsa_select_planned(plan: Plan, q: torch.Tensor, k: torch.Tensor, stream=None
     spec = plan.spec
     sel = Selection(keep, row_ptr, col_idx, spec.block_q, spec.block_kv, spec.budget, q.shape[2], k.shape[2])
     csel = sel._c()
-    st = _check(lib().nsa_select_planned(plan._h, ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)),
+    img = ctypes.c_void_p(plan_dev.data_ptr()) if plan_dev is not None else None
+    st = _check(lib().nsa_select_planned(plan._h, img, ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)),
                                          ctypes.byref(csel), ctypes.c_void_p(workspace.data_ptr()),
                                          workspace.numel(), _stream(stream)), "nsa_select_planned")
     return None if st == NSA_DENSE else sel

@@ -164,13 +164,43 @@ def test_growing_logits_move_the_softmax_reference(causal):
     say(f"  {rep}")
 
 
-def test_all_tied_scores_pick_lowest_index():
-    say("all ties")
-    B, H, S, D = 1, 2, 2048, 128
+@pytest.mark.parametrize("H,S", [(2, 2048), (16, 16384)])
+def test_all_tied_scores_pick_lowest_index(H, S):
+    """q = 0: every score is +-0, so each row keeps its k_r lowest-index candidates
+    (the second case has more than 1024 rows: one wavefront per row)."""
+    say(f"all ties H={H} S={S}")
+    B, D = 1, 128
     _, k, v = _qkv(B, H, H, S, D, seed=8, dtype=torch.bfloat16)
     q = torch.zeros(B, H, S, D, dtype=torch.bfloat16)
-    rep = run_case(q, k, v, tkt.SparseSpec(budget=0.3), False, where="ties")
+    rows = None if S <= 2048 else [(0, 0, 0), (0, H - 1, S // 128 - 1), (0, 3, 40)]
+    rep = run_case(q, k, v, tkt.SparseSpec(budget=0.3), False, rows=rows, where="ties")
     say(f"  {rep}")
+
+
+@pytest.mark.parametrize("nk", [256, 2048])
+def test_crowded_threshold_bucket(nk):
+    """Five kv tiles score a thousand times above the rest and the rest spread
+    over +-10%: the first histogram puts every other candidate into its lowest
+    bucket, so the search narrows to that bucket's own value range before
+    cutting. Scores are sums of positive terms (no cancellation), so fp32
+    rounding on either side stays far below the gaps between them."""
+    say(f"crowded bucket nk={nk}")
+    B, Hq, Hkv, D, bq, bkv = 1, 16, 4, 64, 64, 16
+    S = nk * bkv
+    g = torch.Generator().manual_seed(nk)
+    q = torch.randn(B, Hq, S, D, generator=g).abs()
+    base = torch.randn(1, Hkv, 1, D, generator=g).abs() + 0.5
+    f = 0.9 + 0.2 * torch.rand(nk, generator=g)                     # one factor per kv tile
+    f[torch.randperm(nk, generator=g)[:5]] = 1000.0
+    k = base * f.repeat_interleave(bkv)[None, None, :, None]
+    q = q.to(torch.bfloat16)
+    k = k.to(torch.bfloat16)
+    spec = tkt.SparseSpec(budget=0.1, block_q=bq, block_kv=bkv)
+    ref = oracle.select_blocks(q, k, spec.budget, bq, bkv, False, False)
+    sel = tkt.nsa_select(to_dev(q), to_dev(k), spec)
+    torch.cuda.synchronize()
+    _, nflag = check_selection(sel, ref, "crowded")
+    say(f"  rows {B * Hq * (S // bq)}, near-tie rows {nflag}")
 
 
 def test_few_long_rows():

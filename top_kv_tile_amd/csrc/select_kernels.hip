@@ -857,6 +857,312 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(TopkArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- top-k, grouped layout
+//
+// One wavefront per row, for the many-row case with NK <= 256 G and NK a
+// multiple of 4 (every score row then starts 16-byte aligned). Lane L holds
+// the 4 consecutive elements e = 256 x + 4 L + c (c = 0..3) of each group x,
+// read by one 16-byte load, and element e is bit t = 4 x + c of the lane's
+// masks. A group's mask bits of a lane are then one nibble of one 64-bit mask
+// word (word 4 x + L / 16, bits 4 (L % 16) .. + 3), and a group's kept flags
+// leave as one 4-byte store. Index order (the tie break) is group, then lane,
+// then c.
+//
+// Selection of the k_r-th largest candidate (score descending, index
+// ascending), exact:
+//  1. non-candidates are set to -inf; lo / hi over the candidates;
+//  2. one histogram of 256 buckets over [lo, hi] (a monotone map) gives the
+//     bucket b* that holds the k-th largest and the count above it;
+//  3. the elements of b* (few: a bucket holds about c / 256 scores unless
+//     scores crowd) are compacted by ballot into LDS and ranked against each
+//     other, giving the k-th element's value T and index i_T;
+//  4. picked = candidates with score > T, or == T and index <= i_T.
+// If b* holds more than 64 elements the search narrows to that bucket's
+// exact value range and repeats on its elements; a range that collapses to
+// one value is cut in index order.
+
+// Nibble of the bits lo..hi (clipped to 0..3); empty when lo > hi.
+__device__ __forceinline__ uint32_t nibble_range(int lo, int hi) {
+    lo = lo < 0 ? 0 : lo;
+    hi = hi > 3 ? 3 : hi;
+    if (lo > hi) return 0u;
+    return ((2u << hi) - 1u) & ~((1u << lo) - 1u);
+}
+
+// Bucket of x in the map u = x * scale + off, clamped to 0 .. 255 (monotone
+// in x: the fma rounds a monotone function; -inf goes to bucket 0).
+__device__ __forceinline__ uint32_t bucket_of(float x, float scale, float off) {
+    const float u = __builtin_amdgcn_fmed3f(__builtin_fmaf(x, scale, off), 0.0f, 255.0f);
+    return (uint32_t)(int)u & 255u;
+}
+
+// From a 256-bucket histogram (lane L owns buckets 4L .. 4L+3): the bucket b*
+// holding the need-th largest element, the number of elements above it and
+// the number in it. Results are wave-uniform.
+__device__ __forceinline__ void find_bucket(const uint32_t* hist, int need, int lane, int& bstar, int& above,
+                                            int& inside) {
+    const u32x4 hv = *(const u32x4*)(hist + 4 * lane);
+    const int own = (int)(hv[0] + hv[1] + hv[2] + hv[3]);
+    const int incl = wave_prefix_sum(own);
+    int ab = __builtin_amdgcn_readlane(incl, 63) - incl;  // elements in higher lanes' buckets
+    int found = -1, found_above = 0, found_in = 0;
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+        if (found < 0 && ab < need && need <= ab + (int)hv[e]) {
+            found = 4 * lane + e;
+            found_above = ab;
+            found_in = (int)hv[e];
+        }
+        ab += (int)hv[e];
+    }
+    const uint64_t who = __ballot(found >= 0);
+    const int src = who ? __builtin_ctzll(who) : 0;
+    bstar = __builtin_amdgcn_readlane(found, src);
+    above = __builtin_amdgcn_readlane(found_above, src);
+    inside = __builtin_amdgcn_readlane(found_in, src);
+}
+
+// Index (in index order) of the r-th (0-based) element of `m` (bit 4x + c of
+// lane L is element 256 x + 4 L + c); wave-uniform. r must be < popcount.
+template <int G>
+__device__ int kth_index(uint32_t m, int r, int lane) {
+    int res = 0;
+#pragma unroll
+    for (int x = 0; x < G; ++x) {
+        const uint32_t nib = (m >> (4 * x)) & 0xFu;
+        const int cnt = __builtin_popcount(nib);
+        const int incl = wave_prefix_sum(cnt);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (r < total) {  // in this group: the lane whose prefix covers r
+            const int excl = incl - cnt;
+            const bool mine = r >= excl && r < incl;
+            int e = 0;
+            if (mine) {
+                uint32_t q = nib;
+                for (int skip = r - excl; skip > 0; --skip) q &= q - 1u;
+                e = 256 * x + 4 * lane + __builtin_ctz(q);
+            }
+            const uint64_t who = __ballot(mine);
+            res = __builtin_amdgcn_readlane(e, __builtin_ctzll(who));
+            break;
+        }
+        r -= total;
+    }
+    return res;
+}
+
+template <int G>
+__global__ __launch_bounds__(256, 3) void topk_grouped_kernel(TopkArgs a) {
+    constexpr int E = 4 * G;
+    __shared__ uint32_t hist_all[4][256];
+    __shared__ uint2 list_all[4][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i = (int)blockIdx.x * 4 + wave;  // query tile
+    if (i >= a.NQ) return;
+    uint32_t* hist = hist_all[wave];
+    uint2* list = list_all[wave];
+    const int hl = blockIdx.y, b = blockIdx.z;
+    const int h = a.h0 + hl;
+    const int64_t lr = ((int64_t)b * a.nh + hl) * a.NQ + i;  // row of the score chunk
+    const int64_t r = ((int64_t)b * a.Hsel + h) * a.NQ + i;  // row of the selection
+    const float* srow = a.scores + lr * a.NK;
+    const int pbi = a.pb == 1 ? 0 : b, phi = a.ph == 1 ? 0 : h;
+    const int dbi = a.db == 1 ? 0 : b, dhi_ = a.dh == 1 ? 0 : h;
+    const uint32_t* pw =
+        a.pin_words ? (const uint32_t*)(a.pin_words + (((int64_t)pbi * a.ph + phi) * a.NQ + i) * a.NKW) : nullptr;
+    const uint32_t* dw =
+        a.drop_words ? (const uint32_t*)(a.drop_words + (((int64_t)dbi * a.dh + dhi_) * a.NQ + i) * a.NKW) : nullptr;
+    // Diagonal: floor((o + i bq) / bkv) <= j <= ceil((o + (i+1) bq) / bkv) - 1 (o = q_off;
+    // 32-bit: the host keeps o + S + bq below 2^31).
+    const uint32_t qa = (uint32_t)a.q_off + (uint32_t)i * (uint32_t)a.block_q;
+    const int dlo = (int)(qa / (uint32_t)a.block_kv);
+    const int dhi = (int)((qa + (uint32_t)a.block_q + (uint32_t)a.block_kv - 1u) / (uint32_t)a.block_kv) - 1;
+
+    // Every load first (addresses clamped into the row, so none is conditional
+    // and all are in flight together), then the masks.
+    f32x4 v[G];
+    uint32_t pwv[G], dwv[G];
+    const int mw = 2 * (lane >> 4) + ((lane >> 3) & 1);  // the lane's 32-bit half word within a group
+    const int msh = 4 * (lane & 7);
+    const int last_w = 2 * a.NKW - 1;
+#pragma unroll
+    for (int x = 0; x < G; ++x) {
+        v[x] = *(const f32x4*)(srow + min(256 * x + 4 * lane, a.NK - 4));
+        pwv[x] = pw ? pw[min(8 * x + mw, last_w)] : 0u;
+        dwv[x] = dw ? dw[min(8 * x + mw, last_w)] : 0u;
+    }
+    // Non-candidates become -inf (a bitfield select on the candidate bit spread
+    // to a full-word mask), so later passes need no masks.
+    float s[E];
+    uint32_t cand = 0, must_kept = 0;
+    const float kInf = __builtin_huge_valf();
+    float lo = kInf, hi = -kInf;
+#pragma unroll
+    for (int x = 0; x < G; ++x) {
+        const int e0 = 256 * x + 4 * lane;
+        const bool valid = e0 < a.NK;  // NK % 4 == 0: all four or none
+        const uint32_t val4 = valid ? 0xFu : 0u;
+        const uint32_t diag4 = nibble_range(dlo - e0, dhi - e0);
+        const uint32_t pin4 = (pwv[x] >> msh) & val4;
+        const uint32_t drop4 = (dwv[x] >> msh) & val4;
+        const uint32_t must4 = (diag4 | pin4) & val4;
+        const uint32_t cand4 = val4 & ~must4 & ~drop4;
+        cand |= cand4 << (4 * x);
+        must_kept |= (must4 & ~drop4) << (4 * x);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            // + 0: -0.0 becomes +0.0 (equal in the ranking) and the value is canonical
+            const float sc = v[x][c] + 0.0f;
+            const uint32_t keepbit = 0u - ((cand4 >> c) & 1u);  // all ones for a candidate
+            const float sm = __uint_as_float((__float_as_uint(sc) & keepbit) | (__float_as_uint(-kInf) & ~keepbit));
+            const float sp = __uint_as_float((__float_as_uint(sc) & keepbit) | (__float_as_uint(kInf) & ~keepbit));
+            s[4 * x + c] = sm;
+            hi = fmaxf(hi, sm);
+            lo = fminf(lo, sp);
+        }
+    }
+    const int c = wave_sum_i(__builtin_popcount(cand));
+    // k_r = ceil(fl32(c) * fl32(budget)): the product rounds to fp32 first.
+    const float kf = ceilf(__fmul_rn((float)c, a.budget));
+    const int k = (kf >= (float)c) ? c : (int)kf;
+    uint32_t picked = 0;
+    if (k >= c) {
+        picked = cand;
+    } else if (k > 0) {
+        lo = wave_min_f(lo);
+        hi = wave_max_f(hi);
+        float T = hi;
+        int iT = 0;
+        if (!(hi > lo)) {  // every candidate has one score: the k lowest indices
+            iT = kth_index<G>(cand, k - 1, lane);
+        } else {
+            // First pass over every element (non-candidates, at -inf, land in bucket 0).
+            float scale = 128.0f / (0.5f * hi - 0.5f * lo);
+            float off = -lo * scale;
+            *(u32x4*)(hist + 4 * lane) = (u32x4){0u, 0u, 0u, 0u};
+            wave_lds_sync();
+#pragma unroll
+            for (int t = 0; t < E; ++t) atomicAdd(&hist[bucket_of(s[t], scale, off)], 1u);
+            wave_lds_sync();
+            if (lane == 0) hist[0] -= (uint32_t)(64 * E - c);
+            wave_lds_sync();
+            int bstar, above, inside;
+            find_bucket(hist, k, lane, bstar, above, inside);
+            uint32_t active = 0;  // elements of the bucket b*, among the candidates
+#pragma unroll
+            for (int t = 0; t < E; ++t) active |= (uint32_t)(bucket_of(s[t], scale, off) == (uint32_t)bstar) << t;
+            active &= cand;
+            int need = k - above;  // the need-th largest inside `active`
+            // Crowded bucket: narrow to its exact value range, only its elements counted.
+            bool tied = false;
+            for (int iter = 0; iter < 64 && inside > 64; ++iter) {
+                float blo = kInf, bhi = -kInf;
+#pragma unroll
+                for (int t = 0; t < E; ++t) {
+                    const bool on = (active >> t) & 1u;
+                    blo = fminf(blo, on ? s[t] : kInf);
+                    bhi = fmaxf(bhi, on ? s[t] : -kInf);
+                }
+                blo = wave_min_f(blo);
+                bhi = wave_max_f(bhi);
+                if (!(bhi > blo)) {  // one value: cut in index order below
+                    T = blo;
+                    tied = true;
+                    break;
+                }
+                scale = 128.0f / (0.5f * bhi - 0.5f * blo);
+                off = -blo * scale;
+                wave_lds_sync();
+                *(u32x4*)(hist + 4 * lane) = (u32x4){0u, 0u, 0u, 0u};
+                wave_lds_sync();
+#pragma unroll
+                for (int t = 0; t < E; ++t)
+                    if ((active >> t) & 1u) atomicAdd(&hist[bucket_of(s[t], scale, off)], 1u);
+                wave_lds_sync();
+                int ab2;
+                find_bucket(hist, need, lane, bstar, ab2, inside);
+                uint32_t next = 0;
+#pragma unroll
+                for (int t = 0; t < E; ++t) next |= (uint32_t)(bucket_of(s[t], scale, off) == (uint32_t)bstar) << t;
+                active &= next;
+                need -= ab2;
+            }
+            if (tied) {
+                // the need-th element (index order) among those equal to T in the bucket
+                iT = kth_index<G>(active, need - 1, lane);
+            } else {
+                // Compact the bucket's (value, index) pairs into LDS by ballot, in index order.
+                int n = 0;
+                const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+                for (int t = 0; t < E; ++t) {
+                    const bool on = (active >> t) & 1u;
+                    const uint64_t m = __ballot(on);
+                    if (m == 0) continue;
+                    if (on) {
+                        const int e = 256 * (t >> 2) + 4 * lane + (t & 3);
+                        list[n + __builtin_popcountll(m & below)] = make_uint2(__float_as_uint(s[t]), (uint32_t)e);
+                    }
+                    n += __builtin_popcountll(m);
+                }
+                wave_lds_sync();
+                // Rank each entry: entries before it in (score desc, index asc) order.
+                const uint2 mine = lane < n ? list[lane] : make_uint2(__float_as_uint(-kInf), 0xFFFFFFFFu);
+                const float vm = __uint_as_float(mine.x);
+                int rank = 0;
+                for (int q = 0; q < n; ++q) {
+                    const float vq = __uint_as_float(__builtin_amdgcn_readlane((int)mine.x, q));
+                    const uint32_t iq = (uint32_t)__builtin_amdgcn_readlane((int)mine.y, q);
+                    rank += (vq > vm || (vq == vm && iq < mine.y)) ? 1 : 0;
+                }
+                const uint64_t who = __ballot(lane < n && rank == need - 1);
+                const int src = who ? __builtin_ctzll(who) : 0;
+                T = __uint_as_float(__builtin_amdgcn_readlane((int)mine.x, src));
+                iT = __builtin_amdgcn_readlane((int)mine.y, src);
+            }
+        }
+        // picked: candidates before or at the k-th in (score desc, index asc) order
+#pragma unroll
+        for (int t = 0; t < E; ++t) {
+            const int e = 256 * (t >> 2) + 4 * lane + (t & 3);
+            const bool pk = s[t] > T || (s[t] == T && e <= iT);
+            picked |= (uint32_t)pk << t;
+        }
+        picked &= cand;
+    }
+    const uint32_t keepm = must_kept | picked;
+
+    int8_t* krow = a.keep + r * a.NK;
+    const int32_t row_begin = a.row_src ? a.row_src[r] : (int32_t)(r * a.row_step);
+    const int32_t row_end = a.row_src ? a.row_src[r + 1] : (int32_t)((r + 1) * a.row_step);
+    const int32_t row_len = row_end - row_begin;  // planned on the host from the same rule
+    if (lane == 0) {  // the caller's row offsets (the last row also writes the end)
+        a.row_ptr[r] = row_begin;
+        if (r + 1 == (int64_t)a.B * a.Hsel * a.NQ) a.row_ptr[r + 1] = row_end;
+    }
+    int32_t* crow = a.col_idx + row_begin;
+    int pos = 0;
+#pragma unroll
+    for (int x = 0; x < G; ++x) {
+        const int e0 = 256 * x + 4 * lane;
+        const uint32_t nib = (keepm >> (4 * x)) & 0xFu;
+        // four keep bytes of the nibble (byte c = bit c)
+        if (e0 < a.NK) *(uint32_t*)(krow + e0) = (nib * 0x00204081u) & 0x01010101u;
+        const int cnt = __builtin_popcount(nib);
+        const int incl = wave_prefix_sum(cnt);
+        int slot = pos + incl - cnt;
+        uint32_t m = nib;
+        while (m) {  // the lane's kept elements of this group, ascending
+            const int cc = __builtin_ctz(m);
+            if (slot < row_len) crow[slot] = e0 + cc;  // never write past the planned row
+            ++slot;
+            m &= m - 1u;
+        }
+        pos += __builtin_amdgcn_readlane(incl, 63);
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
@@ -961,6 +1267,21 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
         else if (ept <= 8) NSA_TOPK_ROWS(8);
         else NSA_TOPK_ROWS(16);
 #undef NSA_TOPK_ROWS
+        return hipGetLastError();
+    }
+    // Grouped layout: 16-byte aligned score rows, 4-byte aligned keep rows, masks in memory.
+    const bool grouped = a.NK % 4 == 0 && a.NK <= 2048 && a.pin_at < 0 && a.drop_at < 0 &&
+                         ((uintptr_t)a.keep & 3) == 0 && ((uintptr_t)a.scores & 15) == 0 &&
+                         a.q_off + (int64_t)(a.NQ + 1) * a.block_q + a.block_kv < ((int64_t)1 << 31);
+    if (grouped) {
+        const dim3 g3((unsigned)((a.NQ + 3) / 4), (unsigned)a.nh, (unsigned)a.B);
+        const int ng = (a.NK + 255) / 256;
+#define NSA_TOPK_G(GG) hipLaunchKernelGGL((topk_grouped_kernel<GG>), g3, dim3(256), 0, stream, a)
+        if (ng <= 1) NSA_TOPK_G(1);
+        else if (ng <= 2) NSA_TOPK_G(2);
+        else if (ng <= 4) NSA_TOPK_G(4);
+        else NSA_TOPK_G(8);
+#undef NSA_TOPK_G
         return hipGetLastError();
     }
     const dim3 grid((unsigned)((rows + 3) / 4));

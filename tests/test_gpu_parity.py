@@ -277,6 +277,9 @@ def test_exact_ties_take_lowest_index(S, bq, bkv, Hq):
     (1, 16, 4, 32768, 256, 16, 0.05),    # 2048 kv tiles
     (1, 16, 16, 8000, 64, 64, 0.30),     # 125 kv tiles (not a multiple of 4)
     (1, 12, 3, 6100, 64, 16, 0.10),      # 382 kv tiles, ragged tail
+    (1, 16, 4, 8000, 64, 16, 0.10),      # 500 kv tiles: a multiple of 4, second group of 256 ragged
+    (1, 8, 2, 20800, 128, 16, 0.97),     # 1300 kv tiles, budget near 1: the cut in the lowest buckets
+    (1, 16, 4, 4096, 32, 16, 0.98),      # 256 kv tiles, all but a few candidates kept
 ])
 def test_many_rows_pins_drops(B, Hq, Hkv, S, bq, bkv, budget):
     """More than 1024 selection rows (one wavefront per row) against the oracle,

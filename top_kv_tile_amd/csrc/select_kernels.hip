@@ -862,32 +862,31 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(TopkArgs a) {
 // One wavefront per row, for the many-row case with NK <= 256 G and NK a
 // multiple of 4 (every score row then starts 16-byte aligned). Lane L holds
 // the 4 consecutive elements e = 256 x + 4 L + c (c = 0..3) of each group x,
-// read by one 16-byte load, and element e is bit t = 4 x + c of the lane's
-// masks. A group's mask bits of a lane are then one nibble of one 64-bit mask
-// word (word 4 x + L / 16, bits 4 (L % 16) .. + 3), and a group's kept flags
-// leave as one 4-byte store. Index order (the tie break) is group, then lane,
-// then c.
+// read by one 16-byte load. Index order (the tie break) is group, then lane,
+// then c. Two per-lane bit layouts are used:
+//  - row masks (candidates, forced tiles): bit 4 x + c, so a group's pin and
+//    drop bits are one nibble of one 64-bit mask word (word 4 x + L / 16,
+//    bits 4 (L % 16) .. + 3);
+//  - per-group byte words: byte c of word x belongs to element (x, c). Each
+//    element's histogram bucket is kept this way, so that later tests on
+//    buckets run on four elements per 32-bit integer operation, and a
+//    group's kept flags leave as one 4-byte store.
 //
-// Selection of the k_r-th largest candidate (score descending, index
-// ascending), exact:
-//  1. non-candidates are set to -inf; lo / hi over the candidates;
-//  2. one histogram of 256 buckets over [lo, hi] (a monotone map) gives the
-//     bucket b* that holds the k-th largest and the count above it;
-//  3. the elements of b* (few: a bucket holds about c / 256 scores unless
+// Selection of the k_r candidates with the largest scores (score
+// descending, index ascending), exact:
+//  1. non-candidates are set to -inf; hi = the largest candidate score, lo =
+//     the smallest score loaded (no larger than any candidate's);
+//  2. one histogram of 256 buckets over [lo, hi] (a monotone map, -inf to
+//     bucket 0, whose non-candidate count is taken out again) gives the
+//     bucket b* that holds the k-th largest candidate and the count above;
+//  3. every element in a bucket above b* is picked (a candidate: -inf is in
+//     the lowest bucket, never above b*);
+//  4. the candidates of b* (few: a bucket holds about c / 256 scores unless
 //     scores crowd) are compacted by ballot into LDS and ranked against each
-//     other, giving the k-th element's value T and index i_T;
-//  4. picked = candidates with score > T, or == T and index <= i_T.
-// If b* holds more than 64 elements the search narrows to that bucket's
+//     other; the first `need` of them are picked.
+// If b* holds more than 64 candidates the search narrows to that bucket's
 // exact value range and repeats on its elements; a range that collapses to
 // one value is cut in index order.
-
-// Nibble of the bits lo..hi (clipped to 0..3); empty when lo > hi.
-__device__ __forceinline__ uint32_t nibble_range(int lo, int hi) {
-    lo = lo < 0 ? 0 : lo;
-    hi = hi > 3 ? 3 : hi;
-    if (lo > hi) return 0u;
-    return ((2u << hi) - 1u) & ~((1u << lo) - 1u);
-}
 
 // Bucket of x in the map u = x * scale + off, clamped to 0 .. 255 (monotone
 // in x: the fma rounds a monotone function; -inf goes to bucket 0).
@@ -925,7 +924,7 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, int need, int 
 // Index (in index order) of the r-th (0-based) element of `m` (bit 4x + c of
 // lane L is element 256 x + 4 L + c); wave-uniform. r must be < popcount.
 template <int G>
-__device__ int kth_index(uint32_t m, int r, int lane) {
+__device__ __forceinline__ int kth_index(uint32_t m, int r, int lane) {
     int res = 0;
 #pragma unroll
     for (int x = 0; x < G; ++x) {
@@ -951,17 +950,50 @@ __device__ int kth_index(uint32_t m, int r, int lane) {
     return res;
 }
 
+// Nibble of the bits lo..hi (clipped to 0..3); empty when lo > hi.
+__device__ __forceinline__ uint32_t nibble_range(int lo, int hi) {
+    lo = lo < 0 ? 0 : lo;
+    hi = hi > 3 ? 3 : hi;
+    if (lo > hi) return 0u;
+    return ((2u << hi) - 1u) & ~((1u << lo) - 1u);
+}
+
+// A nibble's bit c moved to bit 8 c (byte c = 0 or 1); the four partial
+// products land on distinct bits, so no carries mix them.
+__device__ __forceinline__ uint32_t spread_nibble(uint32_t n) { return (n * 0x00204081u) & 0x01010101u; }
+
+// Byte-wise tests on four buckets at once (high bit of each byte).
+//   zero bytes of z:      ~(((z & 0x7f..) + 0x7f..) | z) & 0x80..
+//   x >= y per byte (y in every byte): with t = (x | 0x80..) - (y & 0x7f..),
+//   whose high bits give x_low >= y_low without borrows between bytes,
+//   ((x & ~y) | (~(x ^ y) & t)) & 0x80..
+__device__ __forceinline__ uint32_t bytes_equal(uint32_t x, uint32_t yrep) {
+    const uint32_t z = x ^ yrep;
+    return ~(((z & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | z) & 0x80808080u;
+}
+__device__ __forceinline__ uint32_t bytes_at_least(uint32_t x, uint32_t yrep) {
+    const uint32_t t = (x | 0x80808080u) - (yrep & 0x7F7F7F7Fu);
+    return ((x & ~yrep) | (~(x ^ yrep) & t)) & 0x80808080u;
+}
+
+__device__ __forceinline__ uint32_t wave_or_u(uint32_t x) {
+    return (uint32_t)wave_reduce((int)x, [](int p, int q) { return p | q; });
+}
+
 template <int G>
 __global__ __launch_bounds__(256, 3) void topk_grouped_kernel(TopkArgs a) {
     constexpr int E = 4 * G;
+    constexpr uint32_t kFull = E == 32 ? 0xFFFFFFFFu : ((1u << (E & 31)) - 1u);
     __shared__ uint32_t hist_all[4][256];
     __shared__ uint2 list_all[4][64];
+    __shared__ uint32_t pick_all[4][64 * G];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = (int)blockIdx.x * 4 + wave;  // query tile
     if (i >= a.NQ) return;
     uint32_t* hist = hist_all[wave];
     uint2* list = list_all[wave];
+    uint32_t* pick = pick_all[wave];  // lane L's words x at G L + x: picks inside b*, byte form
     const int hl = blockIdx.y, b = blockIdx.z;
     const int h = a.h0 + hl;
     const int64_t lr = ((int64_t)b * a.nh + hl) * a.NQ + i;  // row of the score chunk
@@ -983,7 +1015,7 @@ __global__ __launch_bounds__(256, 3) void topk_grouped_kernel(TopkArgs a) {
     // and all are in flight together), then the masks.
     f32x4 v[G];
     uint32_t pwv[G], dwv[G];
-    const int mw = 2 * (lane >> 4) + ((lane >> 3) & 1);  // the lane's 32-bit half word within a group
+    const int mw = lane >> 3;  // the lane's 32-bit half word within a group
     const int msh = 4 * (lane & 7);
     const int last_w = 2 * a.NKW - 1;
 #pragma unroll
@@ -992,146 +1024,208 @@ __global__ __launch_bounds__(256, 3) void topk_grouped_kernel(TopkArgs a) {
         pwv[x] = pw ? pw[min(8 * x + mw, last_w)] : 0u;
         dwv[x] = dw ? dw[min(8 * x + mw, last_w)] : 0u;
     }
-    // Non-candidates become -inf (a bitfield select on the candidate bit spread
-    // to a full-word mask), so later passes need no masks.
+
+    // Row masks (bit 4 x + c). Groups of this lane inside the row: 256 x + 4 L < NK.
+    const int nvg = (a.NK - 4 * lane + 255) >> 8;
+    const uint32_t valid = nvg >= G ? kFull : ((1u << (4 * nvg)) - 1u);
+    uint32_t diag = 0;
+    {
+        const int d0 = dlo, d1 = min(dhi, a.NK - 1);
+        if (d1 - d0 < 8) {  // the usual few diagonal tiles, one by one (wave-uniform loop)
+            for (int e = d0; e <= d1; ++e)
+                if (((e & 255) >> 2) == lane) diag |= 1u << (4 * (e >> 8) + (e & 3));
+        } else {
+#pragma unroll
+            for (int x = 0; x < G; ++x) {
+                const int e0 = 256 * x + 4 * lane;
+                diag |= nibble_range(d0 - e0, d1 - e0) << (4 * x);
+            }
+        }
+    }
+    uint32_t pin = 0, drop = 0;
+    if (pw) {
+#pragma unroll
+        for (int x = 0; x < G; ++x) pin |= ((pwv[x] >> msh) & 0xFu) << (4 * x);
+    }
+    if (dw) {
+#pragma unroll
+        for (int x = 0; x < G; ++x) drop |= ((dwv[x] >> msh) & 0xFu) << (4 * x);
+    }
+    const uint32_t forced = (diag | pin) & ~drop & valid;  // kept whatever the scores
+    const uint32_t cand = valid & ~(diag | pin | drop);
+
+    // Non-candidates become -inf (a select on the candidate bit spread to a
+    // full-word mask), so later passes need no masks.
     float s[E];
-    uint32_t cand = 0, must_kept = 0;
     const float kInf = __builtin_huge_valf();
     float lo = kInf, hi = -kInf;
 #pragma unroll
-    for (int x = 0; x < G; ++x) {
-        const int e0 = 256 * x + 4 * lane;
-        const bool valid = e0 < a.NK;  // NK % 4 == 0: all four or none
-        const uint32_t val4 = valid ? 0xFu : 0u;
-        const uint32_t diag4 = nibble_range(dlo - e0, dhi - e0);
-        const uint32_t pin4 = (pwv[x] >> msh) & val4;
-        const uint32_t drop4 = (dwv[x] >> msh) & val4;
-        const uint32_t must4 = (diag4 | pin4) & val4;
-        const uint32_t cand4 = val4 & ~must4 & ~drop4;
-        cand |= cand4 << (4 * x);
-        must_kept |= (must4 & ~drop4) << (4 * x);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            // + 0: -0.0 becomes +0.0 (equal in the ranking) and the value is canonical
-            const float sc = v[x][c] + 0.0f;
-            const uint32_t keepbit = 0u - ((cand4 >> c) & 1u);  // all ones for a candidate
-            const float sm = __uint_as_float((__float_as_uint(sc) & keepbit) | (__float_as_uint(-kInf) & ~keepbit));
-            const float sp = __uint_as_float((__float_as_uint(sc) & keepbit) | (__float_as_uint(kInf) & ~keepbit));
-            s[4 * x + c] = sm;
-            hi = fmaxf(hi, sm);
-            lo = fminf(lo, sp);
-        }
+    for (int t = 0; t < E; ++t) {
+        const float sv = v[t >> 2][t & 3];
+        const uint32_t m = (uint32_t)((int32_t)(cand << (31 - t)) >> 31);  // all ones for a candidate
+        s[t] = __uint_as_float((__float_as_uint(sv) & m) | (__float_as_uint(-kInf) & ~m));
+        hi = fmaxf(hi, s[t]);
+        lo = fminf(lo, sv);
     }
     const int c = wave_sum_i(__builtin_popcount(cand));
     // k_r = ceil(fl32(c) * fl32(budget)): the product rounds to fp32 first.
     const float kf = ceilf(__fmul_rn((float)c, a.budget));
     const int k = (kf >= (float)c) ? c : (int)kf;
-    uint32_t picked = 0;
+
+    uint32_t picked = forced;  // row-mask layout
+    uint32_t bk[G];            // bucket bytes
+#pragma unroll
+    for (int x = 0; x < G; ++x) bk[x] = 0;
+    int bstar = 255;        // elements in buckets above b* are picked (none while b* = 255)
+    bool in_bucket = false;  // picks inside b* were scattered to `pick`
     if (k >= c) {
-        picked = cand;
+        picked |= cand;
     } else if (k > 0) {
         lo = wave_min_f(lo);
         hi = wave_max_f(hi);
-        float T = hi;
-        int iT = 0;
-        if (!(hi > lo)) {  // every candidate has one score: the k lowest indices
-            iT = kth_index<G>(cand, k - 1, lane);
+        uint32_t cut_mask = 0;  // if cut_need > 0: the first cut_need of cut_mask, in index order
+        int cut_need = 0;
+        uint32_t eqb[G];  // byte form, high bit: the candidates of the bucket to rank
+        bool rank_bucket = false;
+        int need = 0;
+        if (!(hi > lo)) {  // every loaded score is the same: the k lowest candidate indices
+            cut_mask = cand;
+            cut_need = k;
         } else {
-            // First pass over every element (non-candidates, at -inf, land in bucket 0).
+            // First pass over every element; non-candidates (-inf) land in bucket 0.
             float scale = 128.0f / (0.5f * hi - 0.5f * lo);
             float off = -lo * scale;
             *(u32x4*)(hist + 4 * lane) = (u32x4){0u, 0u, 0u, 0u};
             wave_lds_sync();
 #pragma unroll
-            for (int t = 0; t < E; ++t) atomicAdd(&hist[bucket_of(s[t], scale, off)], 1u);
+            for (int x = 0; x < G; ++x) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    // u8 conversion saturates: monotone, -inf to 0, above 255 to 255
+                    w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s[4 * x + cc], scale, off), cc, w);
+                    atomicAdd(&hist[(w >> (8 * cc)) & 255u], 1u);
+                }
+                bk[x] = w;
+            }
             wave_lds_sync();
             if (lane == 0) hist[0] -= (uint32_t)(64 * E - c);
             wave_lds_sync();
-            int bstar, above, inside;
+            int above, inside;
             find_bucket(hist, k, lane, bstar, above, inside);
-            uint32_t active = 0;  // elements of the bucket b*, among the candidates
+            need = k - above;  // the need largest candidates of bucket b*
+            if (inside <= 64) {
+                const uint32_t brep = (uint32_t)bstar * 0x01010101u;
 #pragma unroll
-            for (int t = 0; t < E; ++t) active |= (uint32_t)(bucket_of(s[t], scale, off) == (uint32_t)bstar) << t;
-            active &= cand;
-            int need = k - above;  // the need-th largest inside `active`
-            // Crowded bucket: narrow to its exact value range, only its elements counted.
-            bool tied = false;
-            for (int iter = 0; iter < 64 && inside > 64; ++iter) {
-                float blo = kInf, bhi = -kInf;
-#pragma unroll
-                for (int t = 0; t < E; ++t) {
-                    const bool on = (active >> t) & 1u;
-                    blo = fminf(blo, on ? s[t] : kInf);
-                    bhi = fmaxf(bhi, on ? s[t] : -kInf);
+                for (int x = 0; x < G; ++x) {
+                    eqb[x] = bytes_equal(bk[x], brep);
+                    if (bstar == 0) eqb[x] &= spread_nibble((cand >> (4 * x)) & 0xFu) << 7;
                 }
-                blo = wave_min_f(blo);
-                bhi = wave_max_f(bhi);
-                if (!(bhi > blo)) {  // one value: cut in index order below
-                    T = blo;
-                    tied = true;
-                    break;
-                }
-                scale = 128.0f / (0.5f * bhi - 0.5f * blo);
-                off = -blo * scale;
-                wave_lds_sync();
-                *(u32x4*)(hist + 4 * lane) = (u32x4){0u, 0u, 0u, 0u};
-                wave_lds_sync();
+                rank_bucket = true;
+            } else {
+                // Crowded bucket: narrow to its exact value range, only its elements counted.
+                uint32_t active = 0;
 #pragma unroll
                 for (int t = 0; t < E; ++t)
-                    if ((active >> t) & 1u) atomicAdd(&hist[bucket_of(s[t], scale, off)], 1u);
-                wave_lds_sync();
-                int ab2;
-                find_bucket(hist, need, lane, bstar, ab2, inside);
-                uint32_t next = 0;
+                    active |= (uint32_t)(((bk[t >> 2] >> (8 * (t & 3))) & 255u) == (uint32_t)bstar) << t;
+                active &= cand;
+                for (int iter = 0; iter < 64; ++iter) {
+                    float blo = kInf, bhi = -kInf;
 #pragma unroll
-                for (int t = 0; t < E; ++t) next |= (uint32_t)(bucket_of(s[t], scale, off) == (uint32_t)bstar) << t;
-                active &= next;
-                need -= ab2;
-            }
-            if (tied) {
-                // the need-th element (index order) among those equal to T in the bucket
-                iT = kth_index<G>(active, need - 1, lane);
-            } else {
-                // Compact the bucket's (value, index) pairs into LDS by ballot, in index order.
-                int n = 0;
-                const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-                for (int t = 0; t < E; ++t) {
-                    const bool on = (active >> t) & 1u;
-                    const uint64_t m = __ballot(on);
-                    if (m == 0) continue;
-                    if (on) {
-                        const int e = 256 * (t >> 2) + 4 * lane + (t & 3);
-                        list[n + __builtin_popcountll(m & below)] = make_uint2(__float_as_uint(s[t]), (uint32_t)e);
+                    for (int t = 0; t < E; ++t) {
+                        const bool on = (active >> t) & 1u;
+                        blo = fminf(blo, on ? s[t] : kInf);
+                        bhi = fmaxf(bhi, on ? s[t] : -kInf);
                     }
+                    blo = wave_min_f(blo);
+                    bhi = wave_max_f(bhi);
+                    if (!(bhi > blo)) {  // one value left: cut in index order
+                        cut_mask = active;
+                        cut_need = need;
+                        break;
+                    }
+                    scale = 128.0f / (0.5f * bhi - 0.5f * blo);
+                    off = -blo * scale;
+                    wave_lds_sync();
+                    *(u32x4*)(hist + 4 * lane) = (u32x4){0u, 0u, 0u, 0u};
+                    wave_lds_sync();
+#pragma unroll
+                    for (int t = 0; t < E; ++t)
+                        if ((active >> t) & 1u) atomicAdd(&hist[bucket_of(s[t], scale, off)], 1u);
+                    wave_lds_sync();
+                    int b2, ab2, in2;
+                    find_bucket(hist, need, lane, b2, ab2, in2);
+                    uint32_t next = 0, up = 0;
+#pragma unroll
+                    for (int t = 0; t < E; ++t) {
+                        const uint32_t bb = bucket_of(s[t], scale, off);
+                        next |= (uint32_t)(bb == (uint32_t)b2) << t;
+                        up |= (uint32_t)(bb > (uint32_t)b2) << t;
+                    }
+                    picked |= up & active;
+                    active &= next;
+                    need -= ab2;
+                    if (in2 <= 64) {
+#pragma unroll
+                        for (int x = 0; x < G; ++x) eqb[x] = spread_nibble((active >> (4 * x)) & 0xFu) << 7;
+                        rank_bucket = true;
+                        break;
+                    }
+                }
+            }
+        }
+        if (rank_bucket) {
+            // Compact the bucket's (score, index) pairs into LDS by ballot, over
+            // the slots that hold any of them (wave-uniform tests).
+            uint32_t any = 0;  // bit 8 c + x
+#pragma unroll
+            for (int x = 0; x < G; ++x) any |= eqb[x] >> (7 - x);
+            any = wave_or_u(any);
+            int n = 0;
+            const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+            for (int x = 0; x < G; ++x) {
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    if (!((any >> (8 * cc + x)) & 1u)) continue;
+                    const bool on = (eqb[x] >> (8 * cc + 7)) & 1u;
+                    const uint64_t m = __ballot(on);
+                    if (on)
+                        list[n + __builtin_popcountll(m & below)] =
+                            make_uint2(__float_as_uint(s[4 * x + cc]), (uint32_t)(256 * x + 4 * lane + cc));
                     n += __builtin_popcountll(m);
                 }
-                wave_lds_sync();
-                // Rank each entry: entries before it in (score desc, index asc) order.
-                const uint2 mine = lane < n ? list[lane] : make_uint2(__float_as_uint(-kInf), 0xFFFFFFFFu);
-                const float vm = __uint_as_float(mine.x);
-                int rank = 0;
-                for (int q = 0; q < n; ++q) {
-                    const float vq = __uint_as_float(__builtin_amdgcn_readlane((int)mine.x, q));
-                    const uint32_t iq = (uint32_t)__builtin_amdgcn_readlane((int)mine.y, q);
-                    rank += (vq > vm || (vq == vm && iq < mine.y)) ? 1 : 0;
-                }
-                const uint64_t who = __ballot(lane < n && rank == need - 1);
-                const int src = who ? __builtin_ctzll(who) : 0;
-                T = __uint_as_float(__builtin_amdgcn_readlane((int)mine.x, src));
-                iT = __builtin_amdgcn_readlane((int)mine.y, src);
+            }
+            wave_lds_sync();
+            // Rank of each entry: the entries before it in (score desc, index asc)
+            // order. The first `need` are picked: a flag in their owners' words.
+            const uint2 mine = lane < n ? list[lane] : make_uint2(__float_as_uint(-kInf), 0xFFFFFFFFu);
+            const float vm = __uint_as_float(mine.x);
+            int rank = 0;
+            for (int q = 0; q < n; ++q) {
+                const float vq = __uint_as_float(__builtin_amdgcn_readlane((int)mine.x, q));
+                const uint32_t iq = (uint32_t)__builtin_amdgcn_readlane((int)mine.y, q);
+                rank += (vq > vm || (vq == vm && iq < mine.y)) ? 1 : 0;
+            }
+#pragma unroll
+            for (int x = 0; x < G; ++x) pick[G * lane + x] = 0u;
+            wave_lds_sync();
+            if (lane < n && rank < need) {
+                const uint32_t e = mine.y;
+                atomicOr(&pick[G * ((e & 255u) >> 2) + (e >> 8)], 1u << (8 * (e & 3u)));
+            }
+            wave_lds_sync();
+            in_bucket = true;
+        }
+        if (cut_need > 0) {
+            const int iT = kth_index<G>(cut_mask, cut_need - 1, lane);
+#pragma unroll
+            for (int x = 0; x < G; ++x) {
+                const int e0 = 256 * x + 4 * lane;
+                picked |= (nibble_range(0, iT - e0) & (cut_mask >> (4 * x))) << (4 * x);
             }
         }
-        // picked: candidates before or at the k-th in (score desc, index asc) order
-#pragma unroll
-        for (int t = 0; t < E; ++t) {
-            const int e = 256 * (t >> 2) + 4 * lane + (t & 3);
-            const bool pk = s[t] > T || (s[t] == T && e <= iT);
-            picked |= (uint32_t)pk << t;
-        }
-        picked &= cand;
     }
-    const uint32_t keepm = must_kept | picked;
 
     int8_t* krow = a.keep + r * a.NK;
     const int32_t row_begin = a.row_src ? a.row_src[r] : (int32_t)(r * a.row_step);
@@ -1141,25 +1235,44 @@ __global__ __launch_bounds__(256, 3) void topk_grouped_kernel(TopkArgs a) {
         a.row_ptr[r] = row_begin;
         if (r + 1 == (int64_t)a.B * a.Hsel * a.NQ) a.row_ptr[r + 1] = row_end;
     }
+    // Kept flags per group, byte form: forced and rank-picked tiles, buckets above b*.
+    const uint32_t yrep = (uint32_t)min(bstar + 1, 255) * 0x01010101u;
+    const uint32_t hmask = bstar < 255 ? 0x80808080u : 0u;
+    uint32_t kb[G];
+#pragma unroll
+    for (int x = 0; x < G; ++x) {
+        kb[x] = spread_nibble((picked >> (4 * x)) & 0xFu) | ((bytes_at_least(bk[x], yrep) & hmask) >> 7);
+        if (in_bucket) kb[x] |= pick[G * lane + x];
+        const int e0 = 256 * x + 4 * lane;
+        if (e0 < a.NK) *(uint32_t*)(krow + e0) = kb[x];
+    }
+    // CSR: ascending indices at row_begin, never past the planned row. Group
+    // counts are scanned three at a time in 10-bit fields (a field's total is
+    // at most 256).
     int32_t* crow = a.col_idx + row_begin;
     int pos = 0;
 #pragma unroll
-    for (int x = 0; x < G; ++x) {
-        const int e0 = 256 * x + 4 * lane;
-        const uint32_t nib = (keepm >> (4 * x)) & 0xFu;
-        // four keep bytes of the nibble (byte c = bit c)
-        if (e0 < a.NK) *(uint32_t*)(krow + e0) = (nib * 0x00204081u) & 0x01010101u;
-        const int cnt = __builtin_popcount(nib);
-        const int incl = wave_prefix_sum(cnt);
-        int slot = pos + incl - cnt;
-        uint32_t m = nib;
-        while (m) {  // the lane's kept elements of this group, ascending
-            const int cc = __builtin_ctz(m);
-            if (slot < row_len) crow[slot] = e0 + cc;  // never write past the planned row
-            ++slot;
-            m &= m - 1u;
+    for (int x0 = 0; x0 < G; x0 += 3) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int x = x0; x < x0 + 3 && x < G; ++x) packed |= (uint32_t)__builtin_popcount(kb[x]) << (10 * (x - x0));
+        const uint32_t incl = (uint32_t)wave_prefix_sum((int)packed);
+        const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+#pragma unroll
+        for (int x = x0; x < x0 + 3 && x < G; ++x) {
+            const int f = 10 * (x - x0);
+            const int cnt = (int)((packed >> f) & 1023u);
+            int slot = pos + (int)((incl >> f) & 1023u) - cnt;
+            uint32_t m = kb[x];
+            const int e0 = 256 * x + 4 * lane;
+            while (m) {  // the lane's kept elements of this group, ascending
+                const int cc = __builtin_ctz(m) >> 3;
+                if (slot < row_len) crow[slot] = e0 + cc;
+                ++slot;
+                m &= m - 1u;
+            }
+            pos += (int)((tot >> f) & 1023u);
         }
-        pos += __builtin_amdgcn_readlane(incl, 63);
     }
 }
 

@@ -311,7 +311,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
     for (int m = 0; m < DBLK; ++m) oacc[m] = (f32x16){};
     float m_ref = kNegInf;  // exponent reference of this lane's query row (raw dot-product units)
     float l_run = 0.f;      // partial sum over this lane's half of every tile
-    const float tau_raw = 8.0f / a.scale_log2;
 
     // Masks of a partial tile (causal diagonal or ragged tail): keys past the
     // lane's query row or past S get -inf. Only partial tiles take this branch.
@@ -337,29 +336,21 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
         return __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + 32 * mb * G::ROWB + koff[ks_]));
     };
     // One straight-line block: the matrix cores compute S(next) while the
-    // vector ALUs turn S(cur) into P (row max, exponentials, bf16 pack, row
-    // sum). Lane holds query qrow and keys 32*mb + 8*q + 4*hf + e at
-    // sacc[mb][4q + e]; the softmax scale is folded into one FMA per logit.
-    // Lazy reference: m_ref (raw units) moves only when a row's maximum exceeds
-    // it by more than 8 / scale, so p <= 2^8 and O is rescaled on few tiles;
-    // any reference gives the same normalised result and LSE adds it back.
+    // vector ALUs turn S(cur) into P (exponentials, bf16 pack, row sum). Lane
+    // holds query qrow and keys 32*mb + 8*q + 4*hf + e at sacc[mb][4q + e];
+    // the softmax scale is folded into one FMA per logit.
+    // Reference: the exponentials are taken against the row's current
+    // reference m_ref (raw units) without a row maximum. Only when a row's
+    // exponentials of this tile sum past 2^20 (some p beyond 2^20 / 64), or the
+    // row has no reference yet, does the wave take the row maximum: those
+    // rows move their reference to it and recompute the tile. Any reference
+    // gives the same normalised result and LSE adds it back; bounding p keeps
+    // O and the row sum far from overflow.
     auto qk_softmax = [&](f32x16 (&scur)[2], f32x16 (&snext)[2], int kstage, bf16x8 (&pf)[4]) -> float {
         const char* ks = kst[kstage];
         snext[0] = (f32x16){};
         snext[1] = (f32x16){};
-        float mx = kNegInf;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int x = 0; x < 16; ++x) mx = fmaxf(mx, scur[mb][x]);
-        {  // the other half-wave holds the row's other keys
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-            mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
-        }
-        const bool grow = mx > m_ref + tau_raw;
-        const float m_new = grow ? mx : m_ref;
-        const float alpha = grow ? fast_exp2((m_ref - m_new) * a.scale_log2) : 1.0f;  // 0 when m_ref = -inf
-        const float mref_s = (m_new == kNegInf) ? 0.f : m_new * a.scale_log2;
+        const float mref_s = (m_ref == kNegInf) ? 0.f : m_ref * a.scale_log2;
         float psum = 0.f;
         // K fragments one k-step ahead of their products (two buffers),
         // fenced so the reads of step ks + 1 are in flight under step ks.
@@ -392,9 +383,41 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnArgs a) {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        // The row's sum over both lane halves (the other half holds its other
+        // keys): the swap returns this lane's and the other half's value, in an
+        // order that depends on the half, and their sum is the same in both.
+        const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
+        const float prow = __uint_as_float(ps[0]) + __uint_as_float(ps[1]);
+        const bool redo = !(prow <= 1048576.0f) || m_ref == kNegInf;  // 2^20; also catches inf
+        float alpha = 1.0f;
+        if (__ballot(redo)) {  // wave-uniform; rare after a row's first tile
+            float mx = kNegInf;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) mx = fmaxf(mx, scur[mb][x]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+            if (redo) {
+                const float m_new = fmaxf(mx, m_ref);
+                alpha = (m_new > m_ref) ? fast_exp2((m_ref - m_new) * a.scale_log2) : 1.0f;  // 0 from -inf
+                const float ms = (m_new == kNegInf) ? 0.f : m_new * a.scale_log2;
+                psum = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int mb = kk >> 1, q4 = 8 * (kk & 1);
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) {
+                        const float pv = fast_exp2(__builtin_fmaf(scur[mb][q4 + x], a.scale_log2, -ms));
+                        psum += pv;
+                        pf[kk][x] = (__bf16)pv;
+                    }
+                }
+                m_ref = m_new;
+            }
+        }
         l_run = l_run * alpha + psum;
-        m_ref = m_new;
-        return grow ? alpha : 1.0f;
+        return alpha;
     };
     // O^T += V^T P^T ; the V^T fragment of k-step kk, row block m is two
     // transposed reads: keys 16kk + 4hf + (0..3) and 16kk + 8 + 4hf + (0..3).

@@ -205,9 +205,29 @@ def backward_timing(q, k, v, out, lse, sel, w: synth.Workload, fwd_flops: float,
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     flops = 2.5 * fwd_flops
     tflops = flops / (ms * 1e-3) / 1e12
+    # Per-kernel device time from the library's stage events (3 more calls):
+    # delta, the kv-major index, dQ (S, dP and dQ products: 1.5x the forward's
+    # kept-tile FLOPs executed) and dK/dV (S, dP, dV and dK: 2x).
+    tkt.nsa_stage_timing_begin()
+    for _ in range(3):
+        call()
+    recs = tkt.nsa_stage_timing_end()
+    per = {}
+    for name, t in recs:
+        per.setdefault(name, []).append(t)
+    kernels = {}
+    for name, xs in per.items():
+        kms = float(np.median(xs))
+        d = {"ms": round(kms, 3)}
+        mult = {"dq": 1.5, "dkdv": 2.0}.get(name)
+        if mult:
+            d["executed_TFLOPs"] = round(mult * fwd_flops / (kms * 1e-3) / 1e12, 2)
+            d["executed_frac_bf16_peak"] = round(d["executed_TFLOPs"] / PEAK_BF16_TFLOPS, 4)
+        kernels[name] = d
     return {"ms": round(ms, 3), "kept_tile_flops_per_call": flops, "TFLOPs": round(tflops, 2),
-            "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "kernels": "delta, kv-major index (3), bwd_dq_mfma_kernel<128,4>, bwd_dkdv_mfma_kernel<128>"}
+            "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4), "kernels": kernels,
+            "kernel_names": "delta_kernel, kv-major index (colcount, colscan x3, colfill), "
+                            "bwd_dq_mfma_kernel<128,4>, bwd_dkdv_mfma_kernel<128>"}
 
 
 def _event_ms(fn, calls: int, stream, queued: bool = False) -> float:

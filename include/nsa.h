@@ -392,8 +392,9 @@ int nsa_score_blocks(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* s
  * (nsa_select, nsa_select_planned, nsa_decode_select) made on the calling
  * thread record a HIP event on their stream at their start and after each
  * stage: "pool_q", "pool_k", "head_mean" (head_shared), then "scores" and
- * "topk" once per head chunk. Host only; the events are created by the library
- * and destroyed by _end. */
+ * "topk" once per head chunk. nsa_block_sparse_attn_bwd records "delta",
+ * "kv_index" (with a selection), then "dq" and "dkdv" on its MFMA path.
+ * Host only; the events are created by the library and destroyed by _end. */
 typedef struct nsa_stage_time {
     const char* name;   /* static string: the stage that ended at this mark */
     float ms;           /* device time since the previous mark of the same call */

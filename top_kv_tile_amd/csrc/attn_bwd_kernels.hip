@@ -1189,6 +1189,8 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t stream) {
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
+    hipError_t e = stage_mark("dq", stream);
+    if (e != hipSuccess) return e;
     if (kvwork > 0) {
         if (a.D == 128)
             hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<128>), dim3((unsigned)kvwork), dim3(256),
@@ -1196,8 +1198,9 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t stream) {
         else
             hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<64>), dim3((unsigned)kvwork), dim3(256),
                                attn_bwd_dkdv_lds_bytes(64), stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    return hipGetLastError();
+    return stage_mark("dkdv", stream);
 }
 
 hipError_t launch_attn_bwd_simt(const AttnBwdArgs& a, int bf16, hipStream_t stream) {

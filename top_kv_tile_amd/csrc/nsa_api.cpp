@@ -19,6 +19,30 @@
 
 #include "nsa_internal.h"
 
+namespace nsa {
+// Stage timing (nsa_stage_timing_begin / _end): while it is on, the
+// selection and gradient calls of this thread record an event on their
+// stream at the start and after every stage launch. Off, a mark costs one
+// thread-local test.
+struct StageTiming {
+    bool on = false;
+    std::vector<const char*> names;
+    std::vector<hipEvent_t> marks;
+};
+thread_local StageTiming t_stages;
+
+hipError_t stage_mark(const char* name, hipStream_t stream) {
+    StageTiming& t = t_stages;
+    if (!t.on) return hipSuccess;
+    hipEvent_t ev = nullptr;
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) return e;
+    t.names.push_back(name);
+    t.marks.push_back(ev);
+    return hipEventRecord(ev, stream);
+}
+}  // namespace nsa
+
 namespace {
 
 thread_local int g_last_hip = 0;
@@ -321,48 +345,27 @@ hipError_t upload(int n, void* const* dst, const void* const* src, const size_t*
     return hipSuccess;
 }
 
-// Stage timing (nsa_stage_timing_begin / _end): while it is on, the
-// selection calls of this thread record an event on their stream at the start
-// and after every stage launch. Off, a mark costs one thread-local test.
-struct StageTiming {
-    bool on = false;
-    std::vector<const char*> names;
-    std::vector<hipEvent_t> marks;
-};
-thread_local StageTiming t_stages;
-
-hipError_t stage_mark(const char* name, hipStream_t stream) {
-    StageTiming& t = t_stages;
-    if (!t.on) return hipSuccess;
-    hipEvent_t ev = nullptr;
-    hipError_t e = hipEventCreate(&ev);
-    if (e != hipSuccess) return e;
-    t.names.push_back(name);
-    t.marks.push_back(ev);
-    return hipEventRecord(ev, stream);
-}
-
 // Enqueues pooling (+ head means) of q and k into the workspace.
 int run_pool(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec, const Geo& g, const WsLayout& w,
              char* ws, hipStream_t stream, const float** qh, const float** kh, int* Hk) {
     hipError_t e;
     float* pq = (float*)(ws + w.pq);
     float* pk = (float*)(ws + w.pk);
-    if ((e = stage_mark("start", stream)) != hipSuccess) return hip_fail(e);
+    if ((e = nsa::stage_mark("start", stream)) != hipSuccess) return hip_fail(e);
     if ((e = nsa::launch_pool(q->data, g.bf16, (int64_t)g.B * g.Hq, g.Sq, g.D, spec->block_q, pq, stream)) !=
         hipSuccess)
         return hip_fail(e);
-    if ((e = stage_mark("pool_q", stream)) != hipSuccess) return hip_fail(e);
+    if ((e = nsa::stage_mark("pool_q", stream)) != hipSuccess) return hip_fail(e);
     if ((e = nsa::launch_pool(k->data, g.bf16, (int64_t)g.B * g.Hkv, g.Skv, g.D, spec->block_kv, pk,
                               stream)) != hipSuccess)
         return hip_fail(e);
-    if ((e = stage_mark("pool_k", stream)) != hipSuccess) return hip_fail(e);
+    if ((e = nsa::stage_mark("pool_k", stream)) != hipSuccess) return hip_fail(e);
     if (spec->head_shared) {
         float* mq = (float*)(ws + w.mq);
         float* mk = (float*)(ws + w.mk);
         if ((e = nsa::launch_head_mean(pq, g.B, g.Hq, g.NQ, g.D, mq, stream)) != hipSuccess) return hip_fail(e);
         if ((e = nsa::launch_head_mean(pk, g.B, g.Hkv, g.NK, g.D, mk, stream)) != hipSuccess) return hip_fail(e);
-        if ((e = stage_mark("head_mean", stream)) != hipSuccess) return hip_fail(e);
+        if ((e = nsa::stage_mark("head_mean", stream)) != hipSuccess) return hip_fail(e);
         *qh = mq;
         *kh = mk;
         *Hk = 1;
@@ -475,7 +478,7 @@ int score_and_topk(const Plan& p, const nsa_spec* spec, const void* qh, const fl
         hipError_t e = nsa::launch_scores(qh, kh, g.B, g.Hsel, Hk, g.group, h0, nh, g.NQ, g.NK, g.D, scores,
                                           stream, NKs, q_rows);
         if (e != hipSuccess) return hip_fail(e);
-        if ((e = stage_mark("scores", stream)) != hipSuccess) return hip_fail(e);
+        if ((e = nsa::stage_mark("scores", stream)) != hipSuccess) return hip_fail(e);
         nsa::TopkArgs ta;
         ta.scores = scores;
         ta.B = g.B;
@@ -515,7 +518,7 @@ int score_and_topk(const Plan& p, const nsa_spec* spec, const void* qh, const fl
         ta.keep = out->keep;
         ta.col_idx = out->col_idx;
         if ((e = nsa::launch_topk(ta, stream)) != hipSuccess) return hip_fail(e);
-        if ((e = stage_mark("topk", stream)) != hipSuccess) return hip_fail(e);
+        if ((e = nsa::stage_mark("topk", stream)) != hipSuccess) return hip_fail(e);
     }
     return NSA_OK;
 }
@@ -1406,12 +1409,12 @@ int nsa_decode_select(const nsa_tensor* q, const nsa_tensor* pooled_k, int32_t l
         // its single-row tile itself and nothing is launched for it here.
         float* pq = (float*)(ws + w.pq);
         const int q_rows = (g.Sq == 1 && !spec->head_shared) ? (g.bf16 ? 1 : 2) : 0;
-        hipError_t e = stage_mark("start", stream);
+        hipError_t e = nsa::stage_mark("start", stream);
         if (e != hipSuccess) return hip_fail(e);
         if (!q_rows) {
             e = nsa::launch_pool(q->data, g.bf16, (int64_t)g.B * g.Hq, g.Sq, g.D, spec->block_q, pq, stream);
             if (e != hipSuccess) return hip_fail(e);
-            if ((e = stage_mark("pool_q", stream)) != hipSuccess) return hip_fail(e);
+            if ((e = nsa::stage_mark("pool_q", stream)) != hipSuccess) return hip_fail(e);
         }
         const void* qh = q_rows ? q->data : (const void*)pq;
         const float* kh = (const float*)pooled_k->data;
@@ -1497,7 +1500,7 @@ int nsa_decode_attn_static(const nsa_tensor* q, const nsa_tensor* k_cache, const
 }
 
 int nsa_stage_timing_begin(void) {
-    StageTiming& t = t_stages;
+    nsa::StageTiming& t = nsa::t_stages;
     for (hipEvent_t ev : t.marks) (void)hipEventDestroy(ev);
     t.names.clear();
     t.marks.clear();
@@ -1506,7 +1509,7 @@ int nsa_stage_timing_begin(void) {
 }
 
 int nsa_stage_timing_end(nsa_stage_time* out, int32_t capacity, int32_t* count) {
-    StageTiming& t = t_stages;
+    nsa::StageTiming& t = nsa::t_stages;
     t.on = false;
     if (!count || (capacity > 0 && !out)) return NSA_ERR_NULL_ARG;
     int32_t n = 0;
@@ -1694,9 +1697,11 @@ int nsa_block_sparse_attn_bwd(const nsa_tensor* q, const nsa_tensor* k, const ns
     a.NK = (int)ceil_div(k->S, a.block_kv);
     const int bf16 = q->dtype == NSA_BF16;
 
-    hipError_t e = nsa::launch_bwd_delta(out->data, dout->data, bf16, (int64_t)q->B * q->H * q->S, q->D, delta,
-                                         stream);
+    hipError_t e = nsa::stage_mark("start", stream);
     if (e != hipSuccess) return hip_fail(e);
+    e = nsa::launch_bwd_delta(out->data, dout->data, bf16, (int64_t)q->B * q->H * q->S, q->D, delta, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if ((e = nsa::stage_mark("delta", stream)) != hipSuccess) return hip_fail(e);
     if (sel) {
         int32_t* counts = (int32_t*)(ws + w.counts);
         int32_t* col_ptr = (int32_t*)(ws + w.col_ptr);
@@ -1706,6 +1711,7 @@ int nsa_block_sparse_attn_bwd(const nsa_tensor* q, const nsa_tensor* k, const ns
                                        (int32_t)std::max<int64_t>(sel->nnz, 0), counts, col_ptr, sums, row_idx,
                                        stream);
         if (e != hipSuccess) return hip_fail(e);
+        if ((e = nsa::stage_mark("kv_index", stream)) != hipSuccess) return hip_fail(e);
         a.row_ptr = sel->row_ptr;
         a.col_idx = sel->col_idx;
         a.col_ptr = col_ptr;

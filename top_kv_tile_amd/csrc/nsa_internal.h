@@ -131,6 +131,9 @@ hipError_t launch_kv_major_index(const int8_t* keep, int BH, int NQ, int NK, int
 // bf16 MFMA path: block_q in {32, 64, 96, 128}, block_kv == 64, D in {64, 128}.
 bool attn_bwd_mfma_supported(const AttnBwdArgs& a, int bf16);
 hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t stream);
+// Stage timing: records an event named `name` on `stream` while timing is on
+// (nsa_stage_timing_begin / _end), else does nothing.
+hipError_t stage_mark(const char* name, hipStream_t stream);
 // General path (fp32 or bf16, any block sizes, D in {64, 128}).
 hipError_t launch_attn_bwd_simt(const AttnBwdArgs& a, int bf16, hipStream_t stream);
 

@@ -261,3 +261,19 @@ def test_decode_attn_static_rejects_before_launch(L):
              ctypes.byref(_t(1, 32, 32, 128)), None, None) == -1
     assert S(ctypes.byref(q), ctypes.byref(_t(1, 32, 131072, 128, N.NSA_F32)), ctypes.byref(kc), 131072, 0,
              None, ctypes.byref(_t(1, 32, 32, 128)), lse, None) == -3
+
+
+NULL_ARG = -1  # NSA_ERR_NULL_ARG (include/nsa.h)
+
+
+def test_stage_timing_host_side(L):
+    """Begin / end with nothing recorded needs no GPU: an empty list, and NULL_ARG
+    for a missing count or a missing buffer with capacity > 0."""
+    assert L.nsa_stage_timing_begin() == N.NSA_OK
+    n = ctypes.c_int32(-1)
+    assert L.nsa_stage_timing_end(None, 0, ctypes.byref(n)) == N.NSA_OK
+    assert n.value == 0
+    assert L.nsa_stage_timing_end(None, 0, None) == NULL_ARG
+    assert L.nsa_stage_timing_end(None, 4, ctypes.byref(n)) == NULL_ARG
+    tkt.nsa_stage_timing_begin()
+    assert tkt.nsa_stage_timing_end() == []

@@ -164,6 +164,20 @@ def test_growing_logits_move_the_softmax_reference(causal):
     say(f"  {rep}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_huge_logits_move_the_reference_by_the_guard(causal):
+    """q and k scaled by 16: logits reach thousands of scaled units, so a row's
+    exponentials against a stale reference overflow (inf) or pass 2^20, and the
+    kernel must take the row maximum and recompute those tiles; any slip gives
+    inf / NaN or O(1) errors. Softmax rows are nearly one-hot here."""
+    say(f"huge logits causal={causal}")
+    B, H, S, D = 1, 2, 2048, 128
+    q, k, v = _qkv(B, H, H, S, D, seed=37, dtype=torch.float32)
+    q, k, v = (q * 16).to(torch.bfloat16), (k * 16).to(torch.bfloat16), v.to(torch.bfloat16)
+    rep = run_case(q, k, v, tkt.SparseSpec(budget=0.5), causal, where="huge", relative=True)
+    say(f"  {rep}")
+
+
 @pytest.mark.parametrize("H,S", [(2, 2048), (16, 16384)])
 def test_all_tied_scores_pick_lowest_index(H, S):
     """q = 0: every score is +-0, so each row keeps its k_r lowest-index candidates

@@ -874,13 +874,14 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(TopkArgs a) {
 //
 // Selection of the k_r candidates with the largest scores (score
 // descending, index ascending), exact:
-//  1. non-candidates are set to -inf; hi = the largest candidate score, lo =
-//     the smallest score loaded (no larger than any candidate's);
-//  2. one histogram of 256 buckets over [lo, hi] (a monotone map, -inf to
-//     bucket 0, whose non-candidate count is taken out again) gives the
-//     bucket b* that holds the k-th largest candidate and the count above;
-//  3. every element in a bucket above b* is picked (a candidate: -inf is in
-//     the lowest bucket, never above b*);
+//  1. lo and hi = the smallest and largest score loaded (they bound the
+//     candidates);
+//  2. one histogram of 256 buckets over [lo, hi] (a monotone map; the bucket
+//     bytes of non-candidates are cleared to bucket 0, whose non-candidate
+//     count is taken out again) gives the bucket b* that holds the k-th
+//     largest candidate and the count above;
+//  3. every element in a bucket above b* is picked (a candidate: the others
+//     are in bucket 0, never above b*);
 //  4. the candidates of b* (few: a bucket holds about c / 256 scores unless
 //     scores crowd) are compacted by ballot into LDS and ranked against each
 //     other; the first `need` of them are picked.
@@ -893,6 +894,22 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(TopkArgs a) {
 __device__ __forceinline__ uint32_t bucket_of(float x, float scale, float off) {
     const float u = __builtin_amdgcn_fmed3f(__builtin_fmaf(x, scale, off), 0.0f, 255.0f);
     return (uint32_t)(int)u & 255u;
+}
+
+// Raw buffer resource over `bytes` bytes at p (stride 0): loads past the
+// end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+// Scale of the bucket map u = x * scale - lo * scale, which takes [lo, hi]
+// onto [0, 256]. Any positive finite scale keeps the map monotone, so an
+// approximate reciprocal serves; a range so small that the scale would not be
+// finite takes the largest finite one (lo is then tiny, so lo * scale stays
+// finite).
+__device__ __forceinline__ float bucket_scale(float lo, float hi) {
+    const float sc = 128.0f * __builtin_amdgcn_rcpf(0.5f * hi - 0.5f * lo);
+    return sc <= FLT_MAX ? sc : FLT_MAX;
 }
 
 // From a 256-bucket histogram (lane L owns buckets 4L .. 4L+3): the bucket b*
@@ -980,8 +997,12 @@ __device__ __forceinline__ uint32_t wave_or_u(uint32_t x) {
     return (uint32_t)wave_reduce((int)x, [](int p, int q) { return p | q; });
 }
 
+// The kernel waits on its loads and LDS atomics, so resident waves are what
+// hide the latency: it is held to five waves per SIMD (96 VGPRs). At that
+// budget only the crowded-bucket path keeps a few values in scratch; the
+// common path uses none.
 template <int G>
-__global__ __launch_bounds__(256, 3) void topk_grouped_kernel(TopkArgs a) {
+__global__ __launch_bounds__(256, 5) void topk_grouped_kernel(TopkArgs a) {
     constexpr int E = 4 * G;
     constexpr uint32_t kFull = E == 32 ? 0xFFFFFFFFu : ((1u << (E & 31)) - 1u);
     __shared__ uint32_t hist_all[4][256];
@@ -1011,18 +1032,22 @@ __global__ __launch_bounds__(256, 3) void topk_grouped_kernel(TopkArgs a) {
     const int dlo = (int)(qa / (uint32_t)a.block_kv);
     const int dhi = (int)((qa + (uint32_t)a.block_q + (uint32_t)a.block_kv - 1u) / (uint32_t)a.block_kv) - 1;
 
-    // Every load first (addresses clamped into the row, so none is conditional
-    // and all are in flight together), then the masks.
+    // Every load first, all in flight together. Buffer resources bound the
+    // score row and the mask rows: reads past a row's end (and every read of
+    // an absent mask, whose resource is empty) return zeros, so the loads
+    // need no clamping and no branches.
+    const __amdgpu_buffer_rsrc_t srs = row_rsrc(srow, a.NK * 4);
+    const __amdgpu_buffer_rsrc_t prs = row_rsrc(pw ? (const void*)pw : (const void*)srow, pw ? a.NKW * 8 : 0);
+    const __amdgpu_buffer_rsrc_t drs = row_rsrc(dw ? (const void*)dw : (const void*)srow, dw ? a.NKW * 8 : 0);
     f32x4 v[G];
     uint32_t pwv[G], dwv[G];
-    const int mw = lane >> 3;  // the lane's 32-bit half word within a group
+    const int mw4 = 4 * (lane >> 3);  // byte offset of the lane's 32-bit half word within a group
     const int msh = 4 * (lane & 7);
-    const int last_w = 2 * a.NKW - 1;
 #pragma unroll
     for (int x = 0; x < G; ++x) {
-        v[x] = *(const f32x4*)(srow + min(256 * x + 4 * lane, a.NK - 4));
-        pwv[x] = pw ? pw[min(8 * x + mw, last_w)] : 0u;
-        dwv[x] = dw ? dw[min(8 * x + mw, last_w)] : 0u;
+        v[x] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, 16 * lane, 1024 * x, 0));
+        pwv[x] = __builtin_amdgcn_raw_buffer_load_b32(prs, mw4, 32 * x, 0);
+        dwv[x] = __builtin_amdgcn_raw_buffer_load_b32(drs, mw4, 32 * x, 0);
     }
 
     // Row masks (bit 4 x + c). Groups of this lane inside the row: 256 x + 4 L < NK.
@@ -1043,34 +1068,36 @@ __global__ __launch_bounds__(256, 3) void topk_grouped_kernel(TopkArgs a) {
         }
     }
     uint32_t pin = 0, drop = 0;
-    if (pw) {
 #pragma unroll
-        for (int x = 0; x < G; ++x) pin |= ((pwv[x] >> msh) & 0xFu) << (4 * x);
-    }
-    if (dw) {
-#pragma unroll
-        for (int x = 0; x < G; ++x) drop |= ((dwv[x] >> msh) & 0xFu) << (4 * x);
+    for (int x = 0; x < G; ++x) {
+        pin |= ((pwv[x] >> msh) & 0xFu) << (4 * x);
+        drop |= ((dwv[x] >> msh) & 0xFu) << (4 * x);
     }
     const uint32_t forced = (diag | pin) & ~drop & valid;  // kept whatever the scores
     const uint32_t cand = valid & ~(diag | pin | drop);
 
-    // Non-candidates become -inf (a select on the candidate bit spread to a
-    // full-word mask), so later passes need no masks.
-    float s[E];
-    const float kInf = __builtin_huge_valf();
-    float lo = kInf, hi = -kInf;
+    // Scores stay as loaded; non-candidates are taken out of the search by
+    // their bucket bytes (set to bucket 0 below) and by the candidate mask
+    // wherever a bucket is matched. lo and hi bound every valid score loaded,
+    // so they bound the candidates; groups past a ragged row end (zeros) take
+    // the row's first score instead.
+    if (a.NK & 255) {  // wave-uniform
+        const float v0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v[0][0]), 0));
 #pragma unroll
-    for (int t = 0; t < E; ++t) {
-        const float sv = v[t >> 2][t & 3];
-        const uint32_t m = (uint32_t)((int32_t)(cand << (31 - t)) >> 31);  // all ones for a candidate
-        s[t] = __uint_as_float((__float_as_uint(sv) & m) | (__float_as_uint(-kInf) & ~m));
-        hi = fmaxf(hi, s[t]);
-        lo = fminf(lo, sv);
+        for (int x = 0; x < G; ++x)
+            if (x >= nvg) v[x] = (f32x4){v0, v0, v0, v0};
+    }
+    float lo = v[0][0], hi = v[0][0];
+#pragma unroll
+    for (int x = 0; x < G; ++x) {
+        lo = fminf(lo, fminf(fminf(v[x][0], v[x][1]), fminf(v[x][2], v[x][3])));
+        hi = fmaxf(hi, fmaxf(fmaxf(v[x][0], v[x][1]), fmaxf(v[x][2], v[x][3])));
     }
     const int c = wave_sum_i(__builtin_popcount(cand));
     // k_r = ceil(fl32(c) * fl32(budget)): the product rounds to fp32 first.
     const float kf = ceilf(__fmul_rn((float)c, a.budget));
     const int k = (kf >= (float)c) ? c : (int)kf;
+    const float kInf = __builtin_huge_valf();
 
     uint32_t picked = forced;  // row-mask layout
     uint32_t bk[G];            // bucket bytes
@@ -1092,8 +1119,9 @@ __global__ __launch_bounds__(256, 3) void topk_grouped_kernel(TopkArgs a) {
             cut_mask = cand;
             cut_need = k;
         } else {
-            // First pass over every element; non-candidates (-inf) land in bucket 0.
-            float scale = 128.0f / (0.5f * hi - 0.5f * lo);
+            // First pass over every element; the bytes of non-candidates are
+            // cleared, so they count in bucket 0.
+            float scale = bucket_scale(lo, hi);
             float off = -lo * scale;
             *(u32x4*)(hist + 4 * lane) = (u32x4){0u, 0u, 0u, 0u};
             wave_lds_sync();
@@ -1101,11 +1129,11 @@ __global__ __launch_bounds__(256, 3) void topk_grouped_kernel(TopkArgs a) {
             for (int x = 0; x < G; ++x) {
                 uint32_t w = 0;
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    // u8 conversion saturates: monotone, -inf to 0, above 255 to 255
-                    w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s[4 * x + cc], scale, off), cc, w);
-                    atomicAdd(&hist[(w >> (8 * cc)) & 255u], 1u);
-                }
+                for (int cc = 0; cc < 4; ++cc)  // u8 conversion saturates: monotone, clamped to 0 .. 255
+                    w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(v[x][cc], scale, off), cc, w);
+                w &= spread_nibble((cand >> (4 * x)) & 0xFu) * 0xFFu;
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) atomicAdd(&hist[(w >> (8 * cc)) & 255u], 1u);
                 bk[x] = w;
             }
             wave_lds_sync();
@@ -1134,8 +1162,8 @@ __global__ __launch_bounds__(256, 3) void topk_grouped_kernel(TopkArgs a) {
 #pragma unroll
                     for (int t = 0; t < E; ++t) {
                         const bool on = (active >> t) & 1u;
-                        blo = fminf(blo, on ? s[t] : kInf);
-                        bhi = fmaxf(bhi, on ? s[t] : -kInf);
+                        blo = fminf(blo, on ? v[t >> 2][t & 3] : kInf);
+                        bhi = fmaxf(bhi, on ? v[t >> 2][t & 3] : -kInf);
                     }
                     blo = wave_min_f(blo);
                     bhi = wave_max_f(bhi);
@@ -1144,21 +1172,21 @@ __global__ __launch_bounds__(256, 3) void topk_grouped_kernel(TopkArgs a) {
                         cut_need = need;
                         break;
                     }
-                    scale = 128.0f / (0.5f * bhi - 0.5f * blo);
+                    scale = bucket_scale(blo, bhi);
                     off = -blo * scale;
                     wave_lds_sync();
                     *(u32x4*)(hist + 4 * lane) = (u32x4){0u, 0u, 0u, 0u};
                     wave_lds_sync();
 #pragma unroll
                     for (int t = 0; t < E; ++t)
-                        if ((active >> t) & 1u) atomicAdd(&hist[bucket_of(s[t], scale, off)], 1u);
+                        if ((active >> t) & 1u) atomicAdd(&hist[bucket_of(v[t >> 2][t & 3], scale, off)], 1u);
                     wave_lds_sync();
                     int b2, ab2, in2;
                     find_bucket(hist, need, lane, b2, ab2, in2);
                     uint32_t next = 0, up = 0;
 #pragma unroll
                     for (int t = 0; t < E; ++t) {
-                        const uint32_t bb = bucket_of(s[t], scale, off);
+                        const uint32_t bb = bucket_of(v[t >> 2][t & 3], scale, off);
                         next |= (uint32_t)(bb == (uint32_t)b2) << t;
                         up |= (uint32_t)(bb > (uint32_t)b2) << t;
                     }
@@ -1192,7 +1220,7 @@ __global__ __launch_bounds__(256, 3) void topk_grouped_kernel(TopkArgs a) {
                     const uint64_t m = __ballot(on);
                     if (on)
                         list[n + __builtin_popcountll(m & below)] =
-                            make_uint2(__float_as_uint(s[4 * x + cc]), (uint32_t)(256 * x + 4 * lane + cc));
+                            make_uint2(__float_as_uint(v[x][cc]), (uint32_t)(256 * x + 4 * lane + cc));
                     n += __builtin_popcountll(m);
                 }
             }

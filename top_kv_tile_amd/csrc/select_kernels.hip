@@ -896,6 +896,20 @@ __device__ __forceinline__ uint32_t bucket_of(float x, float scale, float off) {
     return (uint32_t)(int)u & 255u;
 }
 
+// Three-operand minimum and maximum of finite scores. Written as the
+// instructions themselves: through fminf / fmaxf the compiler first
+// canonicalises every loaded value (one extra instruction per score).
+__device__ __forceinline__ float min3f(float a, float b, float c) {
+    float r;
+    asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Raw buffer resource over `bytes` bytes at p (stride 0): loads past the
 // end return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, int bytes) {
@@ -965,6 +979,21 @@ __device__ __forceinline__ int kth_index(uint32_t m, int r, int lane) {
         r -= total;
     }
     return res;
+}
+
+// Number of this lane's elements (256 x + 4 L + c, x < G) below index d >= 0.
+template <int G>
+__device__ __forceinline__ int lane_elems_below(int d, int lane) {
+    const int q = d >> 8;
+    const int part = min(max((d & 255) - 4 * lane, 0), 4);
+    return q >= G ? 4 * G : 4 * q + part;
+}
+
+// Bits a .. b - 1 of a 32-bit word (0 <= a, b <= 32); empty when a >= b.
+__device__ __forceinline__ uint32_t bit_range(int a, int b) {
+    const uint32_t upto = b >= 32 ? ~0u : ((1u << b) - 1u);
+    const uint32_t from = a >= 32 ? 0u : ~((1u << a) - 1u);
+    return upto & from;
 }
 
 // Nibble of the bits lo..hi (clipped to 0..3); empty when lo > hi.
@@ -1053,20 +1082,10 @@ __global__ __launch_bounds__(256, 5) void topk_grouped_kernel(TopkArgs a) {
     // Row masks (bit 4 x + c). Groups of this lane inside the row: 256 x + 4 L < NK.
     const int nvg = (a.NK - 4 * lane + 255) >> 8;
     const uint32_t valid = nvg >= G ? kFull : ((1u << (4 * nvg)) - 1u);
-    uint32_t diag = 0;
-    {
-        const int d0 = dlo, d1 = min(dhi, a.NK - 1);
-        if (d1 - d0 < 8) {  // the usual few diagonal tiles, one by one (wave-uniform loop)
-            for (int e = d0; e <= d1; ++e)
-                if (((e & 255) >> 2) == lane) diag |= 1u << (4 * (e >> 8) + (e & 3));
-        } else {
-#pragma unroll
-            for (int x = 0; x < G; ++x) {
-                const int e0 = 256 * x + 4 * lane;
-                diag |= nibble_range(d0 - e0, d1 - e0) << (4 * x);
-            }
-        }
-    }
+    // A lane's elements increase with their bit 4 x + c, so the diagonal
+    // tiles d0 .. d1 are the bits from (elements below d0) to (elements below
+    // d1 + 1).
+    const uint32_t diag = bit_range(lane_elems_below<G>(dlo, lane), lane_elems_below<G>(min(dhi, a.NK - 1) + 1, lane));
     uint32_t pin = 0, drop = 0;
 #pragma unroll
     for (int x = 0; x < G; ++x) {
@@ -1090,8 +1109,8 @@ __global__ __launch_bounds__(256, 5) void topk_grouped_kernel(TopkArgs a) {
     float lo = v[0][0], hi = v[0][0];
 #pragma unroll
     for (int x = 0; x < G; ++x) {
-        lo = fminf(lo, fminf(fminf(v[x][0], v[x][1]), fminf(v[x][2], v[x][3])));
-        hi = fmaxf(hi, fmaxf(fmaxf(v[x][0], v[x][1]), fmaxf(v[x][2], v[x][3])));
+        lo = min3f(min3f(lo, v[x][0], v[x][1]), v[x][2], v[x][3]);
+        hi = max3f(max3f(hi, v[x][0], v[x][1]), v[x][2], v[x][3]);
     }
     const int c = wave_sum_i(__builtin_popcount(cand));
     // k_r = ceil(fl32(c) * fl32(budget)): the product rounds to fp32 first.
@@ -1108,8 +1127,12 @@ __global__ __launch_bounds__(256, 5) void topk_grouped_kernel(TopkArgs a) {
     if (k >= c) {
         picked |= cand;
     } else if (k > 0) {
-        lo = wave_min_f(lo);
-        hi = wave_max_f(hi);
+        // (the same value in every lane; read out as a scalar so that the
+        // compiler treats what follows as wave-uniform)
+        lo = __uint_as_float(__builtin_amdgcn_readfirstlane(
+            __float_as_uint(wave_reduce(lo, [](float p, float q) { return min3f(p, q, q); }))));
+        hi = __uint_as_float(__builtin_amdgcn_readfirstlane(
+            __float_as_uint(wave_reduce(hi, [](float p, float q) { return max3f(p, q, q); }))));
         uint32_t cut_mask = 0;  // if cut_need > 0: the first cut_need of cut_mask, in index order
         int cut_need = 0;
         uint32_t eqb[G];  // byte form, high bit: the candidates of the bucket to rank
@@ -1131,7 +1154,9 @@ __global__ __launch_bounds__(256, 5) void topk_grouped_kernel(TopkArgs a) {
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc)  // u8 conversion saturates: monotone, clamped to 0 .. 255
                     w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(v[x][cc], scale, off), cc, w);
-                w &= spread_nibble((cand >> (4 * x)) & 0xFu) * 0xFFu;
+                // Byte mask of the group's candidates: a byte permute whose
+                // selector is 12 (a zero byte) or 13 (an all-ones byte).
+                w &= __builtin_amdgcn_perm(0u, 0u, 0x0C0C0C0Cu + spread_nibble((cand >> (4 * x)) & 0xFu));
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) atomicAdd(&hist[(w >> (8 * cc)) & 255u], 1u);
                 bk[x] = w;
@@ -1266,11 +1291,16 @@ __global__ __launch_bounds__(256, 5) void topk_grouped_kernel(TopkArgs a) {
     // Kept flags per group, byte form: forced and rank-picked tiles, buckets above b*.
     const uint32_t yrep = (uint32_t)min(bstar + 1, 255) * 0x01010101u;
     const uint32_t hmask = bstar < 255 ? 0x80808080u : 0u;
-    uint32_t kb[G];
+    uint32_t kb[G], pk[G];  // this lane's pick words, read together (one LDS wait)
+#pragma unroll
+    for (int x = 0; x < G; ++x) pk[x] = 0u;
+    if (in_bucket) {
+#pragma unroll
+        for (int x = 0; x < G; ++x) pk[x] = pick[G * lane + x];
+    }
 #pragma unroll
     for (int x = 0; x < G; ++x) {
-        kb[x] = spread_nibble((picked >> (4 * x)) & 0xFu) | ((bytes_at_least(bk[x], yrep) & hmask) >> 7);
-        if (in_bucket) kb[x] |= pick[G * lane + x];
+        kb[x] = spread_nibble((picked >> (4 * x)) & 0xFu) | ((bytes_at_least(bk[x], yrep) & hmask) >> 7) | pk[x];
         const int e0 = 256 * x + 4 * lane;
         if (e0 < a.NK) *(uint32_t*)(krow + e0) = kb[x];
     }

@@ -563,15 +563,25 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_mfma_kernel(AttnBwdArgs a) 
 
 // ============================================================ dK / dV (MFMA)
 //
-// Workgroup = 4 waves on one kv tile of 64 keys; wave w owns keys 32 (w & 1)
-// .. + 31 and queries 32 (w >> 1) .. + 31 of every 64-query chunk ("unit").
-// K and V fragments stay in registers. Units are walked head by head over the
-// group, each head's query tiles ascending, and streamed through four LDS
-// stages (Q chunk, dO chunk, and per wave the LSE and Delta of its 32 queries,
-// all by buffer-to-LDS DMA): units n + 1 .. n + 3 are in flight while unit n is computed,
-// and every wave issues the same number of loads per unit, so a partial vmcnt
-// wait tells unit n has landed. At the end the two waves of each key half add
-// their partial dK^T / dV^T through LDS.
+// Workgroup = 8 waves on one kv tile of 64 keys, two per SIMD. A unit is 64
+// queries (a "chunk") of one query head of the group; each 32-key x 32-query
+// block of it (key half kb, query half qs) belongs to a pair of waves:
+//  - the P wave (waves 0..3) computes S = Q K^T and P = exp(S scale - LSE),
+//    hands P to its partner through LDS and accumulates dV^T += dO^T P;
+//  - the dS wave (waves 4..7) computes dP = dO V^T, takes P, forms
+//    dS = P (dP - Delta) and accumulates dK^T += Q^T dS.
+// Each wave thus runs half the products of its block, and the two waves of a
+// pair sit on one SIMD (wave w and w + 4), so the vector work and the waits
+// of one overlap the matrix products of the other. K (P waves) or V (dS
+// waves) fragments stay in registers.
+// Units are walked head by head over the group, each head's query tiles
+// ascending, and streamed through four LDS stages (Q chunk, dO chunk, and per
+// wave the LSE or Delta of its 32 queries, all by buffer-to-LDS DMA): units
+// n + 1 .. n + 3 are in flight while unit n is computed, and every wave
+// issues the same number of loads per unit, so a partial vmcnt wait tells
+// unit n has landed. Two barriers per unit: the first ends every wave's reads
+// of the stage refilled next, the second publishes P. At the end the two
+// query halves of each key half add their partial dK^T / dV^T through LDS.
 // Workgroups run kv-tile major (tile 0 of every kv head first): under causal,
 // early tiles are seen by the most query tiles, and a pinned tile (a sink) by
 // every one of them, so the longest work starts first.
@@ -582,28 +592,32 @@ struct Unit {
 template <int D>
 struct DkdvLds {
     static constexpr int TILEB = 64 * D * 2;
-    static constexpr int NST = 4;  // stages: the unit in work, the next one, two in flight
-    static constexpr int SIDE = 4 * 2 * 64 * 4;       // per stage: 4 waves x (LSE, Delta) x 64 floats
+    static constexpr int NST = 4;                    // stages: the unit in work, the next one, two in flight
+    static constexpr int SIDE = 8 * 64 * 4;          // per stage: 8 waves x 64 floats (LSE or Delta)
     static constexpr int STAGEB = 2 * TILEB + SIDE;  // a stage: Q chunk, dO chunk, side values
-    static constexpr int BYTES = NST * STAGEB;
-    static_assert(2 * 2 * (D / 32) * 16 * 64 * 4 <= BYTES, "reduction buffer fits the stages");
+    static constexpr int PX = 4 * 16 * 64 * 4;       // P of the four blocks, fp32, 16 per lane
+    static constexpr int BYTES = NST * STAGEB + PX;
+    static_assert(2 * 2 * 2 * (D / 32) * 16 * 64 * 4 <= BYTES, "reduction buffer fits");
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
     constexpr int KSTEPS = D / 16;
     constexpr int DBLK = D / 32;
-    constexpr int NW = 4;
+    constexpr int NW = 8;
     using G = Geo<D>;
     using L = DkdvLds<D>;
-    constexpr int PER_UNIT = 2 * (G::NINSTR / NW) + 2;  // vector memory instructions per wave per unit
+    static_assert(G::NINSTR % NW == 0, "every wave issues the same number of DMA instructions");
+    constexpr int IPW = G::NINSTR / NW;
+    constexpr int PER_UNIT = 2 * IPW + 1;  // vector memory instructions per wave per unit
     extern __shared__ __attribute__((aligned(1024))) char lds[];
     const uint32_t lds0 = lds_address(lds);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool pwave = wave < 4;  // P wave (S, P, dV) or dS wave (dP, dS, dK)
     const int l32 = lane & 31, hf = lane >> 5;
-    const int kb = wave & 1, qs = wave >> 1;
+    const int kb = wave & 1, qs = (wave >> 1) & 1;
     const int64_t BH = (int64_t)a.B * a.Hkv;
     const int j = (int)(blockIdx.x / BH);
     const int g = (int)(blockIdx.x % BH % a.Hkv);
@@ -615,16 +629,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
 
     const int head_bytes = a.S * G::ROWB;
     const int64_t khead = ((int64_t)b * a.Hkv + g) * a.S;
-    bf16x8 kf[KSTEPS], vf[KSTEPS];
+    // K fragments (P waves) or V fragments (dS waves) of this wave's 32 keys.
+    bf16x8 kvf[KSTEPS];
     {
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc((const uint16_t*)a.k + khead * D, head_bytes);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const uint16_t*)a.v + khead * D, head_bytes);
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc((const uint16_t*)(pwave ? a.k : a.v) + khead * D, head_bytes);
         const int off = (mykey * D + 8 * hf) * 2;  // past S: zeros
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            kf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 32 * ks, 0, 0));
-            vf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 32 * ks, 0, 0));
-        }
+        for (int ks = 0; ks < KSTEPS; ++ks)
+            kvf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * ks, 0, 0));
         // Settle these before any DMA: from here on every vmcnt wait is explicit.
         __builtin_amdgcn_s_waitcnt(kVmcnt0);
     }
@@ -663,13 +676,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
     };
 
     // Loads of unit u into stage st: Q and dO chunks and, for this wave's 32
-    // queries, the raw LSE and Delta. Per-lane offsets inside a chunk are the
-    // same for every unit (bswz layout); a chunk is selected by the base of
-    // its buffer resource, whose record count ends at query S - 1, so rows
-    // past it read as zeros (those queries are masked: P = 0, dS = 0). Every
-    // lane of every wave takes part, so each wave issues PER_UNIT loads.
-    static_assert(G::NINSTR % NW == 0, "every wave issues the same number of DMA instructions");
-    constexpr int IPW = G::NINSTR / NW;
+    // queries, the raw LSE (P waves) or Delta (dS waves). Per-lane offsets
+    // inside a chunk are the same for every unit (bswz layout); a chunk is
+    // selected by the base of its buffer resource, whose record count ends at
+    // query S - 1, so rows past it read as zeros (those queries are masked:
+    // P = 0, dS = 0). Every lane of every wave takes part, so each wave
+    // issues PER_UNIT loads.
     int tvo[IPW];
 #pragma unroll
     for (int x = 0; x < IPW; ++x) {
@@ -679,16 +691,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
     }
     // Query rows are counted from the first row of the group's first head.
     const int64_t grow0 = ((int64_t)b * a.Hq + g * GRP) * a.S;
-    const char* qgrp = (const char*)a.q + grow0 * G::ROWB;
-    const char* dgrp = (const char*)a.dout + grow0 * G::ROWB;
-    const float* lgrp = a.lse + grow0;
-    const float* egrp = a.delta + grow0;
+    // Group base addresses; a unit's byte offsets from them fit in 32 bits
+    // (the host keeps the group's rows below 2^32 bytes).
+    const uint64_t qgrp = (uint64_t)a.q + (uint64_t)grow0 * G::ROWB;
+    const uint64_t dgrp = (uint64_t)a.dout + (uint64_t)grow0 * G::ROWB;
+    const uint64_t sgrp = (uint64_t)(pwave ? a.lse : a.delta) + (uint64_t)grow0 * 4;
+    auto words = [](uint64_t base, uint32_t off, uint32_t bytes) -> u32x4 {
+        const uint64_t p = base + off;
+        return (u32x4){(uint32_t)p, (uint32_t)(p >> 32) & 0xFFFFu, bytes, 0x00020000u};
+    };
     auto issue = [&](const Unit& u, int st) {
         const int row0 = u.i * bq + 64 * u.c;
-        const int64_t trow = (int64_t)u.hh * a.S + row0;
+        const uint32_t trow = (uint32_t)(u.hh * a.S + row0);
         const uint32_t tbytes = (uint32_t)(a.S - row0) * G::ROWB;
-        const u32x4 rq = rsrc_words(qgrp + trow * G::ROWB, tbytes);
-        const u32x4 rd = rsrc_words(dgrp + trow * G::ROWB, tbytes);
+        const u32x4 rq = words(qgrp, trow * G::ROWB, tbytes);
+        const u32x4 rd = words(dgrp, trow * G::ROWB, tbytes);
         const uint32_t lq = lds0 + st * L::STAGEB;
 #pragma unroll
         for (int x = 0; x < IPW; ++x) dma16(rq, lq + (wave + NW * x) * 1024, tvo[x]);
@@ -696,26 +713,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
         for (int x = 0; x < IPW; ++x) dma16(rd, lq + G::TILEB + (wave + NW * x) * 1024, tvo[x]);
         const int srow = 32 * qs;  // lanes 32..63 fetch values no one reads
         const uint32_t sbytes = (uint32_t)max(a.S - row0 - srow, 0) * 4;
-        const uint32_t ls = lq + 2 * G::TILEB + wave * 512;
-        dma4(rsrc_words(lgrp + trow + srow, sbytes), ls, lane * 4);
-        dma4(rsrc_words(egrp + trow + srow, sbytes), ls + 256, lane * 4);
+        dma4(words(sgrp, (trow + srow) * 4u, sbytes), lq + 2 * G::TILEB + wave * 256, lane * 4);
     };
 
-    f32x16 dk[DBLK], dv[DBLK];
+    f32x16 acc[DBLK];  // dV^T (P waves) or dK^T (dS waves), partial over this wave's queries
 #pragma unroll
-    for (int m = 0; m < DBLK; ++m) {
-        dk[m] = (f32x16){};
-        dv[m] = (f32x16){};
-    }
+    for (int m = 0; m < DBLK; ++m) acc[m] = (f32x16){};
 
     // Per-lane LDS offsets within a stage, the same for every unit: row
-    // fragments of this wave's queries (chunk 2 ks + hf of row qr), and the
-    // two halves of the transposed fragments (rows 32 qs + 4 hf + (0..3) and
-    // + 8, column block m; the second k-step is 16 rows further on).
+    // fragments of this wave's queries (Q for P waves, dO for dS waves: chunk
+    // 2 ks + hf of row qr), and the two halves of the transposed fragments
+    // (dO for P waves, Q for dS waves: rows 32 qs + 4 hf + (0..3) and + 8,
+    // column block m; the second k-step is 16 rows further on).
     const int qr = 32 * qs + l32;
+    const int rbase = pwave ? 0 : G::TILEB;  // row-read tile
+    const int tbase = pwave ? G::TILEB : 0;  // transposed-read tile
     int roff[KSTEPS], tlo[DBLK], thi[DBLK];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) roff[ks] = qr * G::ROWB + ((2 * ks + hf) ^ G::bswz(qr)) * 16;
+    for (int ks = 0; ks < KSTEPS; ++ks) roff[ks] = rbase + qr * G::ROWB + ((2 * ks + hf) ^ G::bswz(qr)) * 16;
     {
         const int vg = lane >> 4, vs = lane & 15;
         const int r0 = 32 * qs + 4 * hf + (vs >> 2), r1 = r0 + 8;
@@ -723,11 +738,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
         for (int m = 0; m < DBLK; ++m) {
             const int d = 32 * m + 16 * (vg & 1) + 4 * (vs & 3);
             const int c = d >> 3, bo = (d & 7) * 2;
-            tlo[m] = r0 * G::ROWB + (c ^ G::bswz(r0)) * 16 + bo;
-            thi[m] = r1 * G::ROWB + (c ^ G::bswz(r1)) * 16 + bo;
+            tlo[m] = tbase + r0 * G::ROWB + (c ^ G::bswz(r0)) * 16 + bo;
+            thi[m] = tbase + r1 * G::ROWB + (c ^ G::bswz(r1)) * 16 + bo;
         }
     }
-    const int soff = 2 * G::TILEB + wave * 512 + 16 * hf;  // this wave's LSE (Delta 256 bytes on)
+    const int soff = 2 * G::TILEB + wave * 256 + 16 * hf;  // this wave's LSE or Delta
+    // P of this wave's block (written by the P wave, read by the dS wave of
+    // the pair): element x of lane l at float (x / 4) * 256 + 4 l + x % 4.
+    float* px = (float*)(lds + L::NST * L::STAGEB) + (wave & 3) * 1024 + 4 * lane;
     auto rowf = [&](const char* p, int ks) -> bf16x8 {
         return __builtin_bit_cast(bf16x8, *(const u32x4*)(p + roff[ks]));
     };
@@ -738,12 +756,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
         return __builtin_bit_cast(bf16x8, w);
     };
     // Software pipeline over units, one unit deep: an iteration finishes unit
-    // `cur` (its P / dS and the dV / dK products) while it computes S and dP of
-    // the next unit, so the vector arithmetic of one unit runs beside the
-    // matrix products of the next. Unit cur sits in stage st, the next units
-    // nx[0], nx[1], ... in the following stages (valid while hv[]). When an
-    // iteration starts, cur and nx[0] are resident and nx[1] is in flight; it
-    // issues one more unit into the stage of the unit before cur.
+    // `cur` while it computes S (P waves) or dP (dS waves) of the next unit.
+    // Unit cur sits in stage st, the next units nx[0], nx[1], ... in the
+    // following stages (valid while hv[]). When an iteration starts, cur and
+    // nx[0] are resident and nx[1] is in flight; it issues one more unit into
+    // the stage of the unit before cur.
     constexpr int NST = L::NST;
     static_assert(NST == 4, "the waits below assume four stages");
     Unit cur;
@@ -775,26 +792,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
             }
         }
     }
-    // S = Q K^T and dP = dO V^T of the first unit (stage 0), for this wave's 32 queries x 32 keys.
-    f32x16 s = (f32x16){}, dp = (f32x16){};
+    // S (or dP) of the first unit (stage 0), for this wave's 32 queries x 32 keys.
+    f32x16 sc = (f32x16){};
     if (have) {
         // unit cur has landed once at most the units issued after it are outstanding
         if (hv[1]) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER_UNIT));
         else if (hv[0]) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_UNIT));
         else __builtin_amdgcn_s_waitcnt(kVmcnt0);
         bare_barrier();
-        bf16x8 qa[KSTEPS], da[KSTEPS];
+        bf16x8 ra[KSTEPS];
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            qa[ks] = rowf(lds, ks);
-            da[ks] = rowf(lds + G::TILEB, ks);
-        }
+        for (int ks = 0; ks < KSTEPS; ++ks) ra[ks] = rowf(lds, ks);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            s = mfma(qa[ks], kf[ks], s);
-            dp = mfma(da[ks], vf[ks], dp);
-        }
+        for (int ks = 0; ks < KSTEPS; ++ks) sc = mfma(ra[ks], kvf[ks], sc);
     }
     int st = 0;
     while (have) {
@@ -804,94 +815,106 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
         if (hv[1]) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_UNIT));
         else __builtin_amdgcn_s_waitcnt(kVmcnt0);
         bare_barrier();
-        if (hv[1]) {
-            bool ok = false;
-            const Unit u = advance(nx[1], ok);
-            if (ok) {
-                nx[2] = u;
-                hv[2] = true;
-                issue(u, (st + 3) & 3);
+        // The walk to the unit after nx[1] and its loads (into the stage of
+        // the unit before cur, free since the barrier), placed after this
+        // wave's products are issued so that its scalar work runs beside them.
+        auto next_unit = [&]() {
+            if (hv[1]) {
+                bool ok = false;
+                const Unit u = advance(nx[1], ok);
+                if (ok) {
+                    nx[2] = u;
+                    hv[2] = true;
+                    issue(u, (st + 3) & 3);
+                }
             }
-        }
+        };
         const int st1 = (st + 1) & 3;
         const char* sp = lds + st * L::STAGEB;
         const char* sp1 = lds + st1 * L::STAGEB;
-        // Side values of unit cur, then the row fragments of the next unit (stale
-        // but harmless when there is none: its products are then discarded).
-        f32x4 lo[4], de[4];
+        // Side values of unit cur, then the row fragments of the next unit
+        // (stale but harmless when there is none: its products are then discarded).
+        f32x4 side[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            lo[q] = *(const f32x4*)(sp + soff + 32 * q);
-            de[q] = *(const f32x4*)(sp + soff + 256 + 32 * q);
-        }
-        bf16x8 qa[KSTEPS], da[KSTEPS];
+        for (int q = 0; q < 4; ++q) side[q] = *(const f32x4*)(sp + soff + 32 * q);
+        bf16x8 ra[KSTEPS];
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            qa[ks] = rowf(sp1, ks);
-            da[ks] = rowf(sp1 + G::TILEB, ks);
-        }
-        // Lane holds key mykey (column) and queries 32 qs + 8 q + 4 hf + e (chunk rows) at [4 q + e].
-        // Element masks only where this wave's block is partial: under causal
-        // when a key may follow a query, and past the tile end or S. A query
-        // with LSE = -inf sees no key at all, so under causal every pair of its
-        // row here is masked, and without causal it cannot occur in a kept tile.
-        const int tq0 = cur.i * bq + 64 * cur.c + 32 * qs;
-        const int t_lim = min(a.S, cur.i * bq + bq);  // queries of this unit are below t_lim
-        const bool need_mask = (a.causal && key0 + 32 * kb + 31 > tq0) || (tq0 + 31 >= t_lim);
-        const int key_lim = a.causal ? mykey : -1;
-        bf16x8 pf[2], dsf[2];
-        f32x16 s2 = (f32x16){}, dp2 = (f32x16){};
-        auto step = [&](auto masked) {
+        for (int ks = 0; ks < KSTEPS; ++ks) ra[ks] = rowf(sp1, ks);
+        f32x16 sn = (f32x16){};
+        bf16x8 opf[2];  // bf16 operand of this wave's product: P or dS
+        if (pwave) {
+            // Lane holds key mykey (column) and queries 32 qs + 8 q + 4 hf + e
+            // (chunk rows) at [4 q + e]. Element masks only where this block is
+            // partial: under causal when a key may follow a query, and past the
+            // tile end or S. A query with LSE = -inf sees no key at all, so
+            // under causal every pair of its row here is masked, and without
+            // causal it cannot occur in a kept tile.
+            const int tq0 = cur.i * bq + 64 * cur.c + 32 * qs;
+            const int t_lim = min(a.S, cur.i * bq + bq);  // queries of this unit are below t_lim
+            const bool need_mask = (a.causal && key0 + 32 * kb + 31 > tq0) || (tq0 + 31 >= t_lim);
+            const int key_lim = a.causal ? mykey : -1;
+            auto step = [&](auto masked) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    f32x4 pq;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int x = 4 * q + e;
+                        float p = fast_exp2(__builtin_fmaf(sc[x], a.scale_log2, -kLog2e * side[q][e]));
+                        if (decltype(masked)::value) {
+                            const int t = tq0 + 8 * q + 4 * hf + e;
+                            p = (t < t_lim && key_lim <= t) ? p : 0.f;
+                        }
+                        pq[e] = p;
+                        opf[x >> 3][x & 7] = (__bf16)p;
+                    }
+                    *(f32x4*)(px + 256 * q) = pq;
+                }
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks) sn = mfma(ra[ks], kvf[ks], sn);
+                // One product, then a share of the vector work, eight times over.
+#pragma unroll
+                for (int x = 0; x < KSTEPS; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, decltype(masked)::value ? 9 : 6, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            // Two copies, so that full blocks (the common case) carry no mask arithmetic.
+            if (need_mask) step(std::true_type{});
+            else step(std::false_type{});
+            next_unit();
+            bare_barrier();  // P of this unit is in LDS for the dS waves
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) sn = mfma(ra[ks], kvf[ks], sn);
+            next_unit();
+            bare_barrier();  // P of this unit is in LDS
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 pq = *(const f32x4*)(px + 256 * q);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int x = 4 * q + e;
-                    float p = fast_exp2(__builtin_fmaf(s[x], a.scale_log2, -kLog2e * lo[q][e]));
-                    if (decltype(masked)::value) {
-                        const int t = tq0 + 8 * q + 4 * hf + e;
-                        p = (t < t_lim && key_lim <= t) ? p : 0.f;
-                    }
-                    const float ds = p * (dp[x] - de[q][e]);
-                    pf[x >> 3][x & 7] = (__bf16)p;
-                    dsf[x >> 3][x & 7] = (__bf16)ds;
+                    opf[x >> 3][x & 7] = (__bf16)(pq[e] * (sc[x] - side[q][e]));
                 }
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                s2 = mfma(qa[ks], kf[ks], s2);
-                dp2 = mfma(da[ks], vf[ks], dp2);
-            }
-            // One product, then a share of the vector work, sixteen times over.
-#pragma unroll
-            for (int x = 0; x < 2 * KSTEPS; ++x) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, decltype(masked)::value ? 10 : 7, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        // Two copies, so that full blocks (the common case) carry no mask arithmetic.
-        if (need_mask) step(std::true_type{});
-        else step(std::false_type{});
-        // dV^T += dO^T P and dK^T += Q^T dS; contraction over this wave's queries,
-        // k-step s covering rows 32 qs + 16 s + 4 hf + (0..3) and + 8.
-#pragma unroll
-        for (int s3 = 0; s3 < 2; ++s3) {
-            bf16x8 ta[DBLK], tb[DBLK];  // read ahead of the products
-#pragma unroll
-            for (int m = 0; m < DBLK; ++m) {
-                ta[m] = trf(sp + G::TILEB, m, s3);
-                tb[m] = trf(sp, m, s3);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int m = 0; m < DBLK; ++m) {
-                dv[m] = mfma(ta[m], pf[s3], dv[m]);
-                dk[m] = mfma(tb[m], dsf[s3], dk[m]);
             }
         }
-        s = s2;
-        dp = dp2;
+        // dV^T += dO^T P (P waves) or dK^T += Q^T dS (dS waves); contraction
+        // over this wave's queries, k-step s3 covering rows 32 qs + 16 s3 +
+        // 4 hf + (0..3) and + 8.
+#pragma unroll
+        for (int s3 = 0; s3 < 2; ++s3) {
+            bf16x8 ta[DBLK];  // read ahead of the products
+#pragma unroll
+            for (int m = 0; m < DBLK; ++m) ta[m] = trf(sp, m, s3);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < DBLK; ++m) acc[m] = mfma(ta[m], opf[s3], acc[m]);
+        }
+        sc = sn;
         cur = nx[0];
         have = hv[0];
 #pragma unroll
@@ -906,36 +929,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_mfma_kernel(AttnBwdArgs a) {
     __syncthreads();  // every wave is done with the stages (nothing is in flight any more)
 
     // Add the query-half partials: waves with qs = 1 park theirs in LDS.
-    float* red = (float*)lds;  // [kb][2][DBLK][16][64] floats
+    float* red = (float*)lds;  // [pwave][kb][DBLK][16][64] floats
+    const int rw = (pwave ? 0 : 2) + kb;
     if (qs == 1) {
 #pragma unroll
         for (int m = 0; m < DBLK; ++m)
 #pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                red[(((kb * 2 + 0) * DBLK + m) * 16 + x) * 64 + lane] = dk[m][x];
-                red[(((kb * 2 + 1) * DBLK + m) * 16 + x) * 64 + lane] = dv[m][x];
-            }
+            for (int x = 0; x < 16; ++x) red[((rw * DBLK + m) * 16 + x) * 64 + lane] = acc[m][x];
     }
     __syncthreads();
     if (qs == 0 && mykey < a.S) {
-        uint16_t* kp = (uint16_t*)a.dk + (khead + mykey) * D;
-        uint16_t* vp = (uint16_t*)a.dv + (khead + mykey) * D;
+        uint16_t* op = (uint16_t*)(pwave ? a.dv : a.dk) + (khead + mykey) * D;
+        const float sc_out = pwave ? 1.0f : a.scale;
 #pragma unroll
         for (int m = 0; m < DBLK; ++m)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                bf16x4 wk, wv;
+                bf16x4 w;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int x = 4 * q + e;
-                    const float k2 = red[(((kb * 2 + 0) * DBLK + m) * 16 + x) * 64 + lane];
-                    const float v2 = red[(((kb * 2 + 1) * DBLK + m) * 16 + x) * 64 + lane];
-                    wk[e] = (__bf16)((dk[m][x] + k2) * a.scale);
-                    wv[e] = (__bf16)(dv[m][x] + v2);
+                    w[e] = (__bf16)((acc[m][x] + red[((rw * DBLK + m) * 16 + x) * 64 + lane]) * sc_out);
                 }
                 // rows d = 32 m + 8 q + 4 hf + e of column mykey
-                *(bf16x4*)(kp + 32 * m + 8 * q + 4 * hf) = wk;
-                *(bf16x4*)(vp + 32 * m + 8 * q + 4 * hf) = wv;
+                *(bf16x4*)(op + 32 * m + 8 * q + 4 * hf) = w;
             }
     }
 }
@@ -1160,7 +1177,9 @@ hipError_t launch_kv_major_index(const int8_t* keep, int BH, int NQ, int NK, int
 
 bool attn_bwd_mfma_supported(const AttnBwdArgs& a, int bf16) {
     const bool fits = ((int64_t)a.S + 128) * a.D * 2 < ((int64_t)1 << 31);
-    return bf16 && fits && a.block_kv == 64 && a.block_q % 32 == 0 && a.block_q >= 32 && a.block_q <= 128 &&
+    // dK / dV address a unit by its 32-bit byte offset from its GQA group's first row
+    const bool group_fits = (int64_t)(a.Hq / a.Hkv) * ((int64_t)a.S + 128) * a.D * 2 < ((int64_t)1 << 32);
+    return bf16 && fits && group_fits && a.block_kv == 64 && a.block_q % 32 == 0 && a.block_q >= 32 && a.block_q <= 128 &&
            (a.D == 64 || a.D == 128);
 }
 
@@ -1193,10 +1212,10 @@ hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     if (kvwork > 0) {
         if (a.D == 128)
-            hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<128>), dim3((unsigned)kvwork), dim3(256),
+            hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<128>), dim3((unsigned)kvwork), dim3(512),
                                attn_bwd_dkdv_lds_bytes(128), stream, a);
         else
-            hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<64>), dim3((unsigned)kvwork), dim3(256),
+            hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<64>), dim3((unsigned)kvwork), dim3(512),
                                attn_bwd_dkdv_lds_bytes(64), stream, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

@@ -27,15 +27,12 @@ FLAGS = [
     "-ffp-contract=fast",
     "-Wno-unused-command-line-argument",
 ]
-# Matrix-core accumulators: the selection kernels are compiled with them in
-# ordinary VGPRs (-amdgpu-mfma-vgpr-form). The gradient kernels keep the
-# default AGPR form: their dK/dV kernel holds S and dP of the next 64-query
-# chunk in AGPRs while it works on the current one, and in VGPR form the
-# register allocator moved the K and V fragments out to AGPRs and back in
-# front of every product instead. The forward and reordering kernels compile
-# to the same code either way.
+# Matrix-core accumulators are kept in ordinary VGPRs (-amdgpu-mfma-vgpr-form)
+# rather than AGPRs. The selection kernels needed it; the attention and
+# gradient kernels compile to the same code either way (at two waves per
+# SIMD their accumulators fit the unified register file).
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-PER_SOURCE = {"attn_bwd_kernels.hip": []}
+PER_SOURCE: dict = {}
 
 
 def hipcc() -> str:

@@ -1064,7 +1064,10 @@ __global__ __launch_bounds__(256, 5) void topk_grouped_kernel(TopkArgs a) {
     // Every load first, all in flight together. Buffer resources bound the
     // score row and the mask rows: reads past a row's end (and every read of
     // an absent mask, whose resource is empty) return zeros, so the loads
-    // need no clamping and no branches.
+    // need no clamping and no branches. Scores are read once and keep flags
+    // and the CSR written once, so all three stream past the L2 as
+    // nontemporal accesses (cache policy 2 on a buffer load), leaving it to
+    // the masks and the histogram traffic.
     const __amdgpu_buffer_rsrc_t srs = row_rsrc(srow, a.NK * 4);
     const __amdgpu_buffer_rsrc_t prs = row_rsrc(pw ? (const void*)pw : (const void*)srow, pw ? a.NKW * 8 : 0);
     const __amdgpu_buffer_rsrc_t drs = row_rsrc(dw ? (const void*)dw : (const void*)srow, dw ? a.NKW * 8 : 0);
@@ -1074,7 +1077,7 @@ __global__ __launch_bounds__(256, 5) void topk_grouped_kernel(TopkArgs a) {
     const int msh = 4 * (lane & 7);
 #pragma unroll
     for (int x = 0; x < G; ++x) {
-        v[x] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, 16 * lane, 1024 * x, 0));
+        v[x] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, 16 * lane, 1024 * x, 2));
         pwv[x] = __builtin_amdgcn_raw_buffer_load_b32(prs, mw4, 32 * x, 0);
         dwv[x] = __builtin_amdgcn_raw_buffer_load_b32(drs, mw4, 32 * x, 0);
     }
@@ -1302,7 +1305,7 @@ __global__ __launch_bounds__(256, 5) void topk_grouped_kernel(TopkArgs a) {
     for (int x = 0; x < G; ++x) {
         kb[x] = spread_nibble((picked >> (4 * x)) & 0xFu) | ((bytes_at_least(bk[x], yrep) & hmask) >> 7) | pk[x];
         const int e0 = 256 * x + 4 * lane;
-        if (e0 < a.NK) *(uint32_t*)(krow + e0) = kb[x];
+        if (e0 < a.NK) __builtin_nontemporal_store(kb[x], (uint32_t*)(krow + e0));
     }
     // CSR: ascending indices at row_begin, never past the planned row. Group
     // counts are scanned three at a time in 10-bit fields (a field's total is
@@ -1325,7 +1328,7 @@ __global__ __launch_bounds__(256, 5) void topk_grouped_kernel(TopkArgs a) {
             const int e0 = 256 * x + 4 * lane;
             while (m) {  // the lane's kept elements of this group, ascending
                 const int cc = __builtin_ctz(m) >> 3;
-                if (slot < row_len) crow[slot] = e0 + cc;
+                if (slot < row_len) __builtin_nontemporal_store(e0 + cc, crow + slot);
                 ++slot;
                 m &= m - 1u;
             }

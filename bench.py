@@ -287,7 +287,9 @@ def stage_timing(plan, plan_dev, q, k, ws, sel: tkt.Selection, w: synth.Workload
     over `calls` planned selections (run after the timed steps, same inputs),
     with each stage's algorithmic bytes (and FLOPs for the score product):
       pool_q / pool_k: read q / k once, write the pooled fp32 means;
-      scores_c (head chunk c): 2 * B * nh * NQ * NK * D FLOP, writes the chunk's fp32 scores;
+      scores_c (head chunk c): 2 * B * nh * NQ * NK * D FLOP, writes the chunk's fp32 scores
+        (with more than 64 query tiles per head the library runs them as six bf16 matrix
+        products per fp32 one, on split operands: that executed rate is reported too);
       topk_c: reads the chunk's scores, writes its keep bytes, CSR entries and row offsets.
     Reports p10 / p50 / p90 in ms, GB/s and fractions at the published peaks."""
     stream = torch.cuda.current_stream()
@@ -340,11 +342,16 @@ def stage_timing(plan, plan_dev, q, k, ws, sel: tkt.Selection, w: synth.Workload
         d.update({"bytes": float(nbytes), "GBps": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
         if flops is not None:
             tf = flops / (ms * 1e-3) / 1e12
-            d.update({"flops": flops, "TFLOPs": round(tf, 2), "frac_fp32_peak": round(tf / PEAK_FP32_TFLOPS, 4)})
+            d.update({"flops": flops, "TFLOPs": round(tf, 2)})
+            if NQ > 64:  # split-operand bf16 products
+                d.update({"executed_bf16_TFLOPs": round(6 * tf, 2),
+                          "executed_frac_bf16_peak": round(6 * tf / PEAK_BF16_TFLOPS, 4)})
+            else:
+                d["frac_fp32_peak"] = round(tf / PEAK_FP32_TFLOPS, 4)
         out[nm] = d
     out["how"] = (f"HIP events the library records on the selection stream between its launches "
                   f"(nsa_stage_timing_begin/_end), {calls} planned selections after the timed steps; "
-                  f"fractions against 8 TB/s HBM and 157.3 TFLOP/s fp32")
+                  f"fractions against 8 TB/s HBM, 2.5 PFLOP/s bf16 and 157.3 TFLOP/s fp32")
     return out
 
 

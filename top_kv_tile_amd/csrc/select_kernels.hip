@@ -10,12 +10,25 @@
 
 #include <float.h>
 
+#include <algorithm>
+#include <atomic>
+
 namespace nsa {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Raw buffer resource over `bytes` bytes at p (stride 0): loads past the
+// end return zeros, stores past it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -231,108 +244,183 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qh
     store(c11, 32, 32);
 }
 
-// The same product for many query rows (NQ > 64), one 128 x 256 block per
-// workgroup: wave w takes query rows 64 (w / 2) .. + 63 and key columns
-// 128 (w % 2) .. + 127 (2 x 4 blocks of 32 x 32 as above). Loading each lane's
-// own rows from L2 touches a cache line per lane and every wave of a workgroup
-// reloads the rows it shares with the others, so here the operands go through
-// LDS in chunks of 32 contraction indices: the workgroup loads the chunk's 128
-// pooled-query rows and 256 pooled-key rows with 8 lanes per 128-byte row
-// segment, one chunk ahead in registers, and stores them to LDS with rows
-// padded to 36 floats (16-byte reads of 16 consecutive rows then fall in
-// distinct banks). At step (g, e) of a chunk, lane half hf supplies
-// contraction index 16*hf + 4*g + e.
-template <int D>
-__global__ __launch_bounds__(256) void score_lds_kernel(const float* __restrict__ qh, const float* __restrict__ kh,
-                                                        int Hsel, int Hk, int group, int h0, int nh, int NQ,
-                                                        int NK, int NKs, int nbi, int nbj, float* __restrict__ s) {
-    constexpr int KC = 32, PAD = 36, ROWS = 128, COLS = 256;
-    __shared__ __attribute__((aligned(16))) float As[ROWS * PAD];
-    __shared__ __attribute__((aligned(16))) float Bs[COLS * PAD];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int64_t wid = blockIdx.x;
-    const int bj = (int)(wid % nbj);
-    wid /= nbj;
-    const int bi = (int)(wid % nbi);
-    wid /= nbi;
-    const int hl = (int)(wid % nh);
-    const int b = (int)(wid / nh);
-    const int h = h0 + hl;
-    const int hk = (Hk == 1) ? 0 : h / group;
-    const float* A = qh + ((int64_t)b * Hsel + h) * NQ * D;
-    const float* Bm = kh + ((int64_t)b * Hk + hk) * NKs * D;  // NKs >= NK rows per head
-    const int i0 = bi * ROWS, j0 = bj * COLS;
+// The same product for many query rows (NQ > 64) on the bf16 matrix cores.
+// Every pooled value x is split into three bf16 terms, x = x0 + x1 + x2
+// exactly: x0 is x rounded to bf16, x1 the rounding of x - x0 (an exact fp32
+// difference), x2 what is left (at most 8 significant bits, so exact too).
+// The dot product takes the six term products whose scale is at least 2^-16
+// of |x y| (x0y0, x0y1, x1y0, x0y2, x2y0, x1y1); the three dropped ones are
+// below 2^-23 |x y| together, so a score carries fp32-sized errors while the
+// matrix work runs at the bf16 rate (six 32x32x16 products per 16 indices
+// against eight 32x32x2 fp32 ones per 2 at a sixteenth of that rate).
+//
+// A workgroup computes 128 x 256 blocks: wave w takes query rows 64 (w / 2) ..
+// + 63 and key columns 128 (w % 2) .. + 127 as 2 x 4 blocks of 32 x 32. A
+// lane ends with one key column of 16 query rows per block, so each store
+// instruction writes 32 consecutive keys (one whole 128-byte line) of two rows.
+// (Keys as the rows of the product, four consecutive keys per lane and one
+// 16-byte store, wrote 32-byte pieces of 32 rows per instruction and ran 10%
+// slower; staging blocks through LDS for whole-line 16-byte stores gained
+// nothing.) The operands go through LDS 16 contraction indices at a time: the
+// workgroup loads the chunk's 128 pooled-query rows and 256 pooled-key rows as
+// 16-byte pieces (four lanes per 64-byte row segment, one chunk ahead in
+// registers), splits them and stores each row as its three 32-byte term
+// vectors plus 16 bytes of padding (112 bytes: the 16-byte fragment reads of
+// 16 consecutive rows then hit distinct banks). Lane half hf reads indices
+// 8 hf .. 8 hf + 7 of a term vector, the operand layout of the 32x32x16
+// product.
+// The grid holds two workgroups per CU, each walking its blocks in turn.
+// Blocks are numbered so that the blocks of one query-row block run on one
+// XCD (workgroup n runs on XCD n % 8): its pooled queries are fetched into
+// one L2 instead of eight.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+__device__ __forceinline__ void split3_store(char* dst, const f32x4 v) {
+    u32x2 t0, t1, t2;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const float x0 = v[2 * p], x1 = v[2 * p + 1];
+        const uint32_t h = pk_bf16(x0, x1);
+        const float r0 = x0 - bf16lo(h), r1 = x1 - bf16hi(h);
+        const uint32_t m = pk_bf16(r0, r1);
+        t0[p] = h;
+        t1[p] = m;
+        t2[p] = pk_bf16(r0 - bf16lo(m), r1 - bf16hi(m));
+    }
+    *(u32x2*)dst = t0;
+    *(u32x2*)(dst + 32) = t1;
+    *(u32x2*)(dst + 64) = t2;
+}
 
-    // Global loads: thread t takes rows t / 8 + 32 x (x < 4), floats 4 (t % 8) .. + 3
-    // of the chunk (rows past the end repeat the last row; their results are not stored).
-    const int lr = tid >> 3, lq = tid & 7;
-    const float* ag[4];
-    const float* bg[8];
+template <int D>
+__global__ __launch_bounds__(256, 2) void score_split_kernel(const float* __restrict__ qh, const float* __restrict__ kh,
+                                                             int Hsel, int Hk, int group, int h0, int nh, int NQ,
+                                                             int NK, int NKs, int nbi, int nbj, int64_t nblk,
+                                                             float* __restrict__ s) {
+    constexpr int ROWS = 128, COLS = 256, RB = 112, KC = 16;
+    __shared__ __attribute__((aligned(16))) char lds[(ROWS + COLS) * RB];
+    char* const As = lds;
+    char* const Bs = lds + ROWS * RB;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool xcd_map = (nblk & 7) == 0 && (gridDim.x & 7) == 0;
+    const int lr = tid >> 2, lq = tid & 3;
+    const int wi = wave >> 1, wj = wave & 1;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const char* al = As + (wi * 64 + l32) * RB + 16 * hf;
+    const char* bl = Bs + (wj * 128 + l32) * RB + 16 * hf;
+
+    // Block w: its query rows i0.., key columns j0.. of head h0 + hl, batch b.
+    // Global loads: thread t takes rows t / 4 + 64 x, floats 4 (t % 4) .. + 3 of
+    // a chunk (rows past the end repeat the last row; their results are not stored).
+    struct Blk {
+        const float* a[2];
+        const float* k[4];
+        int i0, j0;
+        int64_t row0;  // score row of query row i0
+    };
+    auto block_of = [&](int64_t w) {
+        int64_t wid = xcd_map ? (w & 7) * (nblk >> 3) + (w >> 3) : w;
+        const int bj = (int)(wid % nbj);
+        wid /= nbj;
+        const int bi = (int)(wid % nbi);
+        wid /= nbi;
+        const int hl = (int)(wid % nh);
+        const int b = (int)(wid / nh);
+        const int h = h0 + hl;
+        const int hk = (Hk == 1) ? 0 : h / group;
+        const float* A = qh + ((int64_t)b * Hsel + h) * NQ * D;
+        const float* Bm = kh + ((int64_t)b * Hk + hk) * NKs * D;  // NKs >= NK rows per head
+        Blk o;
+        o.i0 = bi * ROWS;
+        o.j0 = bj * COLS;
+        o.row0 = ((int64_t)b * nh + hl) * NQ + o.i0;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) ag[x] = A + (int64_t)min(i0 + lr + 32 * x, NQ - 1) * D + 4 * lq;
+        for (int x = 0; x < 2; ++x) o.a[x] = A + min(o.i0 + lr + 64 * x, NQ - 1) * D + 4 * lq;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) bg[x] = Bm + (int64_t)min(j0 + lr + 32 * x, NK - 1) * D + 4 * lq;
-    f32x4 ra[4], rb[8];
-    auto gload = [&](int kc) {
+        for (int x = 0; x < 4; ++x) o.k[x] = Bm + min(o.j0 + lr + 64 * x, NK - 1) * D + 4 * lq;
+        return o;
+    };
+    f32x4 ra[2], rb[4];
+    auto gload = [&](const Blk& o, int kc) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) ra[x] = *(const f32x4*)(ag[x] + kc);
+        for (int x = 0; x < 2; ++x) ra[x] = *(const f32x4*)(o.a[x] + kc);
 #pragma unroll
-        for (int x = 0; x < 8; ++x) rb[x] = *(const f32x4*)(bg[x] + kc);
+        for (int x = 0; x < 4; ++x) rb[x] = *(const f32x4*)(o.k[x] + kc);
     };
     auto lstore = [&]() {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) *(f32x4*)(As + (lr + 32 * x) * PAD + 4 * lq) = ra[x];
+        for (int x = 0; x < 2; ++x) split3_store(As + (lr + 64 * x) * RB + 8 * lq, ra[x]);
 #pragma unroll
-        for (int x = 0; x < 8; ++x) *(f32x4*)(Bs + (lr + 32 * x) * PAD + 4 * lq) = rb[x];
+        for (int x = 0; x < 4; ++x) split3_store(Bs + (lr + 64 * x) * RB + 8 * lq, rb[x]);
     };
-    const int wi = wave >> 1, wj = wave & 1;
-    const int l32 = lane & 31, hf = lane >> 5;
-    const float* a0l = As + (wi * 64 + l32) * PAD + 16 * hf;
-    const float* a1l = a0l + 32 * PAD;
-    const float* b0l = Bs + (wj * 128 + l32) * PAD + 16 * hf;
 
-    f32x16 c0[4] = {}, c1[4] = {};
-    gload(0);
+    int64_t w = blockIdx.x;
+    if (w >= nblk) return;
+    Blk cur = block_of(w);
+    gload(cur, 0);
+    // One block: products, then the next block's first chunk requested, then
+    // this block's stores. Out-of-range stores are dropped by the buffer's
+    // bound (rows past NQ) or sent past it (columns past NK), so every lane
+    // issues the same stores, without branches.
+    auto block = [&]() -> bool {
+        f32x16 c[2][4] = {};
 #pragma unroll
-    for (int kc = 0; kc < D; kc += KC) {
-        __syncthreads();  // the previous chunk's LDS reads are done
-        lstore();
-        __syncthreads();
-        if (kc + KC < D) gload(kc + KC);  // in flight under this chunk's products
+        for (int kc = 0; kc < D; kc += KC) {
+            __syncthreads();  // the previous chunk's LDS reads are done
+            lstore();
+            __syncthreads();
+            if (kc + KC < D) gload(cur, kc + KC);  // in flight under this chunk's products
+            bf16x8 a[2][3];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const f32x4 x0 = *(const f32x4*)(a0l + 4 * g), x1 = *(const f32x4*)(a1l + 4 * g);
-            f32x4 y[4];
+            for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) y[jb] = *(const f32x4*)(b0l + jb * 32 * PAD + 4 * g);
+                for (int t = 0; t < 3; ++t) a[ib][t] = *(const bf16x8*)(al + ib * 32 * RB + 32 * t);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int jb = 0; jb < 4; ++jb) {
+                bf16x8 y[3];
 #pragma unroll
-                for (int jb = 0; jb < 4; ++jb) {
-                    c0[jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0[e], y[jb][e], c0[jb], 0, 0, 0);
-                    c1[jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1[e], y[jb][e], c1[jb], 0, 0, 0);
+                for (int t = 0; t < 3; ++t) y[t] = *(const bf16x8*)(bl + jb * 32 * RB + 32 * t);
+                // Smallest terms first: x1y1, x2y0, x0y2, x1y0, x0y1, x0y0.
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    f32x16 acc = c[ib][jb];
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib][1], y[1], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib][2], y[0], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib][0], y[2], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib][1], y[0], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib][0], y[1], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ib][0], y[0], acc, 0, 0, 0);
+                    c[ib][jb] = acc;
                 }
-        }
-    }
-    // Accumulator layout of a 32 x 32 block: lane holds column l32 and rows
-    // 8*q + 4*hf + e at element 4*q + e.
-    float* out = s + ((int64_t)b * nh + hl) * NQ * NK;
-    const int r0 = i0 + wi * 64, cb = j0 + wj * 128;
-    auto store = [&](const f32x16& c, int ib, int jb) {
-        const int col = cb + jb + l32;
-        if (col >= NK) return;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = r0 + ib + 8 * q + 4 * hf + e;
-                if (row < NQ) out[(int64_t)row * NK + col] = c[4 * q + e];
             }
-    };
+        }
+        const int64_t wn = w + gridDim.x;
+        const Blk done = cur;
+        if (wn < nblk) {
+            cur = block_of(wn);
+            gload(cur, 0);
+        }
+        // Accumulator layout of a 32 x 32 block: lane holds key column l32 and
+        // query rows 8*q + 4*hf + e at element 4*q + e.
+        const __amdgpu_buffer_rsrc_t ors = row_rsrc(s + done.row0 * NK, min(ROWS, NQ - done.i0) * NK * 4);
+        const int col0 = done.j0 + wj * 128 + l32;
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-        store(c0[jb], 0, 32 * jb);
-        store(c1[jb], 32, 32 * jb);
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    const int row = wi * 64 + 32 * ib + 8 * (x >> 2) + 4 * hf + (x & 3);
+                    const int col = col0 + 32 * jb;
+                    const uint32_t off = col < NK ? 4u * (uint32_t)(row * NK + col) : 0x80000000u;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c[ib][jb][x]), ors, off, 0, 0);
+                }
+        if (wn >= nblk) return false;
+        w = wn;
+        return true;
+    };
+    while (block()) {
     }
 }
 
@@ -910,11 +998,6 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
     return r;
 }
 
-// Raw buffer resource over `bytes` bytes at p (stride 0): loads past the
-// end return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
-}
 
 // Scale of the bucket map u = x * scale - lo * scale, which takes [lo, hi]
 // onto [0, 256]. Any positive finite scale keeps the map monotone, so an
@@ -1379,6 +1462,19 @@ hipError_t launch_head_mean(const float* in, int B, int H, int N, int D, float* 
     return hipGetLastError();
 }
 
+// Compute units of the current device, read once per device.
+static int device_cus() {
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 hipError_t launch_scores(const void* qh, const float* kh, int B, int Hsel, int Hk, int group, int h0, int nh,
                          int NQ, int NK, int D, float* s, hipStream_t stream, int NKs, int q_rows) {
     if (NKs <= 0) NKs = NK;
@@ -1404,15 +1500,16 @@ hipError_t launch_scores(const void* qh, const float* kh, int B, int Hsel, int H
     const float* qf = (const float*)qh;
     if (NQ > 64) {
         const int nbi = (NQ + 127) / 128, nbj = (NK + 255) / 256;
-        const dim3 grid((unsigned)((int64_t)B * nh * nbi * nbj));
-#define NSA_SCORE_LDS(DD)                                                                                     \
-    hipLaunchKernelGGL((score_lds_kernel<DD>), grid, dim3(256), 0, stream, qf, kh, Hsel, Hk, group, h0, nh, NQ, \
-                       NK, NKs, nbi, nbj, s)
-        if (D == 64) NSA_SCORE_LDS(64);
-        else if (D == 128) NSA_SCORE_LDS(128);
-        else if (D == 256) NSA_SCORE_LDS(256);
+        const int64_t nblk = (int64_t)B * nh * nbi * nbj;
+        const dim3 grid((unsigned)std::min<int64_t>(nblk, 2 * (int64_t)device_cus()));
+#define NSA_SCORE_SPLIT(DD)                                                                                     \
+    hipLaunchKernelGGL((score_split_kernel<DD>), grid, dim3(256), 0, stream, qf, kh, Hsel, Hk, group, h0, nh, NQ, \
+                       NK, NKs, nbi, nbj, nblk, s)
+        if (D == 64) NSA_SCORE_SPLIT(64);
+        else if (D == 128) NSA_SCORE_SPLIT(128);
+        else if (D == 256) NSA_SCORE_SPLIT(256);
         else return hipErrorInvalidValue;
-#undef NSA_SCORE_LDS
+#undef NSA_SCORE_SPLIT
         return hipGetLastError();
     }
     const int nbi = (NQ + 63) / 64, nbj = (NK + 63) / 64;

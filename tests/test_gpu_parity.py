@@ -45,7 +45,7 @@ def test_pool_blocks(dtype, S, D, block):
 
 @pytest.mark.parametrize("Hq,Hkv,shared,S,D,bq,bkv", [
     (4, 4, False, 2000, 128, 128, 64), (8, 2, False, 2000, 128, 128, 64), (6, 3, True, 2000, 128, 128, 64),
-    # more than 64 query tiles (the LDS-staged kernel), ragged in both block dimensions
+    # more than 64 query tiles (the split-operand bf16 kernel), ragged in both block dimensions
     (4, 2, False, 20000, 128, 128, 64), (2, 1, False, 9000, 64, 64, 32), (2, 2, True, 12000, 256, 128, 64),
 ])
 def test_score_blocks(Hq, Hkv, shared, S, D, bq, bkv):
@@ -58,6 +58,35 @@ def test_score_blocks(Hq, Hkv, shared, S, D, bq, bkv):
     mag = np.abs(qh.double().numpy()) @ np.swapaxes(np.abs(kh.double().numpy()), -1, -2)
     assert got.shape == ref.shape
     assert np.all(np.abs(got - ref) <= 4 * D * 2.0 ** -24 * mag + 1e-30)
+
+
+@pytest.mark.parametrize("S,bkv", [(9000, 64), (16384, 64)])
+def test_score_blocks_wide_range(S, bkv):
+    """The many-row score kernel splits each pooled fp32 value into three bf16
+    terms. Operands whose dimensions span 2^-20 .. 2^20 in magnitude (fp32
+    inputs, so the pooled values carry all 24 significant bits) must still
+    score within the fp32 bound: against the oracle, and against the exact
+    (fp64) product of the library's own pooled operands, which isolates the
+    score kernel's error. 141 kv tiles leave ragged 256-key blocks, 256 whole ones."""
+    D, bq = 128, 128
+    say(f"scores wide range S={S} bkv={bkv}")
+    g = torch.Generator().manual_seed(S)
+    scale = torch.exp2(torch.randint(-20, 21, (1, 1, 1, D), generator=g).float())
+    q = torch.randn(1, 4, S, D, generator=g) * scale
+    k = torch.randn(1, 2, S, D, generator=g) / scale.flip(-1)
+    spec = tkt.SparseSpec(block_q=bq, block_kv=bkv)
+    got = tkt.nsa_score_blocks(to_dev(q), to_dev(k), spec).cpu().numpy().astype(np.float64)
+    ref = oracle.score_blocks(q, k, bq, bkv, False).astype(np.float64)
+    qh, kh = oracle.head_operands(oracle.pool_blocks(q, bq), oracle.pool_blocks(k, bkv), False)
+    mag = np.abs(qh.double().numpy()) @ np.swapaxes(np.abs(kh.double().numpy()), -1, -2)
+    assert got.shape == ref.shape and got.shape[2] > 64
+    assert np.all(np.abs(got - ref) <= 4 * D * 2.0 ** -24 * mag + 1e-30)
+    pq = tkt.nsa_pool_blocks(to_dev(q), bq).cpu()
+    pk = tkt.nsa_pool_blocks(to_dev(k), bkv).cpu()
+    gq, gk = oracle.head_operands(pq, pk, False)
+    qd, kd = gq.double().numpy(), np.swapaxes(gk.double().numpy(), -1, -2)
+    exact, gmag = qd @ kd, np.abs(qd) @ np.abs(kd)
+    assert np.all(np.abs(got - exact) <= 2 * D * 2.0 ** -24 * gmag + 1e-30)
 
 
 CASES = [

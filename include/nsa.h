@@ -383,7 +383,11 @@ int nsa_pool_blocks(const nsa_tensor* x, int32_t block, float* out, void* stream
 
 /* Stage entry point: the full fp32 score tensor of score_blocks on the
  * selection page, (B, H', NQ, NK), written to scores (device). Needs a
- * workspace of nsa_sizes.workspace_bytes (as nsa_select). */
+ * workspace of nsa_sizes.workspace_bytes (as nsa_select). Each score is the
+ * pooled dot product to within fp32 rounding of the products and their sum
+ * (|error| <= 2 D 2^-24 sum |q_d k_d|); with more than 64 query tiles per
+ * head it is computed from exact three-term bf16 splits of the pooled
+ * operands on the bf16 matrix cores. */
 int nsa_score_blocks(const nsa_tensor* q, const nsa_tensor* k, const nsa_spec* spec,
                      float* scores, void* workspace, size_t workspace_bytes, void* stream);
 

@@ -1,5 +1,6 @@
 // Selection-stage kernels for gfx950 (CDNA4): pooling, head means, the pooled
-// score product on fp32 MFMA, and the per-row top-k with CSR compaction.
+// score product in fp32 (on the matrix cores: split-operand bf16 for many rows,
+// fp32 MFMA for a few), and the per-row top-k with CSR compaction.
 //
 // What is computed follows the page "automatic/modules/attention/sparse/selector.py"
 // (pool_blocks, score_blocks, diagonal_blocks, selection_plan, select_blocks).

@@ -1113,21 +1113,20 @@ __device__ __forceinline__ uint32_t wave_or_u(uint32_t x) {
 // The kernel waits on its loads and LDS atomics, so resident waves are what
 // hide the latency: it is held to five waves per SIMD (96 VGPRs). At that
 // budget only the crowded-bucket path keeps a few values in scratch; the
-// common path uses none.
+// common path uses none. One wave per workgroup: each wave's histogram and
+// lists then sit at fixed LDS addresses, so a histogram address is one
+// shift of the bucket byte (byte-select operand) with no per-wave base
+// (4% faster than four waves per workgroup).
 template <int G>
-__global__ __launch_bounds__(256, 5) void topk_grouped_kernel(TopkArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void topk_grouped_kernel(TopkArgs a) {
     constexpr int E = 4 * G;
     constexpr uint32_t kFull = E == 32 ? 0xFFFFFFFFu : ((1u << (E & 31)) - 1u);
-    __shared__ uint32_t hist_all[4][256];
-    __shared__ uint2 list_all[4][64];
-    __shared__ uint32_t pick_all[4][64 * G];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int i = (int)blockIdx.x * 4 + wave;  // query tile
+    __shared__ uint32_t hist[256];
+    __shared__ uint2 list[64];
+    __shared__ uint32_t pick[64 * G];  // lane L's words x at G L + x: picks inside b*, byte form
+    const int lane = threadIdx.x;
+    const int i = (int)blockIdx.x;  // query tile
     if (i >= a.NQ) return;
-    uint32_t* hist = hist_all[wave];
-    uint2* list = list_all[wave];
-    uint32_t* pick = pick_all[wave];  // lane L's words x at G L + x: picks inside b*, byte form
     const int hl = blockIdx.y, b = blockIdx.z;
     const int h = a.h0 + hl;
     const int64_t lr = ((int64_t)b * a.nh + hl) * a.NQ + i;  // row of the score chunk
@@ -1546,9 +1545,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
                          ((uintptr_t)a.keep & 3) == 0 && ((uintptr_t)a.scores & 15) == 0 &&
                          a.q_off + (int64_t)(a.NQ + 1) * a.block_q + a.block_kv < ((int64_t)1 << 31);
     if (grouped) {
-        const dim3 g3((unsigned)((a.NQ + 3) / 4), (unsigned)a.nh, (unsigned)a.B);
+        const dim3 g3((unsigned)a.NQ, (unsigned)a.nh, (unsigned)a.B);
         const int ng = (a.NK + 255) / 256;
-#define NSA_TOPK_G(GG) hipLaunchKernelGGL((topk_grouped_kernel<GG>), g3, dim3(256), 0, stream, a)
+#define NSA_TOPK_G(GG) hipLaunchKernelGGL((topk_grouped_kernel<GG>), g3, dim3(64), 0, stream, a)
         if (ng <= 1) NSA_TOPK_G(1);
         else if (ng <= 2) NSA_TOPK_G(2);
         else if (ng <= 4) NSA_TOPK_G(4);

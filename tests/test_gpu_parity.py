@@ -47,6 +47,8 @@ def test_pool_blocks(dtype, S, D, block):
     (4, 4, False, 2000, 128, 128, 64), (8, 2, False, 2000, 128, 128, 64), (6, 3, True, 2000, 128, 128, 64),
     # more than 64 query tiles (the split-operand bf16 kernel), ragged in both block dimensions
     (4, 2, False, 20000, 128, 128, 64), (2, 1, False, 9000, 64, 64, 32), (2, 2, True, 12000, 256, 128, 64),
+    # 567 blocks of 128 x 256: more than the persistent grid holds, and not a multiple of 8
+    (63, 7, False, 40000, 64, 128, 64),
 ])
 def test_score_blocks(Hq, Hkv, shared, S, D, bq, bkv):
     say(f"scores Hq={Hq} Hkv={Hkv} shared={shared} S={S} D={D} bq={bq} bkv={bkv}")

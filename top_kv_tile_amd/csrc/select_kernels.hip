@@ -638,13 +638,11 @@ template <int EPL>
 // Up to 2048 kv tiles per row the register budget is held to four waves per
 // SIMD: the kernel waits on loads and LDS atomics, and more resident waves
 // hide that.
-__global__ __launch_bounds__(256, (EPL <= 32 ? 4 : 1)) void topk_kernel(TopkArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(EPL <= 32 ? 4 : 1))) void topk_kernel(TopkArgs a) {
     typedef typename MaskT<EPL>::type M;
-    __shared__ uint32_t hist_all[4][256];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar row math
-    uint32_t* hist = hist_all[wave];
-    const int64_t lr = (int64_t)blockIdx.x * 4 + wave;
+    __shared__ uint32_t hist[256];  // one wave per workgroup: fixed LDS addresses
+    const int lane = threadIdx.x;
+    const int64_t lr = blockIdx.x;
     const int64_t nrows = (int64_t)a.B * a.nh * a.NQ;
     if (lr >= nrows) return;
     const int i = (int)(lr % a.NQ);
@@ -1555,9 +1553,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
 #undef NSA_TOPK_G
         return hipGetLastError();
     }
-    const dim3 grid((unsigned)((rows + 3) / 4));
+    const dim3 grid((unsigned)rows);
     const int epl = (a.NK + 63) / 64;
-#define NSA_TOPK(E) hipLaunchKernelGGL((topk_kernel<E>), grid, dim3(256), 0, stream, a)
+#define NSA_TOPK(E) hipLaunchKernelGGL((topk_kernel<E>), grid, dim3(64), 0, stream, a)
     if (epl <= 1) NSA_TOPK(1);
     else if (epl <= 2) NSA_TOPK(2);
     else if (epl <= 4) NSA_TOPK(4);
